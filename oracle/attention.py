@@ -1,0 +1,210 @@
+"""Attention over a rank's shard and the exact partial-softmax merge (oracle).
+
+Float64 throughout. Inputs are float64 arrays (or any array plus a ``decode``
+callable that turns a slice of stored bits into float64, see ``formats``).
+
+Definitions written out here:
+
+* Causal attention -- *Long Context* 1.1: a token's output compares its query
+  with the keys of all tokens up to and including it, turns the scores into
+  probabilities with a softmax and sums the values with those weights.
+  Scores are ``scale * q . k``; the softmax scale is an explicit argument.
+* Log-sum-exp -- *Long Context* 3.3: besides its output each shard reports
+  the natural log of its sum of exponentiated scores, ``lse = log sum_t
+  exp(s_t)``. Written with the usual max shift ``m + log sum exp(s - m)``,
+  which is the same number. An empty key set has output 0 and lse = -inf.
+* GQA -- vLLM DCP post, 5.4: kv heads are broadcast to groups of query heads;
+  reading taken: query head h uses kv head ``h // (Hq / Hkv)``.
+* MLA -- *Long Context* 1.3 and vLLM DCP post, 5.3: one latent vector per
+  token is read by all heads; the vLLM GLM-5.3 post, footnote 1, counts QK
+  over 576 dims and PV over 512. Reading taken: keys are the 576-dim latent
+  and values are its first 512 dims (``v=None, dv=512``).
+* Merge -- *Long Context* 3.3: ``lse = logsumexp_c lse_c``,
+  ``scale_c = exp(lse_c - lse)``, ``O = sum_c scale_c * O_c``; exact apart
+  from the order of additions (3.3; DeepSeek-V4 notes, section 5).
+* Merge in statistics form -- DeepSeek-V4 notes, section 5: per shard
+  ``m_p = max s``, ``l_p = sum exp(s - m_p)``, ``u_p = sum exp(s - m_p) v``;
+  globally ``m = max m_p``, ``Z = sum e^(m_p - m) l_p``,
+  ``o = sum e^(m_p - m) u_p / Z``.
+
+Rows are independent; ``prefill_shard`` computes several rows with one
+matrix product only to keep numpy fast, with the causal limit of each row
+applied as an explicit mask. Nothing is tiled over keys and there is no
+running (online) softmax here.
+
+Pins (``tests/test_oracle_attention.py``): the two-GPU example of
+*Long Context* 3.2/3.3 (exp-scores 4, 2, 1, 1) to exact rationals; torch's
+float64 ``scaled_dot_product_attention(is_causal=True)`` for C = 1; union of
+all ranks' outputs equals unsharded attention; merged split-KV equals
+unsharded attention; single-key and equal-score closed forms; the two merge
+forms agree.
+"""
+
+import numpy as np
+
+_NEG_INF = -np.inf
+
+
+def _f64(x, decode=None):
+    return decode(x) if decode is not None else np.asarray(x, dtype=np.float64)
+
+
+def attend(q, keys, values, scale):
+    """One query against a key set. q [D], keys [n, D], values [n, Dv].
+    Returns (o [Dv], lse)."""
+    q = np.asarray(q, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    if keys.shape[0] == 0:
+        return np.zeros(values.shape[-1]), _NEG_INF
+    s = scale * (keys @ q)
+    m = np.max(s)
+    e = np.exp(s - m)
+    ell = np.sum(e)
+    return (e @ values) / ell, m + np.log(ell)
+
+
+def _group(Hq, Hkv):
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return Hq // Hkv
+
+
+def prefill_shard(q, k, segments, scale, v=None, dv=None, rows=None, decode=None,
+                  max_elems=1 << 25):
+    """Causal attention for a rank's local query rows against their true
+    causal history (cached prefix included).
+
+    q        [n_local, Hq, Dqk]   local queries in plan order
+    k        [T_kv, Hkv, Dqk]     packed full keys, request j at rows kv_row0_j ..
+    v        [T_kv, Hkv, Dv]      packed values, or None for MLA (v = k[..., :dv])
+    segments list of (req, q_row0, q_len, pos0, pos_stride, kv_row0)
+    rows     optional list of local rows to compute (others are not computed)
+
+    Returns (O, LSE): O [len(rows), Hq, Dv], LSE [len(rows), Hq] in the order
+    of ``rows`` (all local rows, ascending, when rows is None).
+    """
+    n_local, Hq, Dqk = q.shape
+    Hkv = k.shape[1]
+    G = _group(Hq, Hkv)
+    if v is None:
+        if dv is None:
+            raise ValueError("MLA needs dv")
+        Dv = dv
+    else:
+        Dv = v.shape[-1]
+    # local row -> (kv_row0, position)
+    where = {}
+    for (_req, r0, n, pos0, stride, kv0) in segments:
+        for i in range(n):
+            where[r0 + i] = (kv0, pos0 + i * stride)
+    if rows is None:
+        rows = sorted(where)
+    rows = list(rows)
+    O = np.full((len(rows), Hq, Dv), np.nan)
+    L = np.full((len(rows), Hq), np.nan)
+    # batch rows that share a request (same kv_row0) to use matrix products
+    by_req = {}
+    for out_i, r in enumerate(rows):
+        kv0, p = where[r]
+        by_req.setdefault(kv0, []).append((out_i, r, p))
+    for kv0, items in by_req.items():
+        items.sort(key=lambda t: t[2])
+        pmax = items[-1][2]
+        chunk = max(1, max_elems // max(1, Hq * (pmax + 1)))
+        for c0 in range(0, len(items), chunk):
+            part = items[c0:c0 + chunk]
+            p_hi = part[-1][2]
+            keys = _f64(k[kv0:kv0 + p_hi + 1], decode)  # [n_keys, Hkv, Dqk]
+            vals = keys[..., :Dv] if v is None else _f64(v[kv0:kv0 + p_hi + 1], decode)
+            qr = _f64(q[[t[1] for t in part]], decode)  # [R, Hq, Dqk]
+            pos = np.array([t[2] for t in part])
+            # key index t is visible to a row at position p iff t <= p
+            visible = np.arange(p_hi + 1)[None, :] <= pos[:, None]  # [R, n_keys]
+            for hk in range(Hkv):
+                R = len(part)
+                qh = qr[:, hk * G:(hk + 1) * G, :].reshape(R * G, Dqk)
+                kh = np.ascontiguousarray(keys[:, hk, :])  # [n_keys, D]
+                s = (scale * (qh @ kh.T)).reshape(R, G, p_hi + 1)
+                s = np.where(visible[:, None, :], s, _NEG_INF)
+                m = np.max(s, axis=-1, keepdims=True)
+                e = np.exp(s - m)
+                ell = np.sum(e, axis=-1, keepdims=True)
+                vh = np.ascontiguousarray(vals[:, hk, :])
+                o = (e.reshape(R * G, p_hi + 1) @ vh).reshape(R, G, Dv) / ell
+                lse = (m + np.log(ell))[..., 0]
+                for j, t in enumerate(part):
+                    O[t[0], hk * G:(hk + 1) * G] = o[j]
+                    L[t[0], hk * G:(hk + 1) * G] = lse[j]
+    return O, L
+
+
+def decode_shard(q, kcache, begin, end, scale, vcache=None, dv=None, decode=None,
+                 kv_scale=None, batch=None):
+    """Split-KV decode on one shard: for request b and query head h, attention
+    of the single query q[b, h] over cache rows [begin_b, end_b).
+
+    q       [B, Hq, Dqk]
+    kcache  [B, Lmax, Hkv, Dqk]   (decode turns a slice into float64 values,
+                                   e.g. fp8 codes times the per-token scale)
+    vcache  [B, Lmax, Hkv, Dv] or None for MLA (v = k[..., :dv])
+    kv_scale [B, Lmax] per-token scale or None: the entry of token t is
+            decode(code_t) * kv_scale[b, t] (FP8 cache)
+    Returns O [B, Hq, Dv] (0 for an empty range), LSE [B, Hq] (-inf if empty).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, Dqk = q.shape
+    Hkv = kcache.shape[2]
+    G = _group(Hq, Hkv)
+    Dv = dv if vcache is None else vcache.shape[-1]
+    O = np.zeros((B, Hq, Dv))
+    L = np.full((B, Hq), _NEG_INF)
+    for b in (range(B) if batch is None else batch):
+        s0, s1 = int(begin[b]), int(end[b])
+        if s1 <= s0:
+            continue
+        keys = _f64(kcache[b, s0:s1], decode)  # [n, Hkv, Dqk]
+        if kv_scale is not None:
+            keys = keys * np.asarray(kv_scale[b, s0:s1], np.float32).astype(np.float64)[:, None, None]
+        vals = keys[..., :Dv] if vcache is None else _f64(vcache[b, s0:s1], decode)
+        for h in range(Hq):
+            o, lse = attend(q[b, h], keys[:, h // G, :], vals[:, h // G, :], scale)
+            O[b, h] = o
+            L[b, h] = lse
+    return O, L
+
+
+def merge_states(o_parts, lse_parts):
+    """Exact LSE merge of S partial states. o_parts [S, ..., Dv],
+    lse_parts [S, ...]. A state with lse = -inf carries no mass; if every
+    state is empty the result is O = 0, lse = -inf."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = np.max(lse_parts, axis=0)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    tot = np.sum(np.exp(lse_parts - m_safe), axis=0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(np.isfinite(m), m_safe + np.log(tot), _NEG_INF)
+    lse_safe = np.where(np.isfinite(lse), lse, 0.0)
+    w = np.where(np.isfinite(lse)[None], np.exp(lse_parts - lse_safe[None]), 0.0)
+    out = np.sum(w[..., None] * o_parts, axis=0)
+    return out, lse
+
+
+def shard_stats(q, keys, values, scale):
+    """Per-shard statistics of the DeepSeek-V4 notes, section 5:
+    (m_p, l_p, u_p) for one query over one shard's key set."""
+    s = scale * (np.asarray(keys, np.float64) @ np.asarray(q, np.float64))
+    m = np.max(s)
+    e = np.exp(s - m)
+    return m, np.sum(e), e @ np.asarray(values, np.float64)
+
+
+def merge_stats(ms, ls, us):
+    """Global combine of the DeepSeek-V4 notes, section 5: returns (o, Z, m)."""
+    ms = np.asarray(ms, np.float64)
+    m = np.max(ms)
+    w = np.exp(ms - m)
+    Z = np.sum(w * np.asarray(ls, np.float64))
+    o = np.sum(w[:, None] * np.asarray(us, np.float64), axis=0) / Z
+    return o, Z, m
