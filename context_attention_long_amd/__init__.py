@@ -1,0 +1,267 @@
+"""Python binding of libcpattn (context-parallel attention shards, gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+PyTorch supplies device memory and the current stream. The library is built
+in-tree (``python -m context_attention_long_amd.build``); if it is missing,
+every call raises: there is no fallback.
+
+Names follow the C ABI in ``include/cpattn.h``:
+``cp_plan_zigzag``, ``cp_plan_interleave``, ``cp_decode_shards``,
+``attn_prefill_shard``, ``attn_decode_shard``, ``attn_merge_states``.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcpattn.so")
+
+CPA_OK, CPA_E_INVAL, CPA_E_UNSUPPORTED, CPA_E_CAPACITY, CPA_E_HIP = range(5)
+CPA_F32, CPA_BF16, CPA_FP8_E4M3 = 0, 1, 2
+
+_STATUS = {1: "CPA_E_INVAL", 2: "CPA_E_UNSUPPORTED", 3: "CPA_E_CAPACITY", 4: "CPA_E_HIP"}
+
+
+class CpaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class CpaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class CpaSegment(ctypes.Structure):
+    _fields_ = [("req", ctypes.c_int32), ("q_row0", ctypes.c_int32), ("q_len", ctypes.c_int32),
+                ("pos0", ctypes.c_int32), ("pos_stride", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("kv_row0", ctypes.c_int64)]
+
+
+class CpaPlan(ctypes.Structure):
+    _fields_ = [("tok_index", ctypes.POINTER(ctypes.c_int64)), ("pos_id", ctypes.POINTER(ctypes.c_int32)),
+                ("req_id", ctypes.POINTER(ctypes.c_int32)), ("cap_local", ctypes.c_int64),
+                ("seg", ctypes.POINTER(CpaSegment)), ("cap_seg", ctypes.c_int64),
+                ("n_local", ctypes.c_int64), ("n_seg", ctypes.c_int64), ("n_padded", ctypes.c_int64)]
+
+
+SEGMENT_DTYPE = np.dtype([("req", np.int32), ("q_row0", np.int32), ("q_len", np.int32), ("pos0", np.int32),
+                          ("pos_stride", np.int32), ("reserved", np.int32), ("kv_row0", np.int64)])
+assert SEGMENT_DTYPE.itemsize == ctypes.sizeof(CpaSegment) == 32
+
+# exported symbols of include/cpattn.h
+SYMBOLS = ("cpa_last_error", "cpa_abi_version", "cp_plan_zigzag", "cp_plan_interleave", "cp_decode_shards",
+           "attn_prefill_shard", "attn_decode_workspace_size", "attn_decode_shard", "attn_merge_states")
+
+_lib_handle = None
+
+
+def lib():
+    """Load libcpattn.so (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m context_attention_long_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.cpa_last_error.restype = ctypes.c_char_p
+        L.cpa_abi_version.restype = ctypes.c_int32
+        for name in ("cp_plan_zigzag", "cp_plan_interleave"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int32),
+                          P(CpaPlan)]
+        L.cp_decode_shards.restype = ctypes.c_int
+        L.cp_decode_shards.argtypes = [ctypes.c_int64, ctypes.c_int32, P(ctypes.c_int64), P(ctypes.c_int64)]
+        L.attn_prefill_shard.restype = ctypes.c_int
+        L.attn_prefill_shard.argtypes = [P(CpaTensor), P(CpaTensor), P(CpaTensor), P(CpaSegment), ctypes.c_int32,
+                                         ctypes.c_float, P(CpaTensor), P(CpaTensor), ctypes.c_void_p]
+        L.attn_decode_workspace_size.restype = ctypes.c_size_t
+        L.attn_decode_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
+        L.attn_decode_shard.restype = ctypes.c_int
+        L.attn_decode_shard.argtypes = [P(CpaTensor), P(CpaTensor), P(CpaTensor), P(CpaTensor), ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, P(CpaTensor),
+                                        P(CpaTensor), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.attn_merge_states.restype = ctypes.c_int
+        L.attn_merge_states.argtypes = [ctypes.c_int32, P(CpaTensor), P(CpaTensor), P(CpaTensor), P(CpaTensor),
+                                        ctypes.c_void_p]
+        _lib_handle = L
+    return _lib_handle
+
+
+def _check(status):
+    if status != CPA_OK:
+        raise CpaError(status, lib().cpa_last_error().decode())
+
+
+def _i32(a):
+    return (ctypes.c_int32 * len(a))(*[int(x) for x in a])
+
+
+# ------------------------------------------------------------------ planners
+
+class Plan:
+    """Host plan of one rank: numpy arrays tok_index, pos_id, req_id and a
+    structured ``segments`` array (SEGMENT_DTYPE), plus n_padded."""
+
+    def __init__(self, tok_index, pos_id, req_id, segments, n_padded):
+        self.tok_index, self.pos_id, self.req_id = tok_index, pos_id, req_id
+        self.segments, self.n_padded = segments, n_padded
+
+    @property
+    def n_local(self):
+        return len(self.tok_index)
+
+    @property
+    def n_seg(self):
+        return len(self.segments)
+
+
+def _plan(fn_name, C, rank, new_len, prefix_len):
+    f = getattr(lib(), fn_name)
+    n = len(new_len)
+    nl = _i32(new_len)
+    pl = _i32(prefix_len) if prefix_len is not None else None
+    out = CpaPlan()
+    st = f(C, rank, n, nl, pl, ctypes.byref(out))
+    if st not in (CPA_OK, CPA_E_CAPACITY):
+        _check(st)
+    tok = np.empty(out.n_local, np.int64)
+    pos = np.empty(out.n_local, np.int32)
+    req = np.empty(out.n_local, np.int32)
+    seg = np.zeros(out.n_seg, SEGMENT_DTYPE)
+    out.tok_index = tok.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    out.pos_id = pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    out.req_id = req.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    out.cap_local = out.n_local
+    out.seg = seg.ctypes.data_as(ctypes.POINTER(CpaSegment))
+    out.cap_seg = out.n_seg
+    _check(f(C, rank, n, nl, pl, ctypes.byref(out)))
+    return Plan(tok, pos, req, seg, int(out.n_padded))
+
+
+def cp_plan_zigzag(C, rank, new_len, prefix_len=None):
+    return _plan("cp_plan_zigzag", C, rank, new_len, prefix_len)
+
+
+def cp_plan_interleave(C, rank, new_len, prefix_len=None):
+    return _plan("cp_plan_interleave", C, rank, new_len, prefix_len)
+
+
+def cp_decode_shards(L, C):
+    b = (ctypes.c_int64 * C)()
+    e = (ctypes.c_int64 * C)()
+    _check(lib().cp_decode_shards(int(L), int(C), b, e))
+    return list(zip(list(b), list(e)))
+
+
+# ------------------------------------------------------------------ tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def tensor_desc(t, dtype=None):
+    """cpa_tensor for a torch tensor (dtype override for raw FP8 bytes)."""
+    torch = _torch()
+    if dtype is None:
+        dtype = {torch.float32: CPA_F32, torch.bfloat16: CPA_BF16, torch.uint8: CPA_FP8_E4M3}.get(t.dtype)
+        if dtype is None and hasattr(torch, "float8_e4m3fn") and t.dtype == torch.float8_e4m3fn:
+            dtype = CPA_FP8_E4M3
+        if dtype is None:
+            raise TypeError(f"unsupported dtype {t.dtype}")
+    d = CpaTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = dtype
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(d):
+    return ctypes.byref(d) if d is not None else None
+
+
+# ------------------------------------------------------------------ attention
+
+def attn_prefill_shard(q, k, v, segments, softmax_scale, out=None, lse=None, out_dtype=None, stream=None):
+    """Causal attention of local queries q [n_local, Hq, Dqk] against packed
+    k [T_kv, Hkv, Dqk] / v [T_kv, Hkv, Dv] (v=None: MLA, value = k[..., :512]).
+    ``segments``: host structured array (SEGMENT_DTYPE). Returns (out, lse)."""
+    torch = _torch()
+    n_local, Hq = q.shape[0], q.shape[1]
+    Dv = v.shape[-1] if v is not None else 512
+    if out is None:
+        out = torch.empty((n_local, Hq, Dv), dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((n_local, Hq), dtype=torch.float32, device=q.device)
+    seg = np.ascontiguousarray(segments, dtype=SEGMENT_DTYPE)
+    dq, dk, do, dl = tensor_desc(q), tensor_desc(k), tensor_desc(out), tensor_desc(lse)
+    dv = tensor_desc(v) if v is not None else None
+    _check(lib().attn_prefill_shard(ctypes.byref(dq), ctypes.byref(dk), _ptr(dv),
+                                    seg.ctypes.data_as(ctypes.POINTER(CpaSegment)), len(seg),
+                                    float(softmax_scale), ctypes.byref(do), ctypes.byref(dl), _stream(stream)))
+    return out, lse
+
+
+def attn_decode_workspace_size(batch, n_heads_q, head_dim_v, max_shard_len):
+    return int(lib().attn_decode_workspace_size(int(batch), int(n_heads_q), int(head_dim_v), int(max_shard_len)))
+
+
+def attn_decode_shard(q, kcache, vcache, kv_begin, kv_end, max_shard_len, softmax_scale, kv_scale=None,
+                      o_part=None, lse_part=None, workspace=None, stream=None, kcache_dtype=None):
+    """Split-KV decode of one shard. q [B, Hq, Dqk]; kcache [B, Lmax, Hkv, Dqk]
+    (torch.uint8 = FP8 E4M3 bytes, then kv_scale [B, Lmax] f32); vcache or None
+    (MLA); kv_begin / kv_end int32 device tensors [B]. Returns (o_part, lse_part)."""
+    torch = _torch()
+    B, Hq = q.shape[0], q.shape[1]
+    Dv = vcache.shape[-1] if vcache is not None else 512
+    if o_part is None:
+        o_part = torch.empty((B, Hq, Dv), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace_size(B, Hq, Dv, max_shard_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    dq, dk = tensor_desc(q), tensor_desc(kcache, kcache_dtype)
+    dv = tensor_desc(vcache) if vcache is not None else None
+    ds = tensor_desc(kv_scale) if kv_scale is not None else None
+    do, dl = tensor_desc(o_part), tensor_desc(lse_part)
+    for t in (kv_begin, kv_end):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != q.device:
+            raise TypeError("kv_begin / kv_end must be contiguous int32 tensors on the query's device")
+    _check(lib().attn_decode_shard(ctypes.byref(dq), ctypes.byref(dk), _ptr(dv), _ptr(ds),
+                                   ctypes.c_void_p(kv_begin.data_ptr()), ctypes.c_void_p(kv_end.data_ptr()),
+                                   int(max_shard_len), float(softmax_scale), ctypes.byref(do), ctypes.byref(dl),
+                                   ctypes.c_void_p(ws_ptr), ws_bytes, _stream(stream)))
+    return o_part, lse_part
+
+
+def attn_merge_states(o_parts, lse_parts, out=None, lse_out=None, out_dtype=None, stream=None):
+    """Exact LSE merge: o_parts [S, N, H, Dv] f32, lse_parts [S, N, H] f32.
+    Returns (out [N, H, Dv], lse_out [N, H])."""
+    torch = _torch()
+    S, N, H, Dv = o_parts.shape
+    if out is None:
+        out = torch.empty((N, H, Dv), dtype=out_dtype or torch.float32, device=o_parts.device)
+    if lse_out is None:
+        lse_out = torch.empty((N, H), dtype=torch.float32, device=o_parts.device)
+    do, dl, dout, dlo = tensor_desc(o_parts), tensor_desc(lse_parts), tensor_desc(out), tensor_desc(lse_out)
+    _check(lib().attn_merge_states(S, ctypes.byref(do), ctypes.byref(dl), ctypes.byref(dout), ctypes.byref(dlo),
+                                   _stream(stream)))
+    return out, lse_out

@@ -1,0 +1,467 @@
+// C ABI of libcpattn: argument validation on the host, then kernel dispatch.
+// Every check here runs before any launch, so a rejected call touches no
+// device memory. The kernels assume what these checks establish (shapes,
+// strides, segment bounds).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace cpa {
+
+namespace {
+thread_local std::string g_err;
+}
+
+void clear_error() { g_err.clear(); }
+
+cpa_status fail(cpa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+}  // namespace cpa
+
+namespace {
+
+using cpa::fail;
+
+int elem_size(int32_t dt) { return dt == CPA_F32 ? 4 : dt == CPA_BF16 ? 2 : dt == CPA_FP8_E4M3 ? 1 : 0; }
+
+const char* dt_name(int32_t dt) {
+  return dt == CPA_F32 ? "f32" : dt == CPA_BF16 ? "bf16" : dt == CPA_FP8_E4M3 ? "fp8_e4m3" : "?";
+}
+
+// Checks a tensor: non-null, dtype in `dtypes` (bitmask of 1 << dtype), rank,
+// non-negative shape, unit last stride; base and row strides aligned to
+// `align` bytes (16 for tensors moved with 16-byte vector accesses; 0 means
+// the element size, for tensors accessed element by element).
+cpa_status check_tensor(const cpa_tensor* t, const char* name, unsigned dtypes, int ndim, int align = 16) {
+  if (t == nullptr) return fail(CPA_E_INVAL, "%s: descriptor is NULL", name);
+  if (t->ndim != ndim) return fail(CPA_E_INVAL, "%s: ndim %d, expected %d", name, t->ndim, ndim);
+  if (t->dtype < 0 || t->dtype > 2 || !(dtypes & (1u << t->dtype)))
+    return fail(CPA_E_UNSUPPORTED, "%s: dtype %s not supported here", name, dt_name(t->dtype));
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0) return fail(CPA_E_INVAL, "%s: negative shape", name);
+  int64_t numel = 1;
+  for (int i = 0; i < ndim; ++i) numel *= t->shape[i];
+  if (numel == 0) return CPA_OK;
+  if (t->data == nullptr) return fail(CPA_E_INVAL, "%s: data is NULL", name);
+  if (t->stride[ndim - 1] != 1) return fail(CPA_E_INVAL, "%s: last dimension must be contiguous", name);
+  const int es = elem_size(t->dtype);
+  const int al = align > 0 ? align : es;
+  if (((uintptr_t)t->data) % al) return fail(CPA_E_INVAL, "%s: data must be %d-byte aligned", name, al);
+  for (int i = 0; i < ndim - 1; ++i) {
+    if (t->stride[i] < 0) return fail(CPA_E_INVAL, "%s: negative stride", name);
+    if (t->shape[i] > 1 && (t->stride[i] * es) % al)
+      return fail(CPA_E_INVAL, "%s: stride of dim %d must be a multiple of %d bytes", name, i, al);
+  }
+  return CPA_OK;
+}
+
+#define CPA_TRY(x)                      \
+  do {                                  \
+    cpa_status st_ = (x);               \
+    if (st_ != CPA_OK) return st_;      \
+  } while (0)
+
+cpa_status hip_status(int err, const char* what) {
+  if (err != hipSuccess)
+    return fail(CPA_E_HIP, "%s: %s", what, hipGetErrorString((hipError_t)err));
+  return CPA_OK;
+}
+
+int num_cus() {
+  static int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return 256;
+    return cus;
+  }();
+  return n;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- decode split plan: how many workgroups share one request's shard ----
+struct DecodePlan {
+  bool mla;
+  int nsplit;
+};
+
+int mla_nsplit(int64_t B, int64_t max_len) {
+  if (B <= 0) return 1;
+  const int64_t slots = num_cus();                 // one 4-wave workgroup per CU
+  int64_t ns = (slots + B - 1) / B;                // fill the machine once
+  const int64_t by_len = (max_len + 255) / 256;    // at least 256 tokens per split
+  if (ns > by_len) ns = by_len;
+  if (ns < 1) ns = 1;
+  if (ns > 64) ns = 64;
+  return (int)ns;
+}
+
+int gqa_nsplit(int64_t units, int64_t max_len) {
+  if (units <= 0) return 1;
+  int64_t ns = (2 * (int64_t)num_cus() + units - 1) / units;
+  const int64_t by_len = (max_len + 63) / 64;
+  if (ns > by_len) ns = by_len;
+  if (ns < 1) ns = 1;
+  if (ns > 64) ns = 64;
+  return (int)ns;
+}
+
+size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Dv, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const size_t o = (size_t)nsplit * B * Hq * Dv * sizeof(float);
+  const size_t o_al = (o + 255) / 256 * 256;
+  return o_al + (size_t)nsplit * B * Hq * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" const char* cpa_last_error(void) { return cpa::g_err.c_str(); }
+
+extern "C" int32_t cpa_abi_version(void) { return 100; }
+
+// --------------------------------------------------------------------- merge
+
+extern "C" cpa_status attn_merge_states(int32_t n_states, const cpa_tensor* o_parts,
+                                        const cpa_tensor* lse_parts, const cpa_tensor* out,
+                                        const cpa_tensor* lse_out, void* stream) {
+  cpa::clear_error();
+  if (n_states < 1) return fail(CPA_E_INVAL, "merge: n_states = %d < 1", n_states);
+  CPA_TRY(check_tensor(o_parts, "merge o_parts", 1u << CPA_F32, 4));
+  CPA_TRY(check_tensor(lse_parts, "merge lse_parts", 1u << CPA_F32, 3, 0));
+  if (out == nullptr) return fail(CPA_E_INVAL, "merge out: descriptor is NULL");
+  // f32 rows are stored 16 bytes at a time, bf16 rows 8 bytes at a time
+  CPA_TRY(check_tensor(out, "merge out", (1u << CPA_F32) | (1u << CPA_BF16), 3, out->dtype == CPA_BF16 ? 8 : 16));
+  const int64_t S = o_parts->shape[0], N = o_parts->shape[1], H = o_parts->shape[2],
+                Dv = o_parts->shape[3];
+  if (S != n_states) return fail(CPA_E_INVAL, "merge: o_parts has %lld states, n_states = %d", (long long)S, n_states);
+  if (lse_parts->shape[0] != S || lse_parts->shape[1] != N || lse_parts->shape[2] != H)
+    return fail(CPA_E_INVAL, "merge: lse_parts shape does not match o_parts [S, N, H]");
+  if (out->shape[0] != N || out->shape[1] != H || out->shape[2] != Dv)
+    return fail(CPA_E_INVAL, "merge: out shape must be [N, H, Dv]");
+  if (Dv % 4) return fail(CPA_E_UNSUPPORTED, "merge: Dv = %lld must be a multiple of 4", (long long)Dv);
+  if (N > INT32_MAX || H > INT32_MAX || Dv > INT32_MAX) return fail(CPA_E_INVAL, "merge: dims too large");
+  bool has_lse_out = lse_out != nullptr && lse_out->data != nullptr;
+  if (has_lse_out) {
+    CPA_TRY(check_tensor(lse_out, "merge lse_out", 1u << CPA_F32, 2, 0));
+    if (lse_out->shape[0] != N || lse_out->shape[1] != H)
+      return fail(CPA_E_INVAL, "merge: lse_out must be f32 [N, H]");
+  }
+  // lse_parts need not be 16-byte strided: it is read element-wise
+  cpa::MergeArgs a{};
+  a.o = static_cast<const float*>(o_parts->data);
+  a.lse = static_cast<const float*>(lse_parts->data);
+  a.out = out->data;
+  a.lse_out = has_lse_out ? static_cast<float*>(lse_out->data) : nullptr;
+  a.o_s = o_parts->stride[0];
+  a.o_n = o_parts->stride[1];
+  a.o_h = o_parts->stride[2];
+  a.l_s = lse_parts->stride[0];
+  a.l_n = lse_parts->stride[1];
+  a.l_h = lse_parts->stride[2];
+  a.out_n = out->stride[0];
+  a.out_h = out->stride[1];
+  a.lo_n = has_lse_out ? lse_out->stride[0] : 0;
+  a.lo_h = has_lse_out ? lse_out->stride[1] : 0;
+  a.S = (int32_t)S;
+  a.N = (int32_t)N;
+  a.H = (int32_t)H;
+  a.Dv = (int32_t)Dv;
+  a.out_bf16 = out->dtype == CPA_BF16;
+  if (N * H == 0) return CPA_OK;
+  return hip_status(cpa::launch_merge(a, stream), "merge launch");
+}
+
+// -------------------------------------------------------------------- decode
+
+namespace {
+
+cpa_status decode_plan(const cpa_tensor* q, const cpa_tensor* kcache, const cpa_tensor* vcache,
+                       int64_t max_len, DecodePlan* p) {
+  const int64_t B = q->shape[0], Hq = q->shape[1];
+  const int64_t Hkv = kcache->shape[2];
+  p->mla = vcache == nullptr;
+  if (p->mla) {
+    p->nsplit = mla_nsplit(B, max_len);
+  } else {
+    p->nsplit = gqa_nsplit(B * Hkv, max_len);
+  }
+  (void)Hq;
+  return CPA_OK;
+}
+
+}  // namespace
+
+extern "C" size_t attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t head_dim_v,
+                                             int64_t max_shard_len) {
+  // MLA is recognised by its value width; GQA uses the general split rule
+  // (the GQA rule picks fewer splits for more kv heads, so Hkv = 1 bounds it)
+  const int ns = head_dim_v == 512 ? mla_nsplit(batch, max_shard_len) : gqa_nsplit(batch, max_shard_len);
+  return decode_ws_bytes(batch, n_heads_q, head_dim_v, ns);
+}
+
+extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* kcache,
+                                        const cpa_tensor* vcache, const cpa_tensor* kv_scale,
+                                        const int32_t* kv_begin, const int32_t* kv_end,
+                                        int64_t max_shard_len, float softmax_scale,
+                                        const cpa_tensor* o_part, const cpa_tensor* lse_part,
+                                        void* workspace, size_t ws_bytes, void* stream) {
+  cpa::clear_error();
+  CPA_TRY(check_tensor(q, "decode q", (1u << CPA_F32) | (1u << CPA_BF16), 3));
+  CPA_TRY(check_tensor(kcache, "decode kcache", (1u << CPA_F32) | (1u << CPA_BF16) | (1u << CPA_FP8_E4M3), 4));
+  CPA_TRY(check_tensor(o_part, "decode o_part", 1u << CPA_F32, 3));
+  CPA_TRY(check_tensor(lse_part, "decode lse_part", 1u << CPA_F32, 2, 0));
+  const int64_t B = q->shape[0], Hq = q->shape[1], Dqk = q->shape[2];
+  const int64_t Lmax = kcache->shape[1], Hkv = kcache->shape[2];
+  if (kcache->shape[0] != B || kcache->shape[3] != Dqk)
+    return fail(CPA_E_INVAL, "decode: kcache must be [B, Lmax, Hkv, Dqk] matching q");
+  if (Hkv < 1 || Hq % Hkv) return fail(CPA_E_INVAL, "decode: Hq = %lld not a multiple of Hkv = %lld", (long long)Hq, (long long)Hkv);
+  if (Lmax > INT32_MAX || B > INT32_MAX) return fail(CPA_E_INVAL, "decode: sizes too large");
+  if (max_shard_len < 0) return fail(CPA_E_INVAL, "decode: max_shard_len < 0");
+  if (!std::isfinite(softmax_scale)) return fail(CPA_E_INVAL, "decode: softmax_scale is not finite");
+  if (B > 0 && (kv_begin == nullptr || kv_end == nullptr)) return fail(CPA_E_INVAL, "decode: kv_begin/kv_end NULL");
+  const bool fp8 = kcache->dtype == CPA_FP8_E4M3;
+  int64_t Dv;
+  if (vcache == nullptr) {
+    // MLA: value = first 512 dims of the 576-dim latent
+    if (Hkv != 1 || Dqk != 576) return fail(CPA_E_UNSUPPORTED, "decode: MLA needs Hkv = 1 and Dqk = 576");
+    if (Hq != 64) return fail(CPA_E_UNSUPPORTED, "decode: MLA kernel is built for 64 query heads, got %lld", (long long)Hq);
+    if (q->dtype != CPA_BF16) return fail(CPA_E_UNSUPPORTED, "decode: MLA needs a bf16 query");
+    if (kcache->dtype == CPA_F32) return fail(CPA_E_UNSUPPORTED, "decode: MLA cache must be bf16 or fp8");
+    // the kernel addresses a 32-token tile with 32-bit per-thread offsets
+    if (kcache->stride[1] > (int64_t)1 << 26) return fail(CPA_E_INVAL, "decode: kcache token stride too large");
+    Dv = 512;
+  } else {
+    CPA_TRY(check_tensor(vcache, "decode vcache", (1u << CPA_F32) | (1u << CPA_BF16), 4));
+    if (vcache->dtype != kcache->dtype) return fail(CPA_E_INVAL, "decode: vcache dtype differs from kcache");
+    if (fp8) return fail(CPA_E_UNSUPPORTED, "decode: FP8 is supported for the MLA latent cache only");
+    if (vcache->shape[0] != B || vcache->shape[1] != Lmax || vcache->shape[2] != Hkv)
+      return fail(CPA_E_INVAL, "decode: vcache must be [B, Lmax, Hkv, Dv]");
+    Dv = vcache->shape[3];
+    if (Dv != Dqk) return fail(CPA_E_UNSUPPORTED, "decode: GQA needs Dv == Dqk");
+    if (Dqk > 256 || Dqk < 8 || Dqk % 8) return fail(CPA_E_UNSUPPORTED, "decode: GQA head dim must be a multiple of 8 in [8, 256]");
+    if ((Hq / Hkv) * Dqk > 8192) return fail(CPA_E_UNSUPPORTED, "decode: GQA group * head dim > 8192");
+  }
+  if (fp8) {
+    if (kv_scale == nullptr || kv_scale->data == nullptr) return fail(CPA_E_INVAL, "decode: FP8 cache needs kv_scale");
+    CPA_TRY(check_tensor(kv_scale, "decode kv_scale", 1u << CPA_F32, 2, 0));
+    if (kv_scale->shape[0] != B || kv_scale->shape[1] != Lmax)
+      return fail(CPA_E_INVAL, "decode: kv_scale must be f32 [B, Lmax]");
+  } else if (kv_scale != nullptr && kv_scale->data != nullptr) {
+    return fail(CPA_E_INVAL, "decode: kv_scale is only for an FP8 cache");
+  }
+  if (o_part->shape[0] != B || o_part->shape[1] != Hq || o_part->shape[2] != Dv)
+    return fail(CPA_E_INVAL, "decode: o_part must be [B, Hq, Dv]");
+  if (lse_part->shape[0] != B || lse_part->shape[1] != Hq) return fail(CPA_E_INVAL, "decode: lse_part must be [B, Hq]");
+  if (B == 0 || Hq == 0) return CPA_OK;
+
+  DecodePlan p{};
+  CPA_TRY(decode_plan(q, kcache, vcache, max_shard_len, &p));
+  const size_t need = decode_ws_bytes(B, Hq, Dv, p.nsplit);
+  if (ws_bytes < need || (need > 0 && workspace == nullptr))
+    return fail(CPA_E_CAPACITY, "decode: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (need > 0 && ((uintptr_t)workspace) % 256) return fail(CPA_E_INVAL, "decode: workspace must be 256-byte aligned");
+
+  // partial-state destination: the caller's buffers directly, or the split
+  // scratch [nsplit, B, Hq, Dv] + [nsplit, B, Hq] followed by a merge
+  float* po;
+  float* pl;
+  int64_t po_s, po_b, po_h, pl_s, pl_b, pl_h;
+  if (p.nsplit == 1) {
+    po = static_cast<float*>(o_part->data);
+    pl = static_cast<float*>(lse_part->data);
+    po_s = 0, po_b = o_part->stride[0], po_h = o_part->stride[1];
+    pl_s = 0, pl_b = lse_part->stride[0], pl_h = lse_part->stride[1];
+  } else {
+    po = static_cast<float*>(workspace);
+    const size_t o_bytes = (size_t)p.nsplit * B * Hq * Dv * sizeof(float);
+    pl = reinterpret_cast<float*>(static_cast<char*>(workspace) + (o_bytes + 255) / 256 * 256);
+    po_h = Dv, po_b = Hq * Dv, po_s = B * Hq * Dv;
+    pl_h = 1, pl_b = Hq, pl_s = B * Hq;
+  }
+
+  int err;
+  if (p.mla) {
+    cpa::DecodeMlaArgs a{};
+    a.q = static_cast<const uint16_t*>(q->data);
+    a.cache = kcache->data;
+    a.kv_scale = fp8 ? static_cast<const float*>(kv_scale->data) : nullptr;
+    a.kv_begin = kv_begin;
+    a.kv_end = kv_end;
+    a.o = po;
+    a.lse = pl;
+    a.q_b = q->stride[0];
+    a.q_h = q->stride[1];
+    a.c_b = kcache->stride[0];
+    a.c_t = kcache->stride[1];
+    a.s_b = fp8 ? kv_scale->stride[0] : 0;
+    a.s_t = fp8 ? kv_scale->stride[1] : 0;
+    a.o_s = po_s, a.o_b = po_b, a.o_h = po_h;
+    a.l_s = pl_s, a.l_b = pl_b, a.l_h = pl_h;
+    a.B = (int32_t)B;
+    a.H = (int32_t)Hq;
+    a.Lmax = (int32_t)Lmax;
+    a.nsplit = p.nsplit;
+    a.fp8 = fp8;
+    a.scale_log2 = softmax_scale * kLog2e;
+    err = cpa::launch_decode_mla(a, stream);
+  } else {
+    cpa::DecodeGqaArgs a{};
+    a.q = q->data;
+    a.k = kcache->data;
+    a.v = vcache->data;
+    a.kv_begin = kv_begin;
+    a.kv_end = kv_end;
+    a.o = po;
+    a.lse = pl;
+    a.q_b = q->stride[0];
+    a.q_h = q->stride[1];
+    a.k_b = kcache->stride[0], a.k_t = kcache->stride[1], a.k_h = kcache->stride[2];
+    a.v_b = vcache->stride[0], a.v_t = vcache->stride[1], a.v_h = vcache->stride[2];
+    a.o_s = po_s, a.o_b = po_b, a.o_h = po_h;
+    a.l_s = pl_s, a.l_b = pl_b, a.l_h = pl_h;
+    a.B = (int32_t)B;
+    a.Hq = (int32_t)Hq;
+    a.Hkv = (int32_t)Hkv;
+    a.D = (int32_t)Dqk;
+    a.Lmax = (int32_t)Lmax;
+    a.nsplit = p.nsplit;
+    a.q_bf16 = q->dtype == CPA_BF16;
+    a.kv_dtype = kcache->dtype;
+    a.scale_log2 = softmax_scale * kLog2e;
+    err = cpa::launch_decode_gqa(a, stream);
+  }
+  CPA_TRY(hip_status(err, "decode launch"));
+  if (p.nsplit > 1) {
+    cpa::MergeArgs m{};
+    m.o = po;
+    m.lse = pl;
+    m.out = o_part->data;
+    m.lse_out = static_cast<float*>(lse_part->data);
+    m.o_s = po_s, m.o_n = po_b, m.o_h = po_h;
+    m.l_s = pl_s, m.l_n = pl_b, m.l_h = pl_h;
+    m.out_n = o_part->stride[0], m.out_h = o_part->stride[1];
+    m.lo_n = lse_part->stride[0], m.lo_h = lse_part->stride[1];
+    m.S = p.nsplit;
+    m.N = (int32_t)B;
+    m.H = (int32_t)Hq;
+    m.Dv = (int32_t)Dv;
+    m.out_bf16 = 0;
+    CPA_TRY(hip_status(cpa::launch_merge(m, stream), "decode split merge launch"));
+  }
+  return CPA_OK;
+}
+
+// ------------------------------------------------------------------- prefill
+
+namespace {
+
+// Every segment must stay inside q / out / lse rows and the packed K/V rows;
+// segments must not share q rows (they would race on the same outputs).
+cpa_status check_segments(const cpa_segment* seg, int32_t n_seg, int64_t n_local, int64_t T_kv) {
+  if (n_seg < 0) return fail(CPA_E_INVAL, "prefill: n_seg < 0");
+  if (n_seg > 0 && seg == nullptr) return fail(CPA_E_INVAL, "prefill: segments are NULL");
+  std::vector<std::pair<int64_t, int64_t>> spans;
+  for (int32_t i = 0; i < n_seg; ++i) {
+    const cpa_segment& s = seg[i];
+    if (s.q_len < 0 || s.q_row0 < 0 || s.pos0 < 0 || s.kv_row0 < 0)
+      return fail(CPA_E_INVAL, "prefill: segment %d has a negative field", i);
+    if (s.q_len == 0) continue;
+    if (s.q_len > 1 && s.pos_stride < 1) return fail(CPA_E_INVAL, "prefill: segment %d has pos_stride < 1", i);
+    if ((int64_t)s.q_row0 + s.q_len > n_local)
+      return fail(CPA_E_INVAL, "prefill: segment %d rows [%d, %lld) exceed n_local = %lld", i, s.q_row0,
+                  (long long)s.q_row0 + s.q_len, (long long)n_local);
+    const int64_t last = (int64_t)s.pos0 + (int64_t)(s.q_len - 1) * (s.q_len > 1 ? s.pos_stride : 0);
+    if (last > INT32_MAX) return fail(CPA_E_INVAL, "prefill: segment %d positions exceed int32", i);
+    if (s.kv_row0 + last + 1 > T_kv)
+      return fail(CPA_E_INVAL, "prefill: segment %d reads K/V rows up to %lld but T_kv = %lld", i,
+                  (long long)(s.kv_row0 + last + 1), (long long)T_kv);
+    spans.emplace_back(s.q_row0, (int64_t)s.q_row0 + s.q_len);
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].first < spans[i - 1].second) return fail(CPA_E_INVAL, "prefill: segments overlap in q rows");
+  return CPA_OK;
+}
+
+}  // namespace
+
+extern "C" cpa_status attn_prefill_shard(const cpa_tensor* q, const cpa_tensor* k, const cpa_tensor* v,
+                                         const cpa_segment* seg, int32_t n_seg, float softmax_scale,
+                                         const cpa_tensor* out, const cpa_tensor* lse, void* stream) {
+  cpa::clear_error();
+  CPA_TRY(check_tensor(q, "prefill q", 1u << CPA_BF16, 3));
+  CPA_TRY(check_tensor(k, "prefill k", 1u << CPA_BF16, 3));
+  CPA_TRY(check_tensor(out, "prefill out", (1u << CPA_BF16) | (1u << CPA_F32), 3));
+  CPA_TRY(check_tensor(lse, "prefill lse", 1u << CPA_F32, 2, 0));
+  const int64_t n_local = q->shape[0], Hq = q->shape[1], Dqk = q->shape[2];
+  const int64_t T_kv = k->shape[0], Hkv = k->shape[1];
+  if (k->shape[2] != Dqk) return fail(CPA_E_INVAL, "prefill: k head dim differs from q");
+  if (Hkv < 1 || Hq % Hkv) return fail(CPA_E_INVAL, "prefill: Hq = %lld not a multiple of Hkv = %lld", (long long)Hq, (long long)Hkv);
+  if (!std::isfinite(softmax_scale)) return fail(CPA_E_INVAL, "prefill: softmax_scale is not finite");
+  if (n_local > INT32_MAX || T_kv > ((int64_t)1 << 40)) return fail(CPA_E_INVAL, "prefill: sizes too large");
+  int64_t Dv;
+  if (v == nullptr) {
+    if (Hkv != 1 || Dqk != 576) return fail(CPA_E_UNSUPPORTED, "prefill: MLA (v = NULL) needs Hkv = 1 and Dqk = 576");
+    Dv = 512;
+  } else {
+    CPA_TRY(check_tensor(v, "prefill v", 1u << CPA_BF16, 3));
+    if (v->shape[0] != T_kv || v->shape[1] != Hkv) return fail(CPA_E_INVAL, "prefill: v must be [T_kv, Hkv, Dv]");
+    Dv = v->shape[2];
+  }
+  if (out->shape[0] != n_local || out->shape[1] != Hq || out->shape[2] != Dv)
+    return fail(CPA_E_INVAL, "prefill: out must be [n_local, Hq, Dv]");
+  if (lse->shape[0] != n_local || lse->shape[1] != Hq) return fail(CPA_E_INVAL, "prefill: lse must be [n_local, Hq]");
+  CPA_TRY(check_segments(seg, n_seg, n_local, T_kv));
+  if (n_local == 0 || n_seg == 0) return CPA_OK;
+  if (v != nullptr) {
+    if (Dqk != 128 || Dv != 128) return fail(CPA_E_UNSUPPORTED, "prefill: GQA kernel is built for head dim 128");
+    const int64_t G = Hq / Hkv;
+    if (G > 128 || (128 % G) != 0) return fail(CPA_E_UNSUPPORTED, "prefill: Hq / Hkv = %lld must divide 128", (long long)G);
+    cpa::PrefillGqaArgs a{};
+    a.q = static_cast<const uint16_t*>(q->data);
+    a.k = static_cast<const uint16_t*>(k->data);
+    a.v = static_cast<const uint16_t*>(v->data);
+    a.out = out->data;
+    a.lse = static_cast<float*>(lse->data);
+    a.q_n = q->stride[0], a.q_h = q->stride[1];
+    a.k_t = k->stride[0], a.k_h = k->stride[1];
+    a.v_t = v->stride[0], a.v_h = v->stride[1];
+    a.o_n = out->stride[0], a.o_h = out->stride[1];
+    a.l_n = lse->stride[0], a.l_h = lse->stride[1];
+    a.Hkv = (int32_t)Hkv;
+    a.G = (int32_t)G;
+    a.out_bf16 = out->dtype == CPA_BF16;
+    a.scale_log2 = softmax_scale * kLog2e;
+    return hip_status(cpa::launch_prefill_gqa(a, seg, n_seg, stream), "prefill launch");
+  }
+  if (Hq != 64) return fail(CPA_E_UNSUPPORTED, "prefill: MLA kernel is built for 64 query heads, got %lld", (long long)Hq);
+  if (k->stride[0] > ((int64_t)1 << 40)) return fail(CPA_E_INVAL, "prefill: latent stride too large");
+  cpa::PrefillMlaArgs a{};
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.lat = static_cast<const uint16_t*>(k->data);
+  a.out = out->data;
+  a.lse = static_cast<float*>(lse->data);
+  a.q_n = q->stride[0], a.q_h = q->stride[1];
+  a.k_t = k->stride[0];
+  a.o_n = out->stride[0], a.o_h = out->stride[1];
+  a.l_n = lse->stride[0], a.l_h = lse->stride[1];
+  a.out_bf16 = out->dtype == CPA_BF16;
+  a.scale_log2 = softmax_scale * kLog2e;
+  return hip_status(cpa::launch_prefill_mla(a, seg, n_seg, stream), "prefill launch");
+}

@@ -1,0 +1,96 @@
+// Internal declarations of libcpattn: error state, tensor views handed to the
+// kernels, and the kernel launchers. Not part of the ABI.
+#pragma once
+
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+
+#include "cpattn.h"
+
+namespace cpa {
+
+// Thread-local last-error message (cpa_last_error).
+void clear_error();
+cpa_status fail(cpa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// ---- kernel-side argument blocks (plain data, passed by value) ----
+
+struct MergeArgs {
+  const float* o;       // [S, N, H, Dv]
+  const float* lse;     // [S, N, H]
+  void* out;            // [N, H, Dv] f32 or bf16
+  float* lse_out;       // [N, H] or null
+  int64_t o_s, o_n, o_h;        // element strides of o (Dv contiguous)
+  int64_t l_s, l_n, l_h;        // strides of lse
+  int64_t out_n, out_h;         // strides of out
+  int64_t lo_n, lo_h;           // strides of lse_out
+  int32_t S, N, H, Dv;
+  int32_t out_bf16;
+};
+
+struct DecodeGqaArgs {
+  const void* q;        // [B, Hq, D] f32 or bf16
+  const void* k;        // [B, Lmax, Hkv, D]
+  const void* v;        // [B, Lmax, Hkv, D]
+  const int32_t* kv_begin;
+  const int32_t* kv_end;
+  float* o;             // [nsplit, B, Hq, D] (or o_part when nsplit == 1)
+  float* lse;           // [nsplit, B, Hq]
+  int64_t q_b, q_h;
+  int64_t k_b, k_t, k_h;
+  int64_t v_b, v_t, v_h;
+  int64_t o_s, o_b, o_h;        // strides of the partial output
+  int64_t l_s, l_b, l_h;
+  int32_t B, Hq, Hkv, D, Lmax, nsplit;
+  int32_t q_bf16, kv_dtype;
+  float scale_log2;             // softmax scale * log2(e)
+};
+
+struct DecodeMlaArgs {
+  const uint16_t* q;    // [B, H, 576] bf16
+  const void* cache;    // [B, Lmax, 576] bf16 words or E4M3 bytes (one kv head)
+  const float* kv_scale;  // [B, Lmax] (FP8) or null
+  const int32_t* kv_begin;
+  const int32_t* kv_end;
+  float* o;             // [nsplit, B, H, 512]
+  float* lse;           // [nsplit, B, H]
+  int64_t q_b, q_h;
+  int64_t c_b, c_t;     // cache strides (elements of its dtype)
+  int64_t s_b, s_t;     // kv_scale strides
+  int64_t o_s, o_b, o_h;
+  int64_t l_s, l_b, l_h;
+  int32_t B, H, Lmax, nsplit;
+  int32_t fp8;
+  float scale_log2;
+};
+
+struct PrefillGqaArgs {
+  const uint16_t* q;    // [n_local, Hq, 128] bf16
+  const uint16_t* k;    // [T_kv, Hkv, 128]
+  const uint16_t* v;    // [T_kv, Hkv, 128]
+  void* out;            // [n_local, Hq, 128] bf16 or f32
+  float* lse;           // [n_local, Hq]
+  int64_t q_n, q_h, k_t, k_h, v_t, v_h, o_n, o_h, l_n, l_h;
+  int32_t Hkv, G, out_bf16;
+  float scale_log2;
+};
+
+struct PrefillMlaArgs {
+  const uint16_t* q;    // [n_local, 64, 576] bf16
+  const uint16_t* lat;  // [T_kv, 1, 576] latent (value = first 512 dims)
+  void* out;            // [n_local, 64, 512] bf16 or f32
+  float* lse;           // [n_local, 64]
+  int64_t q_n, q_h, k_t, o_n, o_h, l_n, l_h;
+  int32_t out_bf16;
+  float scale_log2;
+};
+
+// ---- launchers (return hipSuccess or the launch error) ----
+int launch_merge(const MergeArgs& a, void* stream);
+int launch_decode_gqa(const DecodeGqaArgs& a, void* stream);
+int launch_decode_mla(const DecodeMlaArgs& a, void* stream);
+int launch_prefill_gqa(const PrefillGqaArgs& a, const cpa_segment* seg, int n_seg, void* stream);
+int launch_prefill_mla(const PrefillMlaArgs& a, const cpa_segment* seg, int n_seg, void* stream);
+
+}  // namespace cpa

@@ -1,0 +1,217 @@
+/*
+ * cpattn.h -- context-parallel attention shards for MI355X (gfx950).
+ *
+ * One rank's share of long-context attention, as the source pages state the
+ * problem:
+ *   - "How GPUs Share a Long Context During LLM Inference" (vincentzed.com),
+ *     cited as Long Context below, sections 1-3;
+ *   - SGLang documentation "Prefill context parallelism" (strategy interface,
+ *     zigzag and interleave strategies);
+ *   - vLLM "Decode Context Parallelism" post (contiguous token chunks, MLA and
+ *     GQA backends);
+ *   - "DeepSeek-V4 Attention Inference Systems" notes, section 5 (exact
+ *     partial-softmax combine).
+ *
+ * Conventions shared by every call:
+ *   - Plain C ABI. No exception crosses it. Every call returns a cpa_status;
+ *     on failure cpa_last_error() returns a message for the calling thread.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t passed as
+ *     void*; NULL is the null stream), allocate nothing and own nothing: the
+ *     caller owns every buffer and keeps it alive until the stream is done.
+ *   - Tensors are described by cpa_tensor with strides in elements; the last
+ *     dimension must be contiguous (stride 1) and the data pointer 16-byte
+ *     aligned. Arguments are validated on the host before any launch; a
+ *     validation failure launches nothing.
+ *   - LSE is the natural log of the sum of exponentiated scores (Long
+ *     Context 3.3); an empty key set gives O = 0 and LSE = -inf.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cpa_status {
+  CPA_OK = 0,
+  CPA_E_INVAL = 1,        /* null pointer, bad shape, dtype, stride or alignment */
+  CPA_E_UNSUPPORTED = 2,  /* head dims or dtype combination this build has no kernel for */
+  CPA_E_CAPACITY = 3,     /* a caller array or workspace is too small; sizes written back */
+  CPA_E_HIP = 4           /* the HIP runtime reported an error at launch */
+} cpa_status;
+
+typedef enum cpa_dtype {
+  CPA_F32 = 0,
+  CPA_BF16 = 1,
+  CPA_FP8_E4M3 = 2  /* OCP E4M3FN bytes: bias 7, max 448, no infinity */
+} cpa_dtype;
+
+typedef struct cpa_tensor {
+  void* data;         /* device pointer */
+  int32_t dtype;      /* cpa_dtype */
+  int32_t ndim;       /* 1..4 */
+  int64_t shape[4];
+  int64_t stride[4];  /* elements; stride[ndim-1] must be 1 */
+} cpa_tensor;
+
+/*
+ * A segment is a run of a rank's local query rows of one request whose
+ * positions step by a constant: local row q_row0 + i (0 <= i < q_len) has
+ * position pos0 + i * pos_stride inside its request (cached prefix
+ * included) and reads keys 0 .. that position, diagonal included (Long
+ * Context 1.1). In the packed full K/V, request `req` starts at row kv_row0
+ * and holds its prefix and new tokens in original order, so the row reads
+ * K/V rows [kv_row0, kv_row0 + pos0 + i * pos_stride + 1).
+ *   zigzag:     stride 1, one segment per non-empty block; the block's
+ *               "where the reads end" (Long Context 2.3) is pos0 + q_len.
+ *   interleave: stride C, one segment per request (each query's own causal
+ *               extent, SGLang docs "Interleave strategy").
+ */
+typedef struct cpa_segment {
+  int32_t req;
+  int32_t q_row0;
+  int32_t q_len;
+  int32_t pos0;
+  int32_t pos_stride;
+  int32_t reserved;   /* set to 0 */
+  int64_t kv_row0;
+} cpa_segment;
+
+/*
+ * Output of the planners (host memory, owned by the caller). The planner
+ * fills at most cap_local rows and cap_seg segments. It always writes
+ * n_local, n_seg and n_padded; if either capacity is too small it writes
+ * nothing else and returns CPA_E_CAPACITY, so a first call with zero
+ * capacities (and NULL arrays) returns the sizes to allocate.
+ */
+typedef struct cpa_plan {
+  int64_t* tok_index;   /* [cap_local] index into the batch's new tokens, flattened request by request */
+  int32_t* pos_id;      /* [cap_local] original position inside the request, prefix included */
+  int32_t* req_id;      /* [cap_local] request of the row */
+  int64_t cap_local;
+  cpa_segment* seg;     /* [cap_seg] */
+  int64_t cap_seg;
+  int64_t n_local;      /* rows owned by this rank */
+  int64_t n_seg;        /* segments written */
+  int64_t n_padded;     /* rows of the largest rank's share (padded buffer size) */
+} cpa_plan;
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* cpa_last_error(void);
+
+/* ABI version of this library (major * 100 + minor). */
+int32_t cpa_abi_version(void);
+
+/*
+ * Zigzag prefill plan. SGLang docs "Zigzag strategy"; Long Context 2.3.
+ * Each request's new tokens are cut into 2C contiguous blocks, the first
+ * (L mod 2C) blocks holding one extra token; rank `rank` takes blocks rank
+ * and 2C-1-rank, request by request, early block first. A cached prefix is
+ * not split and is read by both blocks. Host-only, synchronous, pure.
+ *   C >= 1, 0 <= rank < C, n_req >= 0, new_len[n_req] >= 0,
+ *   prefix_len[n_req] >= 0 or NULL for no prefix.
+ * Errors: CPA_E_INVAL for bad arguments or a batch larger than 2^31-1 new
+ * or packed tokens; CPA_E_CAPACITY as described at cpa_plan.
+ */
+cpa_status cp_plan_zigzag(int32_t C, int32_t rank, int32_t n_req, const int32_t* new_len,
+                          const int32_t* prefix_len, cpa_plan* out);
+
+/*
+ * Interleave prefill plan. SGLang docs "Interleave strategy"; Long Context
+ * 2.4. Rank `rank` owns flattened new-token indices rank, rank+C, ... of the
+ * whole batch (no reset at request boundaries), in ascending order; position
+ * ids keep their original values. One segment of stride C per request that
+ * owns a row. n_padded = ceil(T / C). Arguments and errors as for
+ * cp_plan_zigzag.
+ */
+cpa_status cp_plan_interleave(int32_t C, int32_t rank, int32_t n_req, const int32_t* new_len,
+                              const int32_t* prefix_len, cpa_plan* out);
+
+/*
+ * Contiguous decode shards of an L-token context over C ranks (vLLM DCP
+ * post, section 4: GPU c holds a contiguous chunk of token positions); the
+ * early shards take the remainder. Writes begin[C], end[C] (host arrays).
+ */
+cpa_status cp_decode_shards(int64_t L, int32_t C, int64_t* begin, int64_t* end);
+
+/*
+ * Causal attention of a rank's local queries against their true causal
+ * history (Long Context 2.1 and 2.3: partial Q against the full, gathered
+ * K/V; the cached prefix included).
+ *   q    [n_local, Hq, Dqk]  bf16   local queries in plan order
+ *   k    [T_kv, Hkv, Dqk]    bf16   packed keys (see cpa_segment)
+ *   v    [T_kv, Hkv, Dv]     bf16   packed values, or NULL for MLA, where the
+ *                                   value of a token is the first Dv dims of
+ *                                   its latent vector k (Long Context 1.3;
+ *                                   vLLM GLM-5.3 post footnote 1: QK over 576,
+ *                                   PV over 512)
+ *   seg  [n_seg]             HOST   segments (e.g. from a planner); each is
+ *                                   bounds-checked against q, k and out
+ *   out  [n_local, Hq, Dv]   bf16 or f32 (written for rows covered by a segment)
+ *   lse  [n_local, Hq]       f32
+ * Query head h uses kv head h / (Hq / Hkv). Supported head dims: GQA
+ * Dqk = Dv = 128; MLA (v NULL, Hkv = 1) Dqk = 576, Dv = 512.
+ * Segments must not overlap in q rows. Rows not covered by a segment are not
+ * written.
+ */
+cpa_status attn_prefill_shard(const cpa_tensor* q, const cpa_tensor* k, const cpa_tensor* v,
+                              const cpa_segment* seg, int32_t n_seg, float softmax_scale,
+                              const cpa_tensor* out, const cpa_tensor* lse, void* stream);
+
+/*
+ * Bytes of workspace attn_decode_shard needs for this shape (0 is possible).
+ * max_shard_len is the longest kv_end - kv_begin of the batch.
+ */
+size_t attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t head_dim_v,
+                                  int64_t max_shard_len);
+
+/*
+ * Split-KV decode on one shard (Long Context 3.2-3.4; vLLM DCP post 4.1):
+ * for request b and query head h, attention of the single query q[b, h]
+ * over cache rows [kv_begin[b], kv_end[b]) of request b, emitting the
+ * partial output and its LSE for the merge.
+ *   q        [B, Hq, Dqk]          bf16 or f32
+ *   kcache   [B, Lmax, Hkv, Dqk]   f32, bf16 or FP8 E4M3
+ *   vcache   [B, Lmax, Hkv, Dv]    same dtype as kcache, or NULL for MLA
+ *                                  (value = first Dv dims of the latent)
+ *   kv_scale [B, Lmax] f32         per-token scale, required for FP8 and
+ *                                  otherwise NULL: entry = e4m3 * scale
+ *   kv_begin, kv_end [B] int32     DEVICE arrays; clamped to [0, Lmax] and
+ *                                  an empty range gives O = 0, LSE = -inf
+ *   max_shard_len                  upper bound of kv_end - kv_begin, used to
+ *                                  size the internal split (any length is
+ *                                  still processed in full)
+ *   o_part   [B, Hq, Dv] f32, lse_part [B, Hq] f32
+ *   workspace / ws_bytes           device scratch of at least
+ *                                  attn_decode_workspace_size(...) bytes
+ * Supported: MLA (Hkv = 1, Dqk = 576, Dv = 512, q bf16, cache bf16 or FP8)
+ * and GQA (Dqk = Dv <= 256, any dtype listed).
+ */
+cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* kcache, const cpa_tensor* vcache,
+                             const cpa_tensor* kv_scale, const int32_t* kv_begin,
+                             const int32_t* kv_end, int64_t max_shard_len, float softmax_scale,
+                             const cpa_tensor* o_part, const cpa_tensor* lse_part, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * Exact LSE merge of S partial states (Long Context 3.3; DeepSeek-V4 notes,
+ * section 5): lse = log sum_c exp(lse_c), O = sum_c exp(lse_c - lse) O_c.
+ *   o_parts   [S, N, H, Dv] f32
+ *   lse_parts [S, N, H]     f32
+ *   out       [N, H, Dv]    f32 or bf16
+ *   lse_out   [N, H]        f32, or data NULL to skip
+ * A state with LSE = -inf carries no mass; if all are -inf the row gets
+ * O = 0 and LSE = -inf (no NaN). S = 1 copies.
+ */
+cpa_status attn_merge_states(int32_t n_states, const cpa_tensor* o_parts,
+                             const cpa_tensor* lse_parts, const cpa_tensor* out,
+                             const cpa_tensor* lse_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

@@ -1,0 +1,69 @@
+"""Shared helpers of the GPU parity tests: device upload of stored bits and
+the tolerance gates. No method arithmetic here."""
+
+import numpy as np
+
+# Gates (stated with the workloads): fp32 inputs -> 1e-4 relative; bf16 / fp8
+# inputs -> O max-abs 2e-2 and LSE max-abs 1e-3, against the float64 oracle on
+# the same stored bits.
+F32_REL = 1e-4
+LP_O_ABS = 2e-2
+LP_LSE_ABS = 1e-3
+
+
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def bf16_tensor(bits, device=None):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device or dev())
+
+
+def f32_tensor(x, device=None):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device or dev())
+
+
+def u8_tensor(x, device=None):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(device or dev())
+
+
+def i32_tensor(x, device=None):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(device or dev())
+
+
+def host(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def check_f32(o, lse, o_ref, lse_ref, what=""):
+    """fp32 gate: max|dO| / max|O_ref| <= 1e-4; |dLSE| <= 1e-4 * max(1, |LSE|);
+    -inf LSE must match exactly."""
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lse_ref)), what
+    fin = np.isfinite(lse_ref)
+    err_o = np.max(np.abs(o - o_ref)) / max(np.max(np.abs(o_ref)), 1e-30)
+    err_l = np.max(np.abs(lse[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))) if fin.any() else 0.0
+    assert not np.any(np.isnan(o)), what
+    assert err_o <= F32_REL, f"{what}: O rel err {err_o:.3g}"
+    assert err_l <= F32_REL, f"{what}: LSE rel err {err_l:.3g}"
+    return err_o, err_l
+
+
+def check_lowp(o, lse, o_ref, lse_ref, what=""):
+    """bf16/fp8 gate: O max-abs <= 2e-2, LSE max-abs <= 1e-3."""
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lse_ref)), what
+    fin = np.isfinite(lse_ref)
+    assert not np.any(np.isnan(o)), what
+    err_o = float(np.max(np.abs(o - o_ref))) if o.size else 0.0
+    err_l = float(np.max(np.abs(lse[fin] - lse_ref[fin]))) if fin.any() else 0.0
+    rel = err_o / max(float(np.max(np.abs(o_ref))) if o.size else 1.0, 1e-30)
+    assert err_o <= LP_O_ABS, f"{what}: O max-abs {err_o:.3g}"
+    assert err_l <= LP_LSE_ABS, f"{what}: LSE max-abs {err_l:.3g}"
+    return err_o, err_l, rel

@@ -1,0 +1,194 @@
+"""GPU parity: LSE merge and split-KV decode shards against the oracle."""
+
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import attention as att
+from oracle import formats, plans
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cpa():
+    import torch
+    import context_attention_long_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.lib()
+    return m
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def test_merge_worked_example_fig8(cpa, golden_dir):
+    import json, os
+    g = json.load(open(os.path.join(golden_dir, "merge_fig8.json")))
+    # shard outputs and LSEs of the example: V = I4, GPU0 {0,2}, GPU1 {1,3}
+    o = np.zeros((2, 1, 1, 4))
+    o[0, 0, 0, [0, 2]] = g["local_probs"][0]
+    o[1, 0, 0, [1, 3]] = g["local_probs"][1]
+    lse = np.log(np.array(g["local_sums"], dtype=np.float64)).reshape(2, 1, 1)
+    out, lo = cpa.attn_merge_states(H.f32_tensor(o), H.f32_tensor(lse))
+    _sync()
+    assert np.allclose(H.host(out)[0, 0], g["true_probs"], atol=1e-6)
+    assert abs(H.host(lo)[0, 0] - math.log(8)) < 1e-6
+
+
+@pytest.mark.parametrize("S,N,Hh,Dv", [(1, 3, 5, 8), (4, 7, 3, 128), (8, 64, 64, 512), (3, 2, 2, 1028)])
+def test_merge_random_states(cpa, S, N, Hh, Dv):
+    rng = np.random.default_rng(S * 1000 + Dv)
+    o = rng.standard_normal((S, N, Hh, Dv)).astype(np.float32)
+    lse = (rng.standard_normal((S, N, Hh)) * 4).astype(np.float32)
+    if S > 1:
+        lse[0, 0, :] = -np.inf          # an empty shard carries no mass
+        lse[:, -1, -1] = -np.inf        # an all-empty row: O = 0, LSE = -inf
+        lse[1 % S, 1 % N, 0] = 80.0     # large LSE values must not overflow
+    ref_o, ref_l = att.merge_states(o.astype(np.float64), lse.astype(np.float64))
+    out, lo = cpa.attn_merge_states(H.f32_tensor(o), H.f32_tensor(lse))
+    _sync()
+    H.check_f32(H.host(out), H.host(lo), ref_o, ref_l, "merge f32")
+    import torch
+    outb, lob = cpa.attn_merge_states(H.f32_tensor(o), H.f32_tensor(lse), out_dtype=torch.bfloat16)
+    _sync()
+    H.check_lowp(H.host(outb), H.host(lob), ref_o, ref_l, "merge bf16 out")
+
+
+def _decode_case(cpa, B, Hq, Hkv, D, L, shards, qdt, kvdt, seed, ragged=False):
+    """GQA decode: every shard against the oracle, then the merge against
+    unsharded attention."""
+    import torch
+    rng = np.random.default_rng(seed)
+    scale = 1.0 / math.sqrt(D)
+    if qdt == "f32":
+        q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+        qd, qv = H.f32_tensor(q), q.astype(np.float64)
+    else:
+        qb = synth.f32_to_bf16_bits(rng.standard_normal((B, Hq, D)).astype(np.float32))
+        qd, qv = H.bf16_tensor(qb), formats.bf16_bits_to_f64(qb)
+    kx = rng.standard_normal((B, L, Hkv, D)).astype(np.float32)
+    vx = rng.standard_normal((B, L, Hkv, D)).astype(np.float32)
+    if kvdt == "f32":
+        kd, vd, kv64, vv64 = H.f32_tensor(kx), H.f32_tensor(vx), kx.astype(np.float64), vx.astype(np.float64)
+    else:
+        kb, vb = synth.f32_to_bf16_bits(kx), synth.f32_to_bf16_bits(vx)
+        kd, vd, kv64, vv64 = H.bf16_tensor(kb), H.bf16_tensor(vb), formats.bf16_bits_to_f64(kb), formats.bf16_bits_to_f64(vb)
+    parts_o, parts_l = [], []
+    for (s0, s1) in shards:
+        beg = np.full(B, s0, np.int32)
+        end = np.full(B, s1, np.int32)
+        if ragged:  # per-request ranges inside the shard, one empty
+            end = np.minimum(end, s0 + (np.arange(B) * 37) % max(1, s1 - s0 + 1)).astype(np.int32)
+        o, l = cpa.attn_decode_shard(qd, kd, vd, H.i32_tensor(beg), H.i32_tensor(end), s1 - s0, scale)
+        _sync()
+        ro, rl = att.decode_shard(qv, kv64, beg, end, scale, vcache=vv64)
+        chk = H.check_f32 if (qdt == "f32" and kvdt == "f32") else H.check_lowp
+        chk(H.host(o), H.host(l), ro, rl, f"shard {s0}:{s1}")
+        parts_o.append(o)
+        parts_l.append(l)
+    if not ragged:
+        mo, ml = cpa.attn_merge_states(torch.stack(parts_o), torch.stack(parts_l))
+        _sync()
+        fo, fl = att.decode_shard(qv, kv64, [0] * B, [L] * B, scale, vcache=vv64)
+        chk = H.check_f32 if (qdt == "f32" and kvdt == "f32") else H.check_lowp
+        chk(H.host(mo), H.host(ml), fo, fl, "merged vs unsharded")
+
+
+def test_decode_gqa_f32_workload(cpa):
+    """Split-KV decode + merge, fp32: batch 1, 8 query heads on 1 kv head,
+    head dim 128, 4096-token context cut into 4 contiguous 1024-token shards."""
+    c = synth.config(1)
+    B, Hq, Hkv, D, L = c["B"], c["Hq"], c["Hkv"], c["Dqk"], c["L"]
+    q = synth.f32_normal(1, 1, (B, Hq, D))
+    k = synth.f32_normal(1, 2, (B, L, Hkv, D), chunk=1)
+    v = synth.f32_normal(1, 3, (B, L, Hkv, D), chunk=1)
+    import torch
+    shards = plans.contiguous_shards(L, c["C"])
+    qd, kd, vd = H.f32_tensor(q), H.f32_tensor(k), H.f32_tensor(v)
+    po, pl = [], []
+    for (s0, s1) in shards:
+        o, l = cpa.attn_decode_shard(qd, kd, vd, H.i32_tensor([s0]), H.i32_tensor([s1]), s1 - s0, c["scale"])
+        po.append(o); pl.append(l)
+    mo, ml = cpa.attn_merge_states(torch.stack(po), torch.stack(pl))
+    _sync()
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    for i, (s0, s1) in enumerate(shards):
+        ro, rl = att.decode_shard(q64, k64, [s0], [s1], c["scale"], vcache=v64)
+        H.check_f32(H.host(po[i]), H.host(pl[i]), ro, rl, f"shard {i}")
+    fo, fl = att.decode_shard(q64, k64, [0], [L], c["scale"], vcache=v64)
+    H.check_f32(H.host(mo), H.host(ml), fo, fl, "merged")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,L,nsh", [(2, 8, 2, 64, 300, 3), (3, 32, 8, 128, 1000, 4), (1, 4, 4, 256, 77, 2)])
+def test_decode_gqa_f32_shapes(cpa, B, Hq, Hkv, D, L, nsh):
+    _decode_case(cpa, B, Hq, Hkv, D, L, plans.contiguous_shards(L, nsh), "f32", "f32", B * 7 + D)
+
+
+def test_decode_gqa_bf16_and_ragged(cpa):
+    _decode_case(cpa, 3, 16, 4, 128, 700, plans.contiguous_shards(700, 3), "bf16", "bf16", 17)
+    _decode_case(cpa, 5, 8, 1, 128, 500, [(100, 400)], "bf16", "bf16", 18, ragged=True)
+
+
+def _mla_inputs(B, L, fp8, seed, std=0.5):
+    rng = np.random.default_rng(seed)
+    qb = synth.f32_to_bf16_bits(rng.standard_normal((B, 64, 576)).astype(np.float32))
+    x = (rng.standard_normal((B, L, 1, 576)) * std).astype(np.float32)
+    if fp8:
+        codes, sc = synth.f32_to_e4m3(x)
+        return qb, codes, sc[..., 0]
+    return qb, synth.f32_to_bf16_bits(x), None
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("B,L,ranges", [
+    (2, 64, [(0, 64)]),                      # exactly two tiles
+    (3, 1000, [(0, 333), (333, 1000)]),      # ragged tails, several splits
+    (4, 130, [(5, 5), (0, 1), (7, 130)]),    # empty shard, single key
+])
+def test_decode_mla_small(cpa, fp8, B, L, ranges):
+    import torch
+    qb, cache, sc = _mla_inputs(B, L, fp8, B * 100 + L + fp8)
+    scale = 1.0 / math.sqrt(576)
+    qd = H.bf16_tensor(qb)
+    cd = H.u8_tensor(cache) if fp8 else H.bf16_tensor(cache)
+    sd = H.f32_tensor(sc) if fp8 else None
+    q64 = formats.bf16_bits_to_f64(qb)
+    dec = formats.e4m3_to_f64 if fp8 else formats.bf16_bits_to_f64
+    for (s0, s1) in ranges:
+        beg, end = np.full(B, s0, np.int32), np.full(B, s1, np.int32)
+        o, l = cpa.attn_decode_shard(qd, cd, None, H.i32_tensor(beg), H.i32_tensor(end), s1 - s0, scale,
+                                     kv_scale=sd)
+        _sync()
+        ro, rl = att.decode_shard(q64, cache, beg, end, scale, dv=512, decode=dec, kv_scale=sc)
+        H.check_lowp(H.host(o), H.host(l), ro, rl, f"mla fp8={fp8} [{s0},{s1})")
+        if s1 == s0:
+            assert np.all(H.host(o) == 0) and np.all(np.isneginf(H.host(l)))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_mla_spiky_scores(cpa, fp8):
+    """Planted keys with large logits exercise the running-max rescale."""
+    B, L = 2, 512
+    qb, cache, sc = _mla_inputs(B, L, fp8, 77 + fp8)
+    rng = np.random.default_rng(5)
+    q64 = formats.bf16_bits_to_f64(qb)
+    scale = 8.0 / math.sqrt(576)
+    if not fp8:
+        # copy a query row into a few late keys so their scores dominate
+        for t in (100, 301, 510):
+            cache[:, t, 0, :] = qb[:, 3, :]
+    qd = H.bf16_tensor(qb)
+    cd = H.u8_tensor(cache) if fp8 else H.bf16_tensor(cache)
+    sd = H.f32_tensor(sc) if fp8 else None
+    dec = formats.e4m3_to_f64 if fp8 else formats.bf16_bits_to_f64
+    beg, end = np.zeros(B, np.int32), np.full(B, L, np.int32)
+    o, l = cpa.attn_decode_shard(qd, cd, None, H.i32_tensor(beg), H.i32_tensor(end), L, scale, kv_scale=sd)
+    _sync()
+    ro, rl = att.decode_shard(q64, cache, beg, end, scale, dv=512, decode=dec, kv_scale=sc)
+    H.check_lowp(H.host(o), H.host(l), ro, rl, "mla spiky")

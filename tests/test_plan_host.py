@@ -1,0 +1,56 @@
+"""The library's host planners are bit-exact against the oracle's plans
+(CPU only: the planners are host code)."""
+
+import numpy as np
+import pytest
+
+import context_attention_long_amd as cpa
+from oracle import plans
+
+
+def _same(lib_plan, ref):
+    assert lib_plan.n_local == ref.n_local
+    assert np.array_equal(lib_plan.tok_index, ref.tok_index)
+    assert np.array_equal(lib_plan.pos_id, ref.pos_id)
+    assert np.array_equal(lib_plan.req_id, ref.req_id)
+    assert lib_plan.n_padded == ref.n_padded
+    got = [tuple(int(x) for x in (s["req"], s["q_row0"], s["q_len"], s["pos0"], s["pos_stride"], s["kv_row0"]))
+           for s in lib_plan.segments]
+    assert got == [tuple(int(x) for x in s) for s in ref.segments]
+    assert np.all(lib_plan.segments["reserved"] == 0)
+
+
+@pytest.mark.parametrize("strategy", ["zigzag", "interleave"])
+def test_planner_bit_exact_exhaustive_grid(strategy):
+    lib_fn = cpa.cp_plan_zigzag if strategy == "zigzag" else cpa.cp_plan_interleave
+    ref_fn = plans.plan_zigzag if strategy == "zigzag" else plans.plan_interleave
+    rng = np.random.default_rng(123)
+    batches = [[L] for L in range(0, 41)]
+    for _ in range(60):
+        n = int(rng.integers(1, 7))
+        batches.append([int(x) for x in rng.integers(0, 41, size=n)])
+    for new_len in batches:
+        for prefix in (None, [int(x) for x in rng.integers(0, 6, size=len(new_len))]):
+            for C in range(1, 17):
+                for r in range(C):
+                    _same(lib_fn(C, r, new_len, prefix), ref_fn(C, r, new_len, prefix))
+
+
+def test_planner_workloads_bit_exact():
+    from synth import agentic_lengths
+    cases = [("zigzag", 4, 1, [16384], None), ("zigzag", 8, 0, [131072], [32768]),
+             ("interleave", 4, 2, [int(x) for x in agentic_lengths(5)], None),
+             ("interleave", 8, 7, [128000], None)]
+    for strategy, C, r, L, P in cases:
+        lib_fn = cpa.cp_plan_zigzag if strategy == "zigzag" else cpa.cp_plan_interleave
+        ref_fn = plans.plan_zigzag if strategy == "zigzag" else plans.plan_interleave
+        _same(lib_fn(C, r, L, P), ref_fn(C, r, L, P))
+    p = cpa.cp_plan_interleave(4, 2, [int(x) for x in agentic_lengths(5)])
+    assert p.n_local == 182010 and p.n_seg == 16
+    assert int(np.sum(p.pos_id.astype(np.int64) + 1)) == 6654242875
+
+
+def test_decode_shards_bit_exact():
+    for L in (0, 1, 7, 4096, 131072, 1001):
+        for C in (1, 2, 3, 4, 8, 16):
+            assert cpa.cp_decode_shards(L, C) == plans.contiguous_shards(L, C)
