@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the context-parallel attention shard path on one MI355X.
+
+Headline (the JSON line's ``value``): the zigzag prefill shard -- causal GQA,
+32 query heads on 8 kv heads, head dim 128, bf16, a 16384-token prompt split
+for C=4 ranks, rank 1's share (blocks 1 and 6) -- in TFLOP/s of algorithmic
+work (unmasked causal pairs, diagonal included, 2 * (Dqk + Dv) flops per
+pair and head). A step is the rank's whole hot path for that batch: the
+zigzag plan (host planner) and the shard attention launch.
+
+Secondary (``decode`` object): split-KV MLA decode, batch 64, 64 heads,
+576/512 latent, 131072-token context cut into C=8 contiguous shards, run as 8
+partial launches on one device plus the exact merge; bf16 cache and FP8 E4M3
+cache with per-token scale, in GB/s of algorithmic bytes (cache bytes read
+once, plus queries, partial outputs/LSEs and the merge).
+
+Also reported: the dominant kernel's roofline (live HIP-event timing on the
+launch stream) and the float64 CPU oracle timed on a bounded sample of the
+same workload on this host. All inputs are seeded and synthetic.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "split-KV decode GB/s (% HBM peak); zigzag prefill TFLOP/s (% MFMA peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _events(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def bench_prefill(cpa, torch, synth, steps, warmup):
+    c = synth.config(2)
+    plan = cpa.cp_plan_zigzag(c["C"], c["rank"], c["new_len"], c["prefix_len"])
+    T = sum(c["new_len"])
+    dev = torch.device("cuda:0")
+    to_dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    q = to_dev(synth.bf16_normal(2, 1, (plan.n_local, c["Hq"], c["Dqk"])))
+    k = to_dev(synth.bf16_normal(2, 2, (T, c["Hkv"], c["Dqk"])))
+    v = to_dev(synth.bf16_normal(2, 3, (T, c["Hkv"], c["Dv"])))
+    out = torch.empty((plan.n_local, c["Hq"], c["Dv"]), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((plan.n_local, c["Hq"]), dtype=torch.float32, device=dev)
+    pairs = int(np.sum(plan.pos_id.astype(np.int64) + 1))
+    flops = pairs * c["Hq"] * 2 * (c["Dqk"] + c["Dv"])
+
+    def step(ev=None):
+        p = cpa.cp_plan_zigzag(c["C"], c["rank"], c["new_len"], c["prefix_len"])
+        if ev is not None:
+            ev[0].record()
+        cpa.attn_prefill_shard(q, k, v, p.segments, c["scale"], out=out, lse=lse)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = _events(torch, steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = [a.elapsed_time(b) for a, b in evs]
+    return dict(cfg=c, plan=plan, flops=flops, pairs=pairs, wall=wall, kernel_ms=kms,
+                inputs=(q, k, v))
+
+
+def bench_decode(cpa, torch, synth, steps, warmup):
+    c = synth.config(3)
+    B, L, C, H = c["B"], c["L"], c["C"], c["Hq"]
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    qb = synth.bf16_normal(3, 1, (B, H, c["Dqk"]))
+    bits, codes, scales = synth.latent_cache_both(3, 2, B, L, c["Dqk"], c["std"])
+    log(f"[bench] decode inputs generated in {time.perf_counter() - t0:.1f}s")
+    q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(dev)
+    cache_bf16 = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    del bits
+    cache_fp8 = torch.from_numpy(codes).to(dev)
+    sc = torch.from_numpy(scales).to(dev)
+    del codes
+    shards = cpa.cp_decode_shards(L, C)
+    begins = [torch.full((B,), s0, dtype=torch.int32, device=dev) for s0, _ in shards]
+    ends = [torch.full((B,), s1, dtype=torch.int32, device=dev) for _, s1 in shards]
+    max_len = max(s1 - s0 for s0, s1 in shards)
+    po = torch.empty((C, B, H, 512), dtype=torch.float32, device=dev)
+    pl = torch.empty((C, B, H), dtype=torch.float32, device=dev)
+    mo = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    ml = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, cpa.attn_decode_workspace_size(B, H, 512, max_len)), dtype=torch.uint8, device=dev)
+    res = {}
+    for name, cache, kvs, entry in (("bf16", cache_bf16, None, 576 * 2), ("fp8", cache_fp8, sc, 576 + 4)):
+        def step(ev=None):
+            for i in range(C):
+                if ev is not None:
+                    ev[i][0].record()
+                cpa.attn_decode_shard(q, cache, None, begins[i], ends[i], max_len, c["scale"], kv_scale=kvs,
+                                      o_part=po[i], lse_part=pl[i], workspace=ws)
+                if ev is not None:
+                    ev[i][1].record()
+            cpa.attn_merge_states(po, pl, out=mo, lse_out=ml)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [_events(torch, C) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        launch_ms = [a.elapsed_time(b) for ev in evs for a, b in ev]
+        kv_bytes = B * L * entry
+        q_bytes = C * B * H * 576 * 2
+        part_bytes = C * B * H * (512 + 1) * 4
+        step_bytes = kv_bytes + q_bytes + 2 * part_bytes + B * H * (512 + 1) * 4
+        launch_bytes = kv_bytes / C + B * H * 576 * 2 + B * H * (512 + 1) * 4
+        ms = wall / steps * 1e3
+        lm = float(np.mean(launch_ms))
+        res[name] = dict(ms_per_step=ms, gbs=step_bytes / (ms * 1e-3) / 1e9, algorithmic_bytes=step_bytes,
+                         launch_ms=lm, launch_gbs=launch_bytes / (lm * 1e-3) / 1e9,
+                         launch_bytes=launch_bytes)
+    return res
+
+
+def cpu_baseline(synth, prefill, seconds):
+    """The float64 oracle on rows of the same zigzag workload until ~`seconds`
+    of CPU work, as TFLOP/s of algorithmic work done."""
+    from oracle import attention as att
+    from oracle import formats, plans
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(cores)
+    except Exception:  # pragma: no cover
+        limiter = None
+    c = prefill["cfg"]
+    ref = plans.plan_zigzag(c["C"], c["rank"], c["new_len"], c["prefix_len"])
+    T = sum(c["new_len"])
+    qb = synth.bf16_normal(2, 1, (ref.n_local, c["Hq"], c["Dqk"]))
+    kb = synth.bf16_normal(2, 2, (T, c["Hkv"], c["Dqk"]))
+    vb = synth.bf16_normal(2, 3, (T, c["Hkv"], c["Dv"]))
+    # rows spread over both blocks, cheap and expensive alike, 16 at a time
+    order = synth.rng(2, 9).permutation(ref.n_local)
+    done_rows, flops = 0, 0
+    t0 = time.perf_counter()
+    while done_rows < ref.n_local and time.perf_counter() - t0 < seconds:
+        rows = sorted(int(r) for r in order[done_rows:done_rows + 16])
+        att.prefill_shard(qb, kb, ref.segments, c["scale"], v=vb, rows=rows, decode=formats.bf16_bits_to_f64)
+        flops += int(np.sum(ref.pos_id[rows].astype(np.int64) + 1)) * c["Hq"] * 2 * (c["Dqk"] + c["Dv"])
+        done_rows += len(rows)
+    dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done_rows} of {ref.n_local} local query rows (all 32 heads, random order) of the same "
+                      f"zigzag workload in {dt:.1f} s; float64 numpy; the full step would take "
+                      f"{prefill['flops'] / (flops / dt):.0f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true", help="skip the secondary MLA decode figures")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--decode-only", action="store_true", help="time only the MLA decode (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one 512 MiB device-to-device copy (reference for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(shards are evaluated as partial launches on one device). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import context_attention_long_amd as cpa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cpa.lib()
+
+    if args.copy_calibration:
+        # a plain copy of known size: 512 MiB read + 512 MiB written
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 536870912 bytes read, 536870912 written")
+        del src, dst
+        torch.cuda.empty_cache()
+
+    if args.decode_only:
+        dec = bench_decode(cpa, torch, synth, args.steps, args.warmup)
+        print(json.dumps({"decode": dec}), flush=True)
+        return
+
+    log("[bench] zigzag prefill shard ...")
+    pre = bench_prefill(cpa, torch, synth, args.steps, args.warmup)
+    ms = pre["wall"] / args.steps * 1e3
+    value = pre["flops"] / (ms * 1e-3) / 1e12
+    kms = float(np.mean(pre["kernel_ms"]))
+    achieved = pre["flops"] / (kms * 1e-3) / 1e12
+    log(f"[bench] prefill: {ms:.3f} ms/step, {value:.1f} TFLOP/s; kernel {kms:.3f} ms -> {achieved:.1f} TFLOP/s")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 queries/keys/values)",
+        "config": {
+            "workload": "zigzag prefill shard: causal GQA 32 q / 8 kv heads, d=128, bf16, 16384-token prompt, "
+                        "C=4, rank 1 (blocks 1 and 6), no cached prefix",
+            "seq_len": 16384, "cp_size": 4, "rank": 1, "local_rows": pre["plan"].n_local,
+            "causal_pairs_per_head": pre["pairs"], "algorithmic_gflop": round(pre["flops"] / 1e9, 3),
+        },
+        "roofline": {
+            "kernel": "prefill_gqa_kernel",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel_ms": round(kms, 4),
+        },
+    }
+    del pre["inputs"]
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        log("[bench] split-KV MLA decode (8 partial launches + merge) ...")
+        dec = bench_decode(cpa, torch, synth, max(3, args.steps // 2), args.warmup)
+        line["decode"] = {
+            "workload": "MLA split-KV decode: batch 64, 64 heads, 576/512 latent, 131072-token context, "
+                        "C=8 contiguous shards as 8 partial launches + merge",
+            "unit": "GB/s",
+            "bf16": {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["bf16"].items()},
+            "fp8": {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["fp8"].items()},
+            "roofline": {
+                "kernel": "decode_mla_kernel (bf16 cache)", "bound": "hbm",
+                "achieved": round(dec["bf16"]["launch_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dec["bf16"]["launch_gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+            },
+            "frac_of_hbm_peak_step": {k: round(dec[k]["gbs"] / PEAK_HBM_GBS, 4) for k in ("bf16", "fp8")},
+        }
+        log(f"[bench] decode bf16 {dec['bf16']['gbs']:.0f} GB/s/step, fp8 {dec['fp8']['gbs']:.0f} GB/s/step")
+
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        line["cpu_baseline"] = cpu_baseline(synth, pre, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

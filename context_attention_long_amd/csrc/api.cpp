@@ -233,7 +233,8 @@ extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* k
   if (Hkv < 1 || Hq % Hkv) return fail(CPA_E_INVAL, "decode: Hq = %lld not a multiple of Hkv = %lld", (long long)Hq, (long long)Hkv);
   if (Lmax > INT32_MAX || B > INT32_MAX) return fail(CPA_E_INVAL, "decode: sizes too large");
   if (max_shard_len < 0) return fail(CPA_E_INVAL, "decode: max_shard_len < 0");
-  if (!std::isfinite(softmax_scale)) return fail(CPA_E_INVAL, "decode: softmax_scale is not finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(CPA_E_INVAL, "decode: softmax_scale must be finite and > 0");
   if (B > 0 && (kv_begin == nullptr || kv_end == nullptr)) return fail(CPA_E_INVAL, "decode: kv_begin/kv_end NULL");
   const bool fp8 = kcache->dtype == CPA_FP8_E4M3;
   int64_t Dv;
@@ -413,7 +414,8 @@ extern "C" cpa_status attn_prefill_shard(const cpa_tensor* q, const cpa_tensor* 
   const int64_t T_kv = k->shape[0], Hkv = k->shape[1];
   if (k->shape[2] != Dqk) return fail(CPA_E_INVAL, "prefill: k head dim differs from q");
   if (Hkv < 1 || Hq % Hkv) return fail(CPA_E_INVAL, "prefill: Hq = %lld not a multiple of Hkv = %lld", (long long)Hq, (long long)Hkv);
-  if (!std::isfinite(softmax_scale)) return fail(CPA_E_INVAL, "prefill: softmax_scale is not finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(CPA_E_INVAL, "prefill: softmax_scale must be finite and > 0");
   if (n_local > INT32_MAX || T_kv > ((int64_t)1 << 40)) return fail(CPA_E_INVAL, "prefill: sizes too large");
   int64_t Dv;
   if (v == nullptr) {
@@ -433,6 +435,9 @@ extern "C" cpa_status attn_prefill_shard(const cpa_tensor* q, const cpa_tensor* 
     if (Dqk != 128 || Dv != 128) return fail(CPA_E_UNSUPPORTED, "prefill: GQA kernel is built for head dim 128");
     const int64_t G = Hq / Hkv;
     if (G > 128 || (128 % G) != 0) return fail(CPA_E_UNSUPPORTED, "prefill: Hq / Hkv = %lld must divide 128", (long long)G);
+    // the kernel addresses a 64-key tile with 32-bit per-lane byte offsets
+    if (k->stride[0] >= ((int64_t)1 << 24) || v->stride[0] >= ((int64_t)1 << 24))
+      return fail(CPA_E_INVAL, "prefill: k / v token stride too large");
     cpa::PrefillGqaArgs a{};
     a.q = static_cast<const uint16_t*>(q->data);
     a.k = static_cast<const uint16_t*>(k->data);

@@ -23,15 +23,19 @@
 //    (transposing 16-bit reads), so one LDS copy feeds both products;
 //  * the output accumulator O^T [512 x 16 heads] stays in registers; each
 //    lane's column is one head, so the softmax rescale is lane-local;
-//  * FP8: the tile is converted e4m3 -> bf16 exactly while it is written to
-//    LDS; the per-token scale is folded into the score (s = scale_t q.e_t)
-//    and into P (p_t * scale_t multiplies e_t in PV), never into K itself;
+//  * the cache streams from HBM by direct global -> LDS loads: bf16 keeps 4
+//    tile stages (3 tiles in flight per CU while one is consumed); FP8 keeps
+//    3 stages of 64 raw tokens plus one bf16 tile, converted e4m3 -> bf16
+//    exactly once per CU; the per-token scale is folded into the score
+//    (s = scale_t q.e_t) and into P (p_t * scale_t multiplies e_t in PV),
+//    never into K itself;
 //  * LDS rows are 72 chunks of 16 bytes, XOR-swizzled inside aligned groups
 //    of 8 chunks so that the 16 rows one MFMA operand read touches fall in
 //    distinct banks.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace {
 
@@ -86,91 +90,6 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
                                                  pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])));
 }
 
-template <bool kFp8>
-struct TileLoader {
-  // registers holding the next tile while the current one is consumed
-  uint4 r[kFp8 ? kFp8LdChunks : kLdChunks];
-  float sc;
-  // per-thread element offsets of its chunks inside a tile (loop invariant)
-  uint32_t goff[kFp8 ? kFp8LdChunks : kLdChunks];
-
-  __device__ __forceinline__ void init(const cpa::DecodeMlaArgs& a) {
-    const int tid = threadIdx.x;
-    if constexpr (!kFp8) {
-#pragma unroll
-      for (int k = 0; k < kLdChunks; ++k) {
-        const int P = tid + kThreads * k;
-        const int row = P / kRowChunks, pc = P % kRowChunks;
-        goff[k] = (uint32_t)(row * a.c_t + swz(row, pc) * 8);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kFp8LdChunks; ++k) {
-        const int S = tid + kThreads * k;
-        const int row = S / kFp8RowChunks, sc16 = S % kFp8RowChunks;
-        goff[k] = (uint32_t)(row * a.c_t + sc16 * 16);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void load(const cpa::DecodeMlaArgs& a, int b, int64_t tok0, int nvalid) {
-    const int tid = threadIdx.x;
-    if constexpr (!kFp8) {
-      const uint16_t* base = reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b + tok0 * a.c_t;
-#pragma unroll
-      for (int k = 0; k < kLdChunks; ++k) {
-        const int row = (tid + kThreads * k) / kRowChunks;
-        if (nvalid == kBN || row < nvalid)
-          r[k] = *reinterpret_cast<const uint4*>(base + goff[k]);
-        else
-          r[k] = make_uint4(0, 0, 0, 0);
-      }
-    } else {
-      const uint8_t* base = reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b + tok0 * a.c_t;
-#pragma unroll
-      for (int k = 0; k < kFp8LdChunks; ++k) {
-        const int S = tid + kThreads * k;
-        const int row = S / kFp8RowChunks;
-        if (S < kFp8TileChunks && (nvalid == kBN || row < nvalid))
-          r[k] = *reinterpret_cast<const uint4*>(base + goff[k]);
-        else
-          r[k] = make_uint4(0, 0, 0, 0);
-      }
-      sc = (tid < nvalid) ? a.kv_scale[(int64_t)b * a.s_b + (tok0 + tid) * a.s_t] : 0.f;
-    }
-  }
-
-  __device__ __forceinline__ void store(char* tile, float* scales) {
-    const int tid = threadIdx.x;
-    if constexpr (!kFp8) {
-#pragma unroll
-      for (int k = 0; k < kLdChunks; ++k)
-        *reinterpret_cast<uint4*>(tile + (tid + kThreads * k) * 16) = r[k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < kFp8LdChunks; ++k) {
-        const int S = tid + kThreads * k;
-        if (S < kFp8TileChunks) {
-          const int row = S / kFp8RowChunks, sc16 = S % kFp8RowChunks;
-          const uint32_t w[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
-          uint32_t o[8];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[q], 1.0f, false);
-            bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[q], 1.0f, true);
-            o[2 * q] = __builtin_bit_cast(uint32_t, lo);
-            o[2 * q + 1] = __builtin_bit_cast(uint32_t, hi);
-          }
-          char* rowp = tile + row * (kRowChunks * 16);
-          *reinterpret_cast<uint4*>(rowp + swz(row, 2 * sc16) * 16) = make_uint4(o[0], o[1], o[2], o[3]);
-          *reinterpret_cast<uint4*>(rowp + swz(row, 2 * sc16 + 1) * 16) = make_uint4(o[4], o[5], o[6], o[7]);
-        }
-      }
-      if (tid < kBN) scales[tid] = sc;
-    }
-  }
-};
-
 // Per-lane LDS byte offsets inside a tile. Every operand read of a tile is
 // one of these bases plus a compile-time constant, so the reads use the LDS
 // instruction's immediate offset instead of one address register each.
@@ -209,16 +128,30 @@ template <bool kFp8>
 __device__ __forceinline__ void consume_tile(const char* tile, const float* scales, int nvalid, int g,
                                              const LdsBases& L, const bf16x8 (&qreg)[kDk / 32],
                                              float scale_log2, State& st) {
-  // ---- S^T = K Q^T: two 16-token blocks ----
-  f32x4 sacc[2];
+  // ---- S^T = K Q^T: two 16-token blocks, chains interleaved ----
+  // K operands are read kAhead k-steps ahead of their MFMAs; a scheduling
+  // barrier closes every step so the reads cannot sink next to their use and
+  // LDS latency overlaps MFMA work.
+  constexpr int kSteps = kDk / 32;  // 18
+  constexpr int kAhead = 4;
+  f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  bf16x8 ka[kSteps][2];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < kAhead; ++s)
 #pragma unroll
-    for (int s = 0; s < kDk / 32; ++s) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(tile + L.qk[mt][s & 1] + 128 * (s >> 1));
-      sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[s], sacc[mt], 0, 0, 0);
+    for (int mt = 0; mt < 2; ++mt)
+      ka[s][mt] = *reinterpret_cast<const bf16x8*>(tile + L.qk[mt][s & 1] + 128 * (s >> 1));
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    if (s + kAhead < kSteps) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        ka[s + kAhead][mt] =
+            *reinterpret_cast<const bf16x8*>(tile + L.qk[mt][(s + kAhead) & 1] + 128 * ((s + kAhead) >> 1));
     }
+    sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s][0], qreg[s], sacc[0], 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s][1], qreg[s], sacc[1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // ---- online softmax (log2 domain) ----
   float x[8];
@@ -236,39 +169,92 @@ __device__ __forceinline__ void consume_tile(const char* tile, const float* scal
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m_run, mx);
-  const float alpha = exp2f(st.m_run - m_new);  // 0 on the first tile
-  st.m_run = m_new;
+  // Lazy rescale: the reference max m_run only moves when a score exceeds it
+  // by more than 2^8; until then p = 2^(s - m_run) <= 256, and O and l share
+  // the same reference, so the result is unchanged. The first tile always
+  // sets it (m_run = -inf).
+  if (__any(mx > st.m_run + 8.f)) {
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);  // 0 on the first tile
+    st.m_run = m_new;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int m = 0; m < kDv / 16; ++m) st.oacc[m] *= alpha;
+  }
+  const float m_new = st.m_run;
   float psum = 0.f;
   float pf[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float p = exp2f(x[j] - m_new);
+    const float p = __builtin_amdgcn_exp2f(x[j] - m_new);
     psum += p;
     float pv = p;
     if constexpr (kFp8) pv *= scales[16 * (j >> 2) + 4 * g + (j & 3)];
     pf[j] = pv;
   }
   const bf16x8 pb = pack8(pf);
-  st.l_run = st.l_run * alpha + psum;
-  if (__any(alpha != 1.f)) {
+  st.l_run += psum;
+  // ---- O^T += V^T P^T: V^T operands read kAheadV m-tiles ahead (same scheme) ----
+  constexpr int kMt = kDv / 16;  // 32
+  constexpr int kAheadV = 4;
+  bf16x8 va[kMt];
 #pragma unroll
-    for (int m = 0; m < kDv / 16; ++m) st.oacc[m] *= alpha;
-  }
-  // ---- O^T += V^T P^T ----
+  for (int m = 0; m < kAheadV; ++m)
+    va[m] = join_tr(lds_read_tr(tile + L.pv[0][m & 3] + 128 * (m >> 2)),
+                    lds_read_tr(tile + L.pv[1][m & 3] + 128 * (m >> 2)));
 #pragma unroll
-  for (int m = 0; m < kDv / 16; ++m) {
-    const i16x4 v0 = lds_read_tr(tile + L.pv[0][m & 3] + 128 * (m >> 2));
-    const i16x4 v1 = lds_read_tr(tile + L.pv[1][m & 3] + 128 * (m >> 2));
-    const bf16x8 va = join_tr(v0, v1);
-    st.oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.oacc[m], 0, 0, 0);
+  for (int m = 0; m < kMt; ++m) {
+    if (m + kAheadV < kMt) {
+      const int mm = m + kAheadV;
+      va[mm] = join_tr(lds_read_tr(tile + L.pv[0][mm & 3] + 128 * (mm >> 2)),
+                       lds_read_tr(tile + L.pv[1][mm & 3] + 128 * (mm >> 2)));
+    }
+    st.oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb, st.oacc[m], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+constexpr int kStageBytes = kTileBytes;               // 36 KB: one 32-token bf16 tile
+constexpr int kRawBytes = kBN * kDk;                   // 18 KB: one 32-token FP8 tile
+constexpr int kRawWaveLoads = kRawBytes / 1024;        // 18 wave-wide 16-byte loads per tile
+static_assert(kRawWaveLoads * 1024 == kRawBytes && kDk % 16 == 0, "raw FP8 tile layout");
+
+// FP8 -> bf16 of one raw 32-token tile into a bf16 tile (swizzled layout),
+// each byte converted once per workgroup; the tile's scales travel with it.
+__device__ __forceinline__ void convert_tile(const char* raw, const float* sc_in, char* tile, float* sc_out) {
+  const int tid = threadIdx.x;
+  for (int S = tid; S < kBN * kFp8RowChunks; S += kThreads) {
+    const int row = S / kFp8RowChunks, sc16 = S % kFp8RowChunks;
+    const uint4 r = *reinterpret_cast<const uint4*>(raw + row * kDk + sc16 * 16);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[q], 1.0f, false));
+      o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[q], 1.0f, true));
+    }
+    char* rowp = tile + row * (kRowChunks * 16);
+    *reinterpret_cast<uint4*>(rowp + swz(row, 2 * sc16) * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(rowp + swz(row, 2 * sc16 + 1) * 16) = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+  if (tid < kBN) sc_out[tid] = sc_in[tid];
+}
+
+template <int N>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  // at most `ahead` further tiles of N loads each may still be in flight
+  if (ahead >= 3) cpa::wait_vmcnt<3 * N>();
+  else if (ahead == 2) cpa::wait_vmcnt<2 * N>();
+  else if (ahead == 1) cpa::wait_vmcnt<N>();
+  else cpa::wait_vmcnt<0>();
 }
 
 template <bool kFp8>
 __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaArgs a) {
-  __shared__ __attribute__((aligned(16))) char tiles[2][kTileBytes];
-  __shared__ float scales[2][kBN];
+  // bf16: 4 tile stages. FP8: 4 raw stages (18 KB) + 2 bf16 tiles, in the same bytes.
+  __shared__ __attribute__((aligned(16))) char smem[4 * kStageBytes];
+  __shared__ float rscale[4][4][64];  // FP8: [raw stage][wave copy][token]
+  __shared__ float bscale[2][kBN];    // FP8: scales of the two bf16 tiles
 
   const int split = blockIdx.x % a.nsplit;
   const int b = blockIdx.x / a.nsplit;
@@ -282,14 +268,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
   const int64_t len = end - beg;
   const int64_t t0 = beg + len * split / a.nsplit;
   const int64_t t1 = beg + len * (split + 1) / a.nsplit;
-  const int ntiles = (int)((t1 - t0 + kBN - 1) / kBN);
+  const int ntok = (int)(t1 - t0);
+  const int ntiles = (ntok + kBN - 1) / kBN;
 
   // Q^T operand: lane holds q[h][32s + 8g .. +8] for k-step s
+  // (opaque after loading: otherwise the compiler re-loads these read-only
+  // values from memory inside the tile loop instead of keeping them)
   bf16x8 qreg[kDk / 32];
   {
     const uint16_t* qp = a.q + (int64_t)b * a.q_b + (int64_t)h * a.q_h + 8 * g;
 #pragma unroll
-    for (int s = 0; s < kDk / 32; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+    for (int s = 0; s < kDk / 32; ++s) {
+      qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+      asm volatile("" : "+v"(qreg[s]));
+    }
   }
 
   State st;
@@ -299,33 +291,97 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
   st.l_run = 0.f;
   const LdsBases L = lds_bases(g, c);
 
-  auto tile_valid = [&](int it) {
-    const int64_t tk = t0 + (int64_t)it * kBN;
-    return (int)(t1 - tk < kBN ? t1 - tk : kBN);
-  };
-
-  TileLoader<kFp8> ld;
-  ld.init(a);
-  if (ntiles > 0) {
-    ld.load(a, b, t0, tile_valid(0));
-    ld.store(tiles[0], scales[0]);
-    if (ntiles > 1) ld.load(a, b, t0 + kBN, tile_valid(1));
-  }
-  // Two tiles per trip so each stage's LDS base is a compile-time constant.
-  for (int it = 0; it < ntiles; it += 2) {
-    __syncthreads();  // tile `it` (stage 0) visible; stage 1 free
-    if (it + 1 < ntiles) {
-      ld.store(tiles[1], scales[1]);
-      if (it + 2 < ntiles) ld.load(a, b, t0 + (int64_t)(it + 2) * kBN, tile_valid(it + 2));
+  if constexpr (!kFp8) {
+    // ---- bf16: stage i % 4 holds tile i ----
+    const uint16_t* base = reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b;
+    uint32_t toff[kLdChunks];  // byte offset of this thread's chunks inside a full tile
+#pragma unroll
+    for (int k = 0; k < kLdChunks; ++k) {
+      const int P = tid + kThreads * k;
+      const int row = P / kRowChunks, pc = P % kRowChunks;
+      toff[k] = (uint32_t)((row * a.c_t + swz(row, pc) * 8) * 2);
     }
-    consume_tile<kFp8>(tiles[0], scales[0], tile_valid(it), g, L, qreg, a.scale_log2, st);
-    if (it + 1 >= ntiles) break;
-    __syncthreads();  // tile `it + 1` (stage 1) visible; stage 0 free
-    if (it + 2 < ntiles) {
-      ld.store(tiles[0], scales[0]);
-      if (it + 3 < ntiles) ld.load(a, b, t0 + (int64_t)(it + 3) * kBN, tile_valid(it + 3));
+    auto issue = [&](int i) {
+      const int64_t tok0 = t0 + (int64_t)i * kBN;
+      char* dst0 = smem + (i & 3) * kStageBytes + 64 * w * 16;
+      if (tok0 + kBN <= t1) {
+        const uint16_t* tb = base + tok0 * a.c_t;
+#pragma unroll
+        for (int k = 0; k < kLdChunks; ++k) cpa::lds_dma16_sbase(tb, toff[k], cpa::lds_addr(dst0 + kThreads * k * 16));
+      } else {  // last tile: tokens past the split re-read its last token (masked)
+#pragma unroll
+        for (int k = 0; k < kLdChunks; ++k) {
+          const int P = tid + kThreads * k;
+          const int row = P / kRowChunks, pc = P % kRowChunks;
+          const int64_t tok = min(tok0 + row, t1 - 1);
+          cpa::lds_dma16(base + tok * a.c_t + swz(row, pc) * 8, cpa::lds_addr(dst0 + kThreads * k * 16));
+        }
+      }
+    };
+    for (int i = 0; i < 3 && i < ntiles; ++i) issue(i);
+    for (int i = 0; i < ntiles; ++i) {
+      wait_ahead<kLdChunks>(min(2, ntiles - 1 - i));  // tile i landed
+      __syncthreads();  // tile i visible to all; every wave is done with tile i-1
+      if (i + 3 < ntiles) issue(i + 3);  // into the stage tile i-1 used
+      consume_tile<false>(smem + (i & 3) * kStageBytes, nullptr, min(kBN, ntok - kBN * i), g, L, qreg,
+                          a.scale_log2, st);
     }
-    consume_tile<kFp8>(tiles[1], scales[1], tile_valid(it + 1), g, L, qreg, a.scale_log2, st);
+  } else {
+    // ---- FP8: raw stage u % 4 holds the e4m3 bytes of tile u; bf16 tile u % 2 ----
+    char* raw = smem;                       // 4 x 18 KB
+    char* btile = smem + 4 * kRawBytes;     // 2 x 36 KB
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b;
+    const float* sbase = a.kv_scale + (int64_t)b * a.s_b;
+    // wave w issues the tile's wave-loads w, w+4, ... (5 for waves 0-1, 4 for 2-3)
+    // plus one load of the tile's scales: per-wave counts for the waits
+    const int n_mine = (kRawWaveLoads - w + 3) / 4;
+    uint32_t roff[5];  // byte offset of this lane's 16-byte pieces inside a full raw tile
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const int B = (w + 4 * k) * 1024 + 16 * lane;  // LDS byte of the piece, row-major [32][576]
+      roff[k] = (uint32_t)((B / kDk) * a.c_t + (B % kDk));
+    }
+    auto issue = [&](int u) {
+      const int64_t tok0 = t0 + (int64_t)u * kBN;
+      char* dst = raw + (u & 3) * kRawBytes;
+      if (tok0 + kBN <= t1) {
+        const uint8_t* tb = base + tok0 * a.c_t;
+#pragma unroll
+        for (int k = 0; k < 5; ++k)
+          if (k < n_mine) cpa::lds_dma16_sbase(tb, roff[k], cpa::lds_addr(dst + (w + 4 * k) * 1024));
+      } else {  // last tile: past the split, re-read its last token (masked)
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+          if (k < n_mine) {
+            const int B = (w + 4 * k) * 1024 + 16 * lane;
+            const int64_t tok = min(tok0 + B / kDk, t1 - 1);
+            cpa::lds_dma16(base + tok * a.c_t + (B % kDk), cpa::lds_addr(dst + (w + 4 * k) * 1024));
+          }
+        }
+      }
+      const int64_t tok = min(tok0 + lane, t1 - 1);
+      cpa::lds_dma4(sbase + tok * a.s_t, cpa::lds_addr(&rscale[u & 3][w][0]));
+    };
+    auto wait_raw = [&](int ahead) {
+      if (w < 2) wait_ahead<6>(ahead);  // 5 cache loads + 1 scale load per tile
+      else wait_ahead<5>(ahead);
+    };
+    for (int u = 0; u < 4 && u < ntiles; ++u) issue(u);
+    if (ntiles > 0) {
+      wait_raw(min(3, ntiles - 1));  // raw 0 landed
+      __syncthreads();
+      convert_tile(raw, &rscale[0][0][0], btile, bscale[0]);
+    }
+    for (int u = 0; u < ntiles; ++u) {
+      if (u + 1 < ntiles) wait_raw(min(u + 3, ntiles - 1) - (u + 1));  // raw u+1 landed
+      __syncthreads();  // bf16 tile u complete; raw u+1 visible; tile u-1 and raw u fully consumed
+      if (u + 4 < ntiles) issue(u + 4);  // into the raw stage of tile u
+      if (u + 1 < ntiles)
+        convert_tile(raw + ((u + 1) & 3) * kRawBytes, &rscale[(u + 1) & 3][0][0], btile + ((u + 1) & 1) * kStageBytes,
+                     bscale[(u + 1) & 1]);
+      consume_tile<true>(btile + (u & 1) * kStageBytes, bscale[u & 1], min(kBN, ntok - kBN * u), g, L, qreg,
+                         a.scale_log2, st);
+    }
   }
 
   // ---- finish: combine the four lanes of each head, normalise, store ----

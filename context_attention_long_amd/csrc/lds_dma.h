@@ -1,0 +1,62 @@
+// Direct global -> LDS loads for the gfx950 kernels.
+//
+// global_load_lds_dwordx4 writes each lane's 16 bytes to LDS at
+// M0 + 16 * lane (layout verified on the hardware). It is issued from inline
+// assembly on purpose: the compiler tracks its own LDS-DMA builtin as a
+// write to all of LDS and then waits for every outstanding load (vmcnt(0))
+// before any later LDS read, which serialises the prefetch of tile i+1 with
+// the compute on tile i. Here the kernels wait themselves, with an explicit
+// vmcnt count, before the barrier that publishes a tile.
+//
+// Mixing these loads with compiler-issued vector loads is safe: vector-memory
+// loads complete in issue order, so loads added behind a compiler load can
+// only make the compiler's own vmcnt waits stricter.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace cpa {
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// One 16-byte load per lane into LDS at lds_base + 16 * lane. `lds_base` must
+// be the same for the whole wavefront.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// Same, addressed as a wavefront-uniform 64-bit base plus a per-lane 32-bit
+// byte offset (the base goes to SGPRs, so stepping it costs no VALU work).
+__device__ __forceinline__ void lds_dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// One 4-byte load per lane into LDS at lds_base + 4 * lane.
+__device__ __forceinline__ void lds_dma4(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wavefront are
+// outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+}  // namespace cpa

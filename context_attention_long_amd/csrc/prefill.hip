@@ -32,9 +32,11 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 #include <vector>
 
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace {
 
@@ -172,18 +174,36 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_gqa_kernel(Args a) {
   // re-read that last row (finite data; their scores are masked).
   const uint16_t* kbase = a.k + S.kv_row0 * a.k_t + (int64_t)kvh * a.k_h;
   const uint16_t* vbase = a.v + S.kv_row0 * a.v_t + (int64_t)kvh * a.v_h;
+  const int64_t k_t = a.k_t, v_t = a.v_t;
+  // loop-invariant byte offsets of this thread's 8 chunks inside a tile
+  uint32_t toff[kLdPerThread];
+#pragma unroll
+  for (int k = 0; k < kLdPerThread; ++k) {
+    const int P = tid + kThreads * k;  // chunk P of [K 1024 | V 1024]: K for k < 4
+    const int rr = (P >> 4) & (kBN - 1);
+    toff[k] = (uint32_t)((rr * (k < kLdPerThread / 2 ? k_t : v_t) + swz(rr, P & 15) * 8) * 2);
+  }
   auto load = [&](int kt, int st) {
     const int kb = kt * kBN;
+    char* dst0 = &lds[st][0][0] + 64 * wave * 16;
+    if (kb + kBN - 1 <= wg_last_pos) {
+      // full tile: uniform bases, per-lane offsets fixed
+      const uint16_t* kt_base = kbase + (int64_t)kb * k_t;
+      const uint16_t* vt_base = vbase + (int64_t)kb * v_t;
 #pragma unroll
-    for (int k = 0; k < kLdPerThread; ++k) {
-      const int P = tid + kThreads * k;     // 0..2047: [K 1024 | V 1024]
-      const int isv = P >> 10;
-      const int rr = (P >> 4) & (kBN - 1);  // tile row (key)
-      const int lc = swz(rr, P & 15);       // logical chunk held at this position
-      const int kp = min(kb + rr, wg_last_pos);
-      const uint16_t* src = (isv ? vbase + (int64_t)kp * a.v_t : kbase + (int64_t)kp * a.k_t) + lc * 8;
-      char* dst = &lds[st][0][0] + (64 * wave + kThreads * k) * 16;  // wave-uniform
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      for (int k = 0; k < kLdPerThread; ++k)
+        cpa::lds_dma16_sbase(k < kLdPerThread / 2 ? kt_base : vt_base, toff[k],
+                             cpa::lds_addr(dst0 + kThreads * k * 16));
+    } else {
+      // last tile: keys past the workgroup's last position re-read that row
+#pragma unroll
+      for (int k = 0; k < kLdPerThread; ++k) {
+        const int P = tid + kThreads * k;
+        const int rr = (P >> 4) & (kBN - 1);
+        const int64_t kp = min(kb + rr, wg_last_pos);
+        const uint16_t* src = (k < kLdPerThread / 2 ? kbase + kp * k_t : vbase + kp * v_t) + swz(rr, P & 15) * 8;
+        cpa::lds_dma16(src, cpa::lds_addr(dst0 + kThreads * k * 16));
+      }
     }
   };
 
@@ -214,17 +234,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_gqa_kernel(Args a) {
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  load(0, 0);
-
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's part of tile kt landed
-    __syncthreads();  // tile kt complete in LDS; every wave is done with the other stage
-    const int st = kt & 1;
-    if (kt + 1 < n_tiles) load(kt + 1, st ^ 1);
+  // one tile; ST (the LDS stage) is a compile-time constant so every operand
+  // read is a per-lane base plus an immediate offset
+  auto compute = [&](int kt, auto stage) {
+    constexpr int ST = decltype(stage)::value;
     const int kb = kt * kBN;
-    if (kb > w_last) continue;  // every row of this wave is past: skip (wave-uniform)
-    const char* Kt = &lds[st][0][0];
-    const char* Vt = &lds[st][1][0];
+    if (kb > w_last) return;  // every row of this wave is past: skip (wave-uniform)
+    const char* Kt = &lds[ST][0][0];
+    const char* Vt = &lds[ST][1][0];
 
     // ---- S^T = K Q^T ----
     f32x16 sacc[2];
@@ -238,24 +255,39 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_gqa_kernel(Args a) {
       }
     }
     // ---- mask (only tiles that reach past the wave's first row), max ----
-    const bool diag = kb + kBN - 1 > w_first;
+    // The running max is kept in the scaled log2 domain; the max is taken over
+    // raw scores (the scale is positive) and p = 2^(s * c - m) is one FMA and
+    // one v_exp_f32 (results below 2^-126 flush to 0, which only drops terms
+    // smaller than the fp32 sum can hold).
+    if (kb + kBN - 1 > w_first) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb + 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
+          sacc[mt][i] = key <= pos ? sacc[mt][i] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = sacc[mt][i] * a.scale_log2;
-        if (diag) {
-          const int key = kb + 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
-          x = key <= pos ? x : -INFINITY;
-        }
-        sacc[mt][i] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);  // m_new is finite: key 0 <= pos for every row
-    m_run = m_new;
+    // Lazy rescale: the reference max m_run moves only when the tile's max
+    // exceeds it by more than 2^8 (then p <= 256 until the next move; O and l
+    // share the reference, so the result is unchanged). Key 0 is in the first
+    // tile of every row, so m_run is finite from then on.
+    const float mt = mx * a.scale_log2;
+    if (__any(mt > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
+    }
+    const float m_new = m_run;
     float psum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
@@ -263,17 +295,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_gqa_kernel(Args a) {
       float pf[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float p = exp2f(sacc[ks >> 1][8 * (ks & 1) + j] - m_new);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[ks >> 1][8 * (ks & 1) + j], a.scale_log2, -m_new));
         psum += p;
         pf[j] = p;
       }
       pb[ks] = pack8(pf);
     }
-    l_run = l_run * alpha + psum;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
-    }
+    l_run += psum;
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -285,6 +313,19 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_gqa_kernel(Args a) {
         oacc[mtv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], oacc[mtv], 0, 0, 0);
       }
     }
+  };
+
+  load(0, 0);
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    cpa::wait_vmcnt<0>();  // this thread's part of tile kt landed
+    __syncthreads();       // tile kt complete in LDS; every wave is done with stage 1
+    if (kt + 1 < n_tiles) load(kt + 1, 1);
+    compute(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 >= n_tiles) break;
+    cpa::wait_vmcnt<0>();
+    __syncthreads();       // tile kt + 1 complete; every wave is done with stage 0
+    if (kt + 2 < n_tiles) load(kt + 2, 0);
+    compute(kt + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- finish ----

@@ -23,6 +23,7 @@
 #include <vector>
 
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace {
 
@@ -63,7 +64,11 @@ struct Args {
   Seg seg[kMaxSeg];
 };
 
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+// Physical 16-byte chunk of logical chunk c in latent row r: XOR of the low
+// 3 chunk bits with a permutation of r mod 16, so that the 16 rows of one QK
+// operand read and the 4 rows x 2 chunks of one transposing read fall in
+// distinct banks, and rows 16 apart share offsets (immediate addressing).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ ((r >> 3) & 1)) & 7); }
 
 __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mla_kernel(Args a) {
       const int kp = min(kb + rr, pos);  // past the query: re-read its own row (masked)
       const uint16_t* src = lbase + (int64_t)kp * a.k_t + swz(rr, pc) * 8;
       char* dst = tiles[st] + (64 * wave + kThreads * k) * 16;
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      cpa::lds_dma16(src, cpa::lds_addr(dst));
     }
   };
 
@@ -138,17 +143,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mla_kernel(Args a) {
   // PV A operand (transposing read): 16-lane group lq, lane ls: key row
   // 16 ks + 4 (lq >> 1) + (ls >> 2) (+ 8), dims 128 dq + 32 mtv + 16 (lq & 1) + 4 (ls & 3)
   const int lq = lane >> 4, ls = lane & 15;
-  int pv_off[4][2][2];  // [ks][run][mtv & 1]; (mtv >> 1) adds 64 dims = 8 chunks = 128 B
+  int pv_off[2][2];  // [run][mtv & 1]; k-step ks adds 16 rows, (mtv >> 1) adds 64 dims = 128 B
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int run = 0; run < 2; ++run)
 #pragma unroll
-    for (int run = 0; run < 2; ++run)
-#pragma unroll
-      for (int m1 = 0; m1 < 2; ++m1) {
-        const int rr = 16 * ks + 4 * (lq >> 1) + (ls >> 2) + 8 * run;
-        const int cidx = 128 * dq + 32 * m1 + 16 * (lq & 1) + 4 * (ls & 3);
-        pv_off[ks][run][m1] = rr * kRowBytes + swz(rr, cidx >> 3) * 16 + (cidx & 7) * 2;
-      }
+    for (int m1 = 0; m1 < 2; ++m1) {
+      const int rr = 4 * (lq >> 1) + (ls >> 2) + 8 * run;
+      const int cidx = 128 * dq + 32 * m1 + 16 * (lq & 1) + 4 * (ls & 3);
+      pv_off[run][m1] = rr * kRowBytes + swz(rr, cidx >> 3) * 16 + (cidx & 7) * 2;
+    }
 
   f32x16 oacc[4][2];  // [mtv][head block nt]
 #pragma unroll
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mla_kernel(Args a) {
 
   load(0, 0);
   for (int kt = 0; kt < n_tiles; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    cpa::wait_vmcnt<0>();  // this thread's part of tile kt landed
     __syncthreads();  // tile kt in LDS; PV of tile kt-1 finished everywhere
     const int st = kt & 1;
     if (kt + 1 < n_tiles) load(kt + 1, st ^ 1);
@@ -175,29 +178,36 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mla_kernel(Args a) {
       const bf16x8 ka = *reinterpret_cast<const bf16x8*>(T + qk_off[s & 3] + 128 * (s >> 2));
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc, 0, 0, 0);
     }
-    const bool diag = kb + kBN - 1 > pos;
+    if (kb + kBN - 1 > pos) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb + 32 * kh + 8 * (i >> 2) + 4 * g + (i & 3);
+        sacc[i] = key <= pos ? sacc[i] : -INFINITY;
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float x = sacc[i] * a.scale_log2;
-      if (diag) {
-        const int key = kb + 32 * kh + 8 * (i >> 2) + 4 * g + (i & 3);
-        x = key <= pos ? x : -INFINITY;
-      }
-      sacc[i] = x;
-      mx = fmaxf(mx, x);
-    }
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     if (g == 0) red_max[kh][qk_head] = mx;
     __syncthreads();
-    const float m_new = fmaxf(m_run, fmaxf(red_max[0][qk_head], red_max[1][qk_head]));
-    const float alpha = exp2f(m_run - m_new);  // key 0 is in tile 0, so m_new is finite
-    m_run = m_new;
+    // reference max in the scaled log2 domain, moved lazily (only when the
+    // tile's max exceeds it by more than 2^8; O and l share it, so the result
+    // is unchanged); p = 2^(s * c - m): one FMA + v_exp_f32. Key 0 is in tile
+    // 0, so the reference is finite from then on.
+    const float mt = fmaxf(red_max[0][qk_head], red_max[1][qk_head]) * a.scale_log2;
+    float alpha = 1.f;
+    if (mt > m_run + 8.f) {
+      alpha = __builtin_amdgcn_exp2f(m_run - mt);
+      m_run = mt;
+    }
+    const float m_new = m_run;
     float psum = 0.f;
     uint32_t pk[8];
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
-      const float p0 = exp2f(sacc[i] - m_new), p1 = exp2f(sacc[i + 1] - m_new);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[i], a.scale_log2, -m_new));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[i + 1], a.scale_log2, -m_new));
       psum += p0 + p1;
       pk[i >> 1] = pack_bf16(p0, p1);
     }
@@ -224,8 +234,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mla_kernel(Args a) {
       const bf16x8 pb1 = *reinterpret_cast<const bf16x8*>(plds + (32 + col) * kPRowBytes + (2 * ks + g) * 16);
 #pragma unroll
       for (int mtv = 0; mtv < 4; ++mtv) {
-        const i16x4 v0 = lds_read_tr(T + pv_off[ks][0][mtv & 1] + 128 * (mtv >> 1));
-        const i16x4 v1 = lds_read_tr(T + pv_off[ks][1][mtv & 1] + 128 * (mtv >> 1));
+        const i16x4 v0 = lds_read_tr(T + pv_off[0][mtv & 1] + 16 * ks * kRowBytes + 128 * (mtv >> 1));
+        const i16x4 v1 = lds_read_tr(T + pv_off[1][mtv & 1] + 16 * ks * kRowBytes + 128 * (mtv >> 1));
         const bf16x8 va = join_tr(v0, v1);
         oacc[mtv][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb0, oacc[mtv][0], 0, 0, 0);
         oacc[mtv][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb1, oacc[mtv][1], 0, 0, 0);

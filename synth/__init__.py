@@ -128,6 +128,29 @@ def latent_cache(config, stream, B, L, D, std, chunk=8192, fp8=False):
     return (codes, scales) if fp8 else codes
 
 
+def latent_cache_both(config, stream, B, L, D, std, chunk=8192):
+    """One draw of a [B, L, 1, D] latent cache, stored both as bf16 words and
+    as E4M3 codes with per-token scales: (bf16, codes, scales [B, L])."""
+    bits = np.empty((B, L, 1, D), dtype=np.uint16)
+    codes = np.empty((B, L, 1, D), dtype=np.uint8)
+    scales = np.empty((B, L), dtype=np.float32)
+    jobs = [(b, i, a, e) for b in range(B) for (i, a, e) in _slabs(L, chunk)]
+
+    def work(job):
+        b, i, a, e = job
+        g = rng(config, stream, b * 100000 + i)
+        x = g.standard_normal((e - a, D), dtype=np.float32)
+        x *= np.float32(std)
+        bits[b, a:e, 0] = f32_to_bf16_bits(x)
+        c, s = f32_to_e4m3(x)
+        codes[b, a:e, 0] = c
+        scales[b, a:e] = s
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, jobs))
+    return bits, codes, scales
+
+
 # ---------------------------------------------------------------- workloads
 
 AGENTIC_MEDIAN = 67 * 1024  # "median of ~67k tokens"; k = 1024

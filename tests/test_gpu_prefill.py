@@ -149,3 +149,46 @@ def test_prefill_zigzag_gqa_workload(cpa):
 def torch_isfinite_all(t):
     import torch
     return torch.isfinite(t.float()).all().item()
+
+
+# ------------------------------------------------------------------ MLA prefill
+
+def _run_mla(cpa, strategy, C, rank, new_len, prefix, seed, out_f32=False, spiky=False, rows=None):
+    import torch
+    fn = cpa.cp_plan_zigzag if strategy == "zigzag" else cpa.cp_plan_interleave
+    plan = fn(C, rank, new_len, prefix)
+    ref_plan = (plans.plan_zigzag if strategy == "zigzag" else plans.plan_interleave)(C, rank, new_len, prefix)
+    T_kv = int(sum(new_len) + (sum(prefix) if prefix else 0))
+    rng = np.random.default_rng(seed)
+    qb = synth.f32_to_bf16_bits(rng.standard_normal((max(plan.n_local, 1), 64, 576)).astype(np.float32))[:plan.n_local]
+    lx = rng.standard_normal((T_kv, 1, 576)).astype(np.float32)
+    if spiky:
+        lx[rng.integers(0, T_kv, size=max(1, T_kv // 40))] *= 5.0
+    lb = synth.f32_to_bf16_bits(lx)
+    scale = (6.0 if spiky else 1.0) / math.sqrt(576)
+    o, l = cpa.attn_prefill_shard(H.bf16_tensor(qb), H.bf16_tensor(lb), None, plan.segments, scale,
+                                  out_dtype=torch.float32 if out_f32 else torch.bfloat16)
+    _sync()
+    if plan.n_local == 0:
+        return
+    ro, rl = att.prefill_shard(qb, lb, ref_plan.segments, scale, dv=512, rows=rows, decode=formats.bf16_bits_to_f64)
+    go, gl = H.host(o), H.host(l)
+    if rows is not None:
+        go, gl = go[rows], gl[rows]
+    chk = H.check_lowp_scaled if spiky else H.check_lowp
+    chk(go, gl, ro, rl, f"MLA {strategy} C={C} r={rank} L={new_len} P={prefix}")
+
+
+def test_prefill_mla_zigzag_prefix(cpa):
+    for rank in range(2):
+        _run_mla(cpa, "zigzag", 2, rank, [200], [70], 60 + rank)
+    _run_mla(cpa, "zigzag", 4, 3, [130, 5], [0, 64], 62, out_f32=True)
+
+
+def test_prefill_mla_interleave_ragged(cpa):
+    _run_mla(cpa, "interleave", 3, 1, [90, 1, 140], [10, 0, 63], 63)
+
+
+def test_prefill_mla_spiky(cpa):
+    # planted large latents are large values too (value = latent): f32 output
+    _run_mla(cpa, "zigzag", 2, 0, [300], [30], 64, spiky=True, out_f32=True)

@@ -1,0 +1,144 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times, checked on outputs the oracle computes one by one (sampled
+requests / rows, always including the first and last row of every segment)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import attention as att
+from oracle import formats, plans
+from tests import helpers as H
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module")
+def cpa():
+    import torch
+    import context_attention_long_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.lib()
+    return m
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _sample_rows(plan, n_extra, seed):
+    rows = set()
+    for s in plan.segments:
+        r0, n = int(s["q_row0"]), int(s["q_len"])
+        rows.update([r0, r0 + n - 1, r0 + n // 2])
+    rng = synth.rng(seed, 9)
+    rows.update(int(x) for x in rng.integers(0, plan.n_local, size=n_extra))
+    return sorted(rows)
+
+
+@pytest.fixture(scope="module")
+def mla_decode_inputs():
+    c = synth.config(3)
+    print("[mla decode] generating inputs", flush=True)
+    q = synth.bf16_normal(3, 1, (c["B"], c["Hq"], c["Dqk"]))
+    bits, codes, scales = synth.latent_cache_both(3, 2, c["B"], c["L"], c["Dqk"], c["std"])
+    return c, q, bits, codes, scales
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_mla_decode_workload(cpa, mla_decode_inputs, fp8):
+    """MLA decode: batch 64, 64 heads, 576/512, 131072-token context per
+    request, cut into C=8 contiguous shards run as 8 partial launches on one
+    device + one merge; bf16 cache, then FP8 E4M3 with per-token scale."""
+    import torch
+    c, q, bits, codes, scales = mla_decode_inputs
+    B, L, C = c["B"], c["L"], c["C"]
+    qd = H.bf16_tensor(q)
+    cd = H.u8_tensor(codes) if fp8 else H.bf16_tensor(bits)
+    sd = H.f32_tensor(scales) if fp8 else None
+    shards = plans.contiguous_shards(L, C)
+    po = torch.empty((C, B, 64, 512), dtype=torch.float32, device="cuda")
+    pl = torch.empty((C, B, 64), dtype=torch.float32, device="cuda")
+    ws = torch.empty(cpa.attn_decode_workspace_size(B, 64, 512, L // C), dtype=torch.uint8, device="cuda")
+    for i, (s0, s1) in enumerate(shards):
+        cpa.attn_decode_shard(qd, cd, None, H.i32_tensor(np.full(B, s0)), H.i32_tensor(np.full(B, s1)), s1 - s0,
+                              c["scale"], kv_scale=sd, o_part=po[i], lse_part=pl[i], workspace=ws)
+    mo, ml = cpa.attn_merge_states(po, pl)
+    _sync()
+    print(f"[mla decode fp8={fp8}] kernels done; oracle", flush=True)
+    q64 = formats.bf16_bits_to_f64(q)
+    cache, dec = (codes, formats.e4m3_to_f64) if fp8 else (bits, formats.bf16_bits_to_f64)
+    sc = scales if fp8 else None
+    reqs = [0, 37, 63]
+    # merged output against unsharded attention over the whole context
+    ro, rl = att.decode_shard(q64, cache, [0] * B, [L] * B, c["scale"], dv=512, decode=dec, kv_scale=sc, batch=reqs)
+    e = H.check_lowp(H.host(mo)[reqs], H.host(ml)[reqs], ro[reqs], rl[reqs], f"MLA decode merged fp8={fp8}")
+    print(f"MLA decode fp8={fp8} merged errors (O abs, LSE abs, O rel):", e)
+    # one shard's partial state against the shard oracle
+    s0, s1 = shards[5]
+    ro, rl = att.decode_shard(q64, cache, [s0] * B, [s1] * B, c["scale"], dv=512, decode=dec, kv_scale=sc,
+                              batch=[11])
+    H.check_lowp(H.host(po[5])[[11]], H.host(pl[5])[[11]], ro[[11]], rl[[11]], "MLA decode shard 5")
+    assert bool(torch.isfinite(mo).all()) and bool(torch.isfinite(ml).all())
+
+
+def test_mla_prefill_zigzag_workload(cpa):
+    """MLA zigzag prefill: 64 heads, 576/512, 131072 new tokens after a
+    32768-token cached prefix, C=8 (16 blocks of 8192), rank 0's share."""
+    import torch
+    c = synth.config(4)
+    plan = cpa.cp_plan_zigzag(c["C"], c["rank"], c["new_len"], c["prefix_len"])
+    T = sum(c["new_len"]) + sum(c["prefix_len"])
+    print("[mla prefill] generating inputs", flush=True)
+    qb = synth.bf16_normal(4, 1, (plan.n_local, 64, 576), chunk=256)
+    lb = synth.bf16_normal(4, 2, (T, 1, 576))
+    o, l = cpa.attn_prefill_shard(H.bf16_tensor(qb), H.bf16_tensor(lb), None, plan.segments, c["scale"])
+    _sync()
+    rows = _sample_rows(plan, 10, 4)
+    ref = plans.plan_zigzag(c["C"], c["rank"], c["new_len"], c["prefix_len"])
+    lat64 = formats.bf16_bits_to_f64(lb)
+    print(f"[mla prefill] kernel done; oracle on {len(rows)} rows", flush=True)
+    ro, rl = att.prefill_shard(formats.bf16_bits_to_f64(qb[rows]), lat64, _remap(ref.segments, rows),
+                               c["scale"], dv=512, rows=list(range(len(rows))))
+    e = H.check_lowp(H.host(o)[rows], H.host(l)[rows], ro, rl, "MLA zigzag workload")
+    print("MLA zigzag workload errors (O abs, LSE abs, O rel):", e)
+    assert bool(torch.isfinite(l).all())
+
+
+def _remap(segments, rows):
+    """Segments for a compacted copy of the sampled rows: row i of the copy is
+    local row rows[i], one single-row segment each."""
+    out = []
+    for i, r in enumerate(rows):
+        for (req, r0, n, pos0, stride, kv0) in segments:
+            if r0 <= r < r0 + n:
+                out.append((req, i, 1, pos0 + (r - r0) * stride, 1, kv0))
+    return out
+
+
+def test_interleave_ragged_workload(cpa):
+    """Interleave prefill on a ragged batch: 16 agentic-length requests
+    (T = 728,040), C=4, rank 2; causal GQA 32/8, d=128, bf16."""
+    import torch
+    c = synth.config(5)
+    plan = cpa.cp_plan_interleave(c["C"], c["rank"], c["new_len"], c["prefix_len"])
+    assert plan.n_local == 182010
+    T = sum(c["new_len"])
+    print("[interleave] generating inputs", flush=True)
+    qb = synth.bf16_normal(5, 1, (plan.n_local, 32, 128))
+    kb = synth.bf16_normal(5, 2, (T, 8, 128))
+    vb = synth.bf16_normal(5, 3, (T, 8, 128))
+    o, l = cpa.attn_prefill_shard(H.bf16_tensor(qb), H.bf16_tensor(kb), H.bf16_tensor(vb), plan.segments, c["scale"])
+    _sync()
+    rows = _sample_rows(plan, 16, 5)
+    ref = plans.plan_interleave(c["C"], c["rank"], c["new_len"], c["prefix_len"])
+    segs = _remap(ref.segments, rows)
+    print(f"[interleave] kernel done; oracle on {len(rows)} rows", flush=True)
+    ro, rl = att.prefill_shard(qb[rows].copy(), kb, segs, c["scale"], v=vb, rows=list(range(len(rows))),
+                               decode=formats.bf16_bits_to_f64)
+    e = H.check_lowp(H.host(o)[rows], H.host(l)[rows], ro, rl, "interleave workload")
+    print("interleave workload errors (O abs, LSE abs, O rel):", e)
+    assert bool(torch.isfinite(l).all())
