@@ -179,7 +179,13 @@ __device__ __forceinline__ void consume_tile(const char* tile, const float* scal
     st.m_run = m_new;
     st.l_run *= alpha;
 #pragma unroll
-    for (int m = 0; m < kDv / 16; ++m) st.oacc[m] *= alpha;
+    for (int m = 0; m < kDv / 16; ++m) {
+      // (the opaque step first keeps the AGPR -> VGPR copies inside this rare
+      // branch; otherwise they are hoisted into every tile)
+      asm volatile("" : "+a"(st.oacc[m]));
+      st.oacc[m] *= alpha;
+      asm volatile("" : "+a"(st.oacc[m]));
+    }
   }
   const float m_new = st.m_run;
   float psum = 0.f;
@@ -210,6 +216,9 @@ __device__ __forceinline__ void consume_tile(const char* tile, const float* scal
                        lds_read_tr(tile + L.pv[1][mm & 3] + 128 * (mm >> 2)));
     }
     st.oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb, st.oacc[m], 0, 0, 0);
+    // keep the accumulator in AGPRs across the tile loop (otherwise it is
+    // copied between AGPRs and VGPRs every tile)
+    asm volatile("" : "+a"(st.oacc[m]));
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -286,7 +295,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
 
   State st;
 #pragma unroll
-  for (int m = 0; m < kDv / 16; ++m) st.oacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < kDv / 16; ++m) {
+    st.oacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    asm volatile("" : "+a"(st.oacc[m]));
+  }
   st.m_run = -INFINITY;
   st.l_run = 0.f;
   const LdsBases L = lds_bases(g, c);
