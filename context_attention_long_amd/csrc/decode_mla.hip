@@ -60,8 +60,15 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 static_assert(kTileChunks % kThreads == 0, "tile must split evenly over the threads");
 
-// Physical 16-byte chunk of logical chunk `c` in LDS row `r`.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+// Physical 16-byte chunk of logical chunk `c` in LDS row `r` (XOR inside the
+// aligned group of 8 chunks). gfx950 LDS has 64 four-byte banks (256 B per
+// clock); a row is 1152 B, so rows alternate between the two 128-byte bank
+// halves and the XOR must separate the rows one read pass touches. With
+// f(r) = bits (b0, b2, b1) of r both operand reads run at the full LDS rate:
+// the 16-byte K reads (16 rows x 4 chunks) and the 8-byte transposing V
+// reads (4 rows x 2 chunks per 16 lanes); the previous f(r) = (r ^ r>>3) & 7
+// halved the K read rate (measured with a microbenchmark of these patterns).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 1) | ((r & 2) << 1) | ((r & 4) >> 1)); }
 
 __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(

@@ -72,11 +72,15 @@ struct Args {
   Seg seg[kMaxSeg];
 };
 
-// Physical chunk of logical 16-byte chunk c in tile row r. The 4-bit
-// permutation of the row index makes the 16 rows of one QK operand read and
-// the 4 rows x 2 chunks of one transposing V read hit distinct banks.
+// Physical chunk of logical 16-byte chunk c in tile row r (256-byte rows,
+// XOR over the row's 16 chunks). f is linear in the row's low 4 bits; it
+// keeps both operand reads at the full gfx950 LDS rate (64 banks x 4 B):
+// the 16-byte K reads (32 rows x 2 chunks) and the 8-byte transposing V
+// reads (4 rows x 2 chunk halves per 16 lanes). The rates of these exact
+// patterns were measured; a plain bit permutation of the row index left the
+// V reads at half rate.
 __device__ __forceinline__ int swz(int r, int c) {
-  const int f = ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  const int f = ((r & 1) ? 14 : 0) ^ ((r & 2) ? 9 : 0) ^ ((r & 4) ? 8 : 0) ^ ((r & 8) ? 2 : 0);
   return c ^ f;
 }
 

@@ -64,11 +64,14 @@ struct Args {
   Seg seg[kMaxSeg];
 };
 
-// Physical 16-byte chunk of logical chunk c in latent row r: XOR of the low
-// 3 chunk bits with a permutation of r mod 16, so that the 16 rows of one QK
-// operand read and the 4 rows x 2 chunks of one transposing read fall in
-// distinct banks, and rows 16 apart share offsets (immediate addressing).
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ ((r >> 3) & 1)) & 7); }
+// Physical 16-byte chunk of logical chunk c in latent row r: the low 3 chunk
+// bits XOR f(r), f = row bits (b2, b3, b1), a function of r mod 16 so that
+// rows 16 apart share offsets (immediate addressing). On gfx950's LDS
+// (64 banks x 4 B, 1152-byte rows alternate bank halves) this keeps the
+// 16-byte QK reads (32 rows x 2 chunks) and the 8-byte transposing V reads
+// (4 rows x 2 chunk halves per 16 lanes) at the full read rate; the rates of
+// these patterns were measured.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 2) << 1) | ((r & 4) >> 2) | ((r & 8) >> 2)); }
 
 __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
