@@ -35,6 +35,45 @@ METRIC = "split-KV decode GB/s (% HBM peak); zigzag prefill TFLOP/s (% MFMA peak
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# HBM traffic per launch of the dominant kernels, from rocprofv3 --pmc runs of
+# this script (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled
+# by what the same counter read for a plain device copy of known size. A
+# figure is reported only while the kernel sources still hash to the digest
+# they were measured at; after any change the field is null until re-measured.
+TRAFFIC = {
+    # profiles/prefill_gqa_zigzag_16k_c4_rank1.md
+    "prefill_gqa_kernel": dict(digest="f4c5284df440642f", fetch_kib=59977.3, write_kib=33792.3,
+                               fetch_scale=1.99994, write_scale=1.0,
+                               fetch_bytes=122830013, write_bytes=34603352),
+    # profiles/decode_mla_b64_h64_ctx131072_c8.md
+    "decode_mla_kernel<bf16>": dict(digest="ae03b88e197884f1", fetch_kib=599161.1, write_kib=32832.0,
+                                    fetch_scale=1.99994, write_scale=1.0,
+                                    fetch_bytes=1227047643, write_bytes=33619968),
+}
+
+
+def _src_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "context_attention_long_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "prefill_gqa_kernel": ("prefill.hip", "lds_dma.h"),
+    "decode_mla_kernel<bf16>": ("decode_mla.hip", "lds_dma.h"),
+}
+
+
+def traffic(kernel):
+    """(HBM bytes per launch, how they were obtained), or (None, None)."""
+    t = TRAFFIC.get(kernel)
+    if t is None or t["digest"] != _src_digest(KERNEL_SOURCES[kernel]):
+        return None, None
+    return t["fetch_bytes"] + t["write_bytes"], {k: v for k, v in t.items() if k != "digest"}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -186,7 +225,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-only", action="store_true", help="time only the MLA decode (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run one 512 MiB device-to-device copy (reference for HBM counters)")
+                    help="first run one 2 GiB device-to-device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -202,13 +241,14 @@ def main():
     cpa.lib()
 
     if args.copy_calibration:
-        # a plain copy of known size: 512 MiB read + 512 MiB written
-        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        # a plain copy of known size: 2 GiB read + 2 GiB written (larger than
+        # the last-level cache, so it runs from and to HBM)
+        src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        log("[bench] copy calibration: 536870912 bytes read, 536870912 written")
+        log("[bench] copy calibration: 2147483648 bytes read, 2147483648 written")
         del src, dst
         torch.cuda.empty_cache()
 
@@ -251,7 +291,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic("prefill_gqa_kernel")[0],
+            "traffic_detail": traffic("prefill_gqa_kernel")[1],
             "kernel_ms": round(kms, 4),
         },
     }
@@ -270,7 +311,9 @@ def main():
             "roofline": {
                 "kernel": "decode_mla_kernel (bf16 cache)", "bound": "hbm",
                 "achieved": round(dec["bf16"]["launch_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(dec["bf16"]["launch_gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                "frac": round(dec["bf16"]["launch_gbs"] / PEAK_HBM_GBS, 4),
+                "traffic": traffic("decode_mla_kernel<bf16>")[0],
+                "traffic_detail": traffic("decode_mla_kernel<bf16>")[1],
             },
             "frac_of_hbm_peak_step": {k: round(dec[k]["gbs"] / PEAK_HBM_GBS, 4) for k in ("bf16", "fp8")},
         }

@@ -130,17 +130,36 @@ struct State {
   float l_run;  // this lane's share of the running sum
 };
 
+// Maximum over the four lanes l, l^16, l^32, l^48 (one head's four score
+// groups), with the gfx950 row-swap permutes instead of LDS round trips.
+__device__ __forceinline__ float max4_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // One 32-token tile: scores, online softmax update, PV accumulation.
-template <bool kFp8>
+// hook(s) runs at the start of QK k-step s (the caller issues the next
+// tile's loads there, spread over the MFMA work).
+template <bool kFp8, typename Hook>
 __device__ __forceinline__ void consume_tile(const char* tile, const float* scales, int nvalid, int g,
                                              const LdsBases& L, const bf16x8 (&qreg)[kDk / 32],
-                                             float scale_log2, State& st) {
-  // ---- S^T = K Q^T: two 16-token blocks, chains interleaved ----
-  // K operands are read kAhead k-steps ahead of their MFMAs; a scheduling
-  // barrier closes every step so the reads cannot sink next to their use and
-  // LDS latency overlaps MFMA work.
+                                             float scale_log2, State& st, Hook&& hook) {
   constexpr int kSteps = kDk / 32;  // 18
   constexpr int kAhead = 4;
+  constexpr int kMt = kDv / 16;     // 32 PV m-tiles
+  constexpr int kAheadV = 4;        // V operands read ahead; the first ones load during the last QK steps
+  bf16x8 va[kMt];
+  auto load_v = [&](int m) {
+    va[m] = join_tr(lds_read_tr(tile + L.pv[0][m & 3] + 128 * (m >> 2)),
+                    lds_read_tr(tile + L.pv[1][m & 3] + 128 * (m >> 2)));
+  };
+  // ---- S^T = K Q^T: two 16-token blocks, chains interleaved ----
+  // K operands are read kAhead k-steps ahead of their MFMAs (the last
+  // kAheadV steps also read the first V operands); a scheduling barrier closes every
+  // step so the reads cannot sink next to their use and LDS latency overlaps
+  // MFMA work.
   f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   bf16x8 ka[kSteps][2];
 #pragma unroll
@@ -150,12 +169,14 @@ __device__ __forceinline__ void consume_tile(const char* tile, const float* scal
       ka[s][mt] = *reinterpret_cast<const bf16x8*>(tile + L.qk[mt][s & 1] + 128 * (s >> 1));
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
+    hook(s);
     if (s + kAhead < kSteps) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
         ka[s + kAhead][mt] =
             *reinterpret_cast<const bf16x8*>(tile + L.qk[mt][(s + kAhead) & 1] + 128 * ((s + kAhead) >> 1));
     }
+    if (s >= kSteps - kAheadV) load_v(s - (kSteps - kAheadV));
     sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s][0], qreg[s], sacc[0], 0, 0, 0);
     sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s][1], qreg[s], sacc[1], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -174,8 +195,7 @@ __device__ __forceinline__ void consume_tile(const char* tile, const float* scal
       x[4 * mt + i] = v;
       mx = fmaxf(mx, v);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max4_rows(mx);
   // Lazy rescale: the reference max m_run only moves when a score exceeds it
   // by more than 2^8; until then p = 2^(s - m_run) <= 256, and O and l share
   // the same reference, so the result is unchanged. The first tile always
@@ -208,20 +228,9 @@ __device__ __forceinline__ void consume_tile(const char* tile, const float* scal
   const bf16x8 pb = pack8(pf);
   st.l_run += psum;
   // ---- O^T += V^T P^T: V^T operands read kAheadV m-tiles ahead (same scheme) ----
-  constexpr int kMt = kDv / 16;  // 32
-  constexpr int kAheadV = 4;
-  bf16x8 va[kMt];
-#pragma unroll
-  for (int m = 0; m < kAheadV; ++m)
-    va[m] = join_tr(lds_read_tr(tile + L.pv[0][m & 3] + 128 * (m >> 2)),
-                    lds_read_tr(tile + L.pv[1][m & 3] + 128 * (m >> 2)));
 #pragma unroll
   for (int m = 0; m < kMt; ++m) {
-    if (m + kAheadV < kMt) {
-      const int mm = m + kAheadV;
-      va[mm] = join_tr(lds_read_tr(tile + L.pv[0][mm & 3] + 128 * (mm >> 2)),
-                       lds_read_tr(tile + L.pv[1][mm & 3] + 128 * (mm >> 2)));
-    }
+    if (m + kAheadV < kMt) load_v(m + kAheadV);
     st.oacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb, st.oacc[m], 0, 0, 0);
     // keep the accumulator in AGPRs across the tile loop (otherwise it is
     // copied between AGPRs and VGPRs every tile)
@@ -326,14 +335,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
       if (tok0 + kBN <= t1) {
         const uint16_t* tb = base + tok0 * a.c_t;
 #pragma unroll
-        for (int k = 0; k < kLdChunks; ++k) cpa::lds_dma16_sbase(tb, toff[k], cpa::lds_addr(dst0 + kThreads * k * 16));
+        for (int k = 0; k < kLdChunks; ++k) cpa::lds_dma16_sbase<cpa::Policy::kStream>(tb, toff[k], cpa::lds_addr(dst0 + kThreads * k * 16));
       } else {  // last tile: tokens past the split re-read its last token (masked)
 #pragma unroll
         for (int k = 0; k < kLdChunks; ++k) {
           const int P = tid + kThreads * k;
           const int row = P / kRowChunks, pc = P % kRowChunks;
           const int64_t tok = min(tok0 + row, t1 - 1);
-          cpa::lds_dma16(base + tok * a.c_t + swz(row, pc) * 8, cpa::lds_addr(dst0 + kThreads * k * 16));
+          cpa::lds_dma16<cpa::Policy::kStream>(base + tok * a.c_t + swz(row, pc) * 8, cpa::lds_addr(dst0 + kThreads * k * 16));
         }
       }
     };
@@ -341,9 +350,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
     for (int i = 0; i < ntiles; ++i) {
       wait_ahead<kLdChunks>(min(2, ntiles - 1 - i));  // tile i landed
       __syncthreads();  // tile i visible to all; every wave is done with tile i-1
-      if (i + 3 < ntiles) issue(i + 3);  // into the stage tile i-1 used
+      // tile i+3 goes into the stage tile i-1 used: a full tile's loads are
+      // spread over the QK steps of tile i (one every other step), the
+      // clamped last tile is issued at once
+      const int64_t nxt0 = t0 + (int64_t)(i + 3) * kBN;
+      const bool spread = (i + 3 < ntiles) && (nxt0 + kBN <= t1);
+      if (i + 3 < ntiles && !spread) issue(i + 3);
+      const uint16_t* ntb = base + nxt0 * a.c_t;
+      char* ndst = smem + ((i + 3) & 3) * kStageBytes + 64 * w * 16;
       consume_tile<false>(smem + (i & 3) * kStageBytes, nullptr, min(kBN, ntok - kBN * i), g, L, qreg,
-                          a.scale_log2, st);
+                          a.scale_log2, st, [&](int s) {
+                            if (spread && (s & 1) == 0 && (s >> 1) < kLdChunks)
+                              cpa::lds_dma16_sbase<cpa::Policy::kStream>(ntb, toff[s >> 1], cpa::lds_addr(ndst + kThreads * (s >> 1) * 16));
+                          });
     }
   } else {
     // ---- FP8: raw stage u % 4 holds the e4m3 bytes of tile u; bf16 tile u % 2 ----
@@ -367,19 +386,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
         const uint8_t* tb = base + tok0 * a.c_t;
 #pragma unroll
         for (int k = 0; k < 5; ++k)
-          if (k < n_mine) cpa::lds_dma16_sbase(tb, roff[k], cpa::lds_addr(dst + (w + 4 * k) * 1024));
+          if (k < n_mine) cpa::lds_dma16_sbase<cpa::Policy::kStream>(tb, roff[k], cpa::lds_addr(dst + (w + 4 * k) * 1024));
       } else {  // last tile: past the split, re-read its last token (masked)
 #pragma unroll
         for (int k = 0; k < 5; ++k) {
           if (k < n_mine) {
             const int B = (w + 4 * k) * 1024 + 16 * lane;
             const int64_t tok = min(tok0 + B / kDk, t1 - 1);
-            cpa::lds_dma16(base + tok * a.c_t + (B % kDk), cpa::lds_addr(dst + (w + 4 * k) * 1024));
+            cpa::lds_dma16<cpa::Policy::kStream>(base + tok * a.c_t + (B % kDk), cpa::lds_addr(dst + (w + 4 * k) * 1024));
           }
         }
       }
       const int64_t tok = min(tok0 + lane, t1 - 1);
-      cpa::lds_dma4(sbase + tok * a.s_t, cpa::lds_addr(&rscale[u & 3][w][0]));
+      cpa::lds_dma4<cpa::Policy::kStream>(sbase + tok * a.s_t, cpa::lds_addr(&rscale[u & 3][w][0]));
     };
     auto wait_raw = [&](int ahead) {
       if (w < 2) wait_ahead<6>(ahead);  // 5 cache loads + 1 scale load per tile
@@ -399,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
         convert_tile(raw + ((u + 1) & 3) * kRawBytes, &rscale[(u + 1) & 3][0][0], btile + ((u + 1) & 1) * kStageBytes,
                      bscale[(u + 1) & 1]);
       consume_tile<true>(btile + (u & 1) * kStageBytes, bscale[u & 1], min(kBN, ntok - kBN * u), g, L, qreg,
-                         a.scale_log2, st);
+                         a.scale_log2, st, [](int) {});
     }
   }
 

@@ -22,34 +22,62 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
+// Cache policy of the loads. Stream = data read once per launch (a decode
+// shard of the KV cache): the nontemporal hint, the encoding the compiler
+// itself uses for __builtin_nontemporal_load; it raised the streaming rate of
+// the decode loads from 5.3 to 6.1 TB/s. Reuse = tiles that many workgroups
+// read again through L2 (prefill K/V): default policy.
+enum class Policy { kReuse, kStream };
+
 // One 16-byte load per lane into LDS at lds_base + 16 * lane. `lds_base` must
 // be the same for the whole wavefront.
+template <Policy P = Policy::kReuse>
 __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
+  if constexpr (P == Policy::kStream)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
 }
 
 // Same, addressed as a wavefront-uniform 64-bit base plus a per-lane 32-bit
 // byte offset (the base goes to SGPRs, so stepping it costs no VALU work).
+template <Policy P = Policy::kReuse>
 __device__ __forceinline__ void lds_dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
   const uint64_t b = reinterpret_cast<uint64_t>(sbase);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
   const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
+  if constexpr (P == Policy::kStream)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
 }
 
 // One 4-byte load per lane into LDS at lds_base + 4 * lane.
+template <Policy P = Policy::kReuse>
 __device__ __forceinline__ void lds_dma4(const void* gsrc, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
+  if constexpr (P == Policy::kStream)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off nt"
+                 :
+                 : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
 }
 
 // Wait until at most N vector-memory operations of this wavefront are
