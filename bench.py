@@ -119,6 +119,41 @@ def bench_prefill(cpa, torch, synth, steps, warmup):
                 inputs=(q, k, v))
 
 
+def bench_prefill_config(cpa, torch, synth, k, steps, warmup):
+    """One more prefill shard workload (config 4: MLA zigzag with a cached
+    prefix; config 5: interleave over the ragged agentic batch), timed per
+    launch with HIP events: algorithmic TFLOP/s."""
+    c = synth.config(k)
+    planner = cpa.cp_plan_zigzag if c["strategy"] == "zigzag" else cpa.cp_plan_interleave
+    plan = planner(c["C"], c["rank"], c["new_len"], c["prefix_len"])
+    T = sum(c["new_len"]) + sum(c["prefix_len"])
+    dev = torch.device("cuda:0")
+    to_dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    q = to_dev(synth.bf16_normal(k, 1, (plan.n_local, c["Hq"], c["Dqk"]), chunk=256))
+    kk = to_dev(synth.bf16_normal(k, 2, (T, c["Hkv"], c["Dqk"])))
+    v = None if c["Hkv"] == 1 else to_dev(synth.bf16_normal(k, 3, (T, c["Hkv"], c["Dv"])))
+    out = torch.empty((plan.n_local, c["Hq"], c["Dv"]), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((plan.n_local, c["Hq"]), dtype=torch.float32, device=dev)
+    # causal pairs per head: each local row attends to positions 0..pos (prefix included)
+    pairs = int(np.sum(plan.pos_id.astype(np.int64) + 1))
+    flops = pairs * c["Hq"] * 2 * (c["Dqk"] + c["Dv"])
+    for _ in range(warmup):
+        cpa.attn_prefill_shard(q, kk, v, plan.segments, c["scale"], out=out, lse=lse)
+    torch.cuda.synchronize()
+    evs = _events(torch, steps)
+    for i in range(steps):
+        evs[i][0].record()
+        cpa.attn_prefill_shard(q, kk, v, plan.segments, c["scale"], out=out, lse=lse)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    del q, kk, v, out, lse
+    torch.cuda.empty_cache()
+    tf = flops / (kms * 1e-3) / 1e12
+    return {"workload": c["name"], "local_rows": plan.n_local, "algorithmic_tflop": round(flops / 1e12, 3),
+            "kernel_ms": round(kms, 3), "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def bench_decode(cpa, torch, synth, steps, warmup):
     c = synth.config(3)
     B, L, C, H = c["B"], c["L"], c["C"], c["Hq"]
@@ -224,6 +259,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-only", action="store_true", help="time only the MLA decode (profiling)")
+    ap.add_argument("--no-extra-prefill", action="store_true",
+                    help="skip the MLA zigzag (prefix) and ragged interleave prefill figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 2 GiB device-to-device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -318,6 +355,12 @@ def main():
             "frac_of_hbm_peak_step": {k: round(dec[k]["gbs"] / PEAK_HBM_GBS, 4) for k in ("bf16", "fp8")},
         }
         log(f"[bench] decode bf16 {dec['bf16']['gbs']:.0f} GB/s/step, fp8 {dec['fp8']['gbs']:.0f} GB/s/step")
+
+    if not args.no_extra_prefill:
+        for k, key in ((4, "prefill_mla_zigzag"), (5, "prefill_interleave")):
+            log(f"[bench] {key} (config {k}) ...")
+            line[key] = bench_prefill_config(cpa, torch, synth, k, max(2, args.steps // 10), 1)
+            log(f"[bench] {key}: {line[key]['kernel_ms']} ms, {line[key]['tflops']} TFLOP/s")
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")

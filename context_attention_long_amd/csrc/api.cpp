@@ -456,7 +456,8 @@ extern "C" cpa_status attn_prefill_shard(const cpa_tensor* q, const cpa_tensor* 
     return hip_status(cpa::launch_prefill_gqa(a, seg, n_seg, stream), "prefill launch");
   }
   if (Hq != 64) return fail(CPA_E_UNSUPPORTED, "prefill: MLA kernel is built for 64 query heads, got %lld", (long long)Hq);
-  if (k->stride[0] > ((int64_t)1 << 40)) return fail(CPA_E_INVAL, "prefill: latent stride too large");
+  // the kernel addresses a 32-token tile with 32-bit per-thread byte offsets
+  if (k->stride[0] > ((int64_t)1 << 26)) return fail(CPA_E_INVAL, "prefill: latent token stride too large");
   cpa::PrefillMlaArgs a{};
   a.q = static_cast<const uint16_t*>(q->data);
   a.lat = static_cast<const uint16_t*>(k->data);

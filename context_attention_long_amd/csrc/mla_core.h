@@ -1,0 +1,462 @@
+// Attention of one query (64 heads) over a contiguous range of an MLA latent
+// cache, on one 4-wavefront workgroup: the shared core of the split-KV
+// decode kernel and the MLA prefill kernel.
+//
+// What it computes: "How GPUs Share a Long Context During LLM Inference",
+// 1.3 and 3.2-3.4 -- all heads of a query read one latent vector per token;
+// vLLM GLM-5.3 post, footnote 1 -- QK runs over the 576 latent dims and PV
+// over 512 (the value of a token is the first 512 dims of its latent). FP8
+// entries are e4m3 * scale_t. The result is the unnormalised running state
+// (O, running max, running sum) of the online softmax over the range.
+//
+// Design (gfx950):
+//  * 32-token tiles of the latent are staged in LDS by direct global -> LDS
+//    loads: bf16 keeps 4 stages (3 tiles in flight while one is consumed),
+//    FP8 keeps 4 raw stages plus 2 converted bf16 tiles; the next tile's
+//    loads are spread over the QK steps of the current one;
+//  * QK: wave w computes S^T = K Q^T for heads 16w..16w+15 with
+//    v_mfma_f32_16x16x32_bf16 (A = 16 tokens x 32 dims from the LDS tile,
+//    B = Q^T held in registers for the whole range); each lane ends with 8
+//    scores of one head, the head's row max takes two row-swap permutes;
+//  * the wave turns its scores into bf16 probabilities P and writes them to
+//    LDS (one 16-byte store per lane) together with each head's rescale
+//    factor; one barrier later
+//  * PV: wave w accumulates O^T for value dims [128w, 128w+128) of all 64
+//    heads: A = V^T read from the same latent tile with ds_read_b64_tr_b16
+//    (each read feeds 4 MFMAs, one per head block), B = P^T from LDS. The
+//    32 tokens of a k-step are taken in the order the score registers hold
+//    them, so P needs no shuffle;
+//  * the softmax reference max only moves when a score exceeds it by more
+//    than 2^8 (p <= 256 meanwhile; O and the sum share the reference, so the
+//    result is the same); rescaling O is then a rare branch;
+//  * LDS rows are 72 chunks of 16 bytes, XOR-swizzled inside aligned groups
+//    of 8 chunks (see swz) so both operand reads run at the full LDS rate.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "lds_dma.h"
+
+namespace cpa {
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+constexpr int kH = 64;          // query heads sharing the latent
+constexpr int kDk = 576;        // QK dims (latent)
+constexpr int kDv = 512;        // PV dims (leading part of the latent)
+constexpr int kBN = 32;         // tokens per LDS tile
+constexpr int kThreads = 256;   // 4 wavefronts
+constexpr int kRowChunks = kDk / 8;               // 72 chunks of 16 B per bf16 row
+constexpr int kTileChunks = kBN * kRowChunks;     // 2304
+constexpr int kTileBytes = kTileChunks * 16;      // 36864
+constexpr int kLdChunks = kTileChunks / kThreads; // 9 chunks per thread (bf16)
+constexpr int kStages = 4;
+constexpr int kSmemBytes = kStages * kTileBytes;  // 144 KB
+constexpr int kFp8RowChunks = kDk / 16;           // 36 source chunks per fp8 row
+constexpr int kRawBytes = kBN * kDk;              // 18 KB: one 32-token FP8 tile
+constexpr int kRawWaveLoads = kRawBytes / 1024;   // 18 wave-wide 16-byte loads per tile
+constexpr int kPRowBytes = 64;                    // one head's 32 bf16 probabilities
+constexpr int kQSteps = kDk / 32;                 // 18 QK k-steps
+constexpr int kMv = kDv / 4 / 16;                 // 8 PV m-tiles per wave (128 dims)
+constexpr float kLn2 = 0.69314718055994531f;
+
+static_assert(kTileChunks % kThreads == 0, "tile must split evenly over the threads");
+static_assert(kRawWaveLoads * 1024 == kRawBytes && kDk % 16 == 0, "raw FP8 tile layout");
+
+// LDS the kernels declare and hand to the core.
+struct Lds {
+  char* tiles;     // kSmemBytes: bf16 stages, or FP8 raw stages + 2 bf16 tiles
+  char* p;         // [64 heads][64 B] probabilities of the current tile
+  float* alpha;    // [64] rescale factor of each head for the current tile
+  float* lsum;     // [64] final softmax sum of each head
+  float* rscale;   // FP8: [4 raw stages][4 wave copies][64 tokens]
+  float* bscale;   // FP8: [2 bf16 tiles][32 tokens]
+};
+
+// Physical 16-byte chunk of logical chunk `c` in LDS row `r` (XOR inside the
+// aligned group of 8 chunks). gfx950 LDS has 64 four-byte banks (256 B per
+// clock); a row is 1152 B, so rows alternate between the two 128-byte bank
+// halves and the XOR must separate the rows one read pass touches. With
+// f(r) = bits (b0, b2, b1) of r both operand reads run at the full LDS rate:
+// the 16-byte K reads (16 rows x 4 chunks) and the 8-byte transposing V
+// reads (4 rows x 2 chunks per 16 lanes); the previous f(r) = (r ^ r>>3) & 7
+// halved the K read rate (measured with a microbenchmark of these patterns).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 1) | ((r & 2) << 1) | ((r & 4) >> 1)); }
+
+// Byte offset of head h's 16-byte P chunk g (k-elements 8g..8g+7) in the P
+// buffer; the chunk XOR keeps both the stores and the operand loads free of
+// bank conflicts.
+__device__ __forceinline__ int p_off(int h, int g) { return h * kPRowBytes + 16 * (g ^ ((h >> 1) & 3)); }
+
+__device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(__attribute__((address_space(3))) char*)(p));
+}
+
+// Operand vectors are assembled only from whole registers: packed pairs and
+// whole-vector bit casts. (Building a bf16 vector one element at a time is
+// lowered incorrectly by the gfx950 code generator of this toolchain: it
+// duplicates or misaligns elements.)
+__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// bf16 (round to nearest even) of a pair, as one 32-bit word: a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2v));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+  return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
+                                                 pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])));
+}
+
+// Maximum / sum over the four lanes l, l^16, l^32, l^48 (one head's four
+// score groups), with the gfx950 row-swap permutes instead of LDS round trips.
+__device__ __forceinline__ float max4_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum4_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Per-lane LDS byte offsets inside a tile. Every operand read of a tile is
+// one of these bases plus a compile-time constant, so the reads use the LDS
+// instruction's immediate offset instead of one address register each.
+struct LdsBases {
+  int qk[2][2];  // [token block mt][k-step parity]: row 16mt + c, chunk (4(s&1) + g) ^ f
+  int pv[2][4];  // [row r0 / r1][m & 3]: rows 4g + c/4 (+16), chunk of dims 128w + 16m + 4(c&3)
+};
+
+__device__ __forceinline__ LdsBases lds_bases(int w, int g, int c) {
+  LdsBases L;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int row = 16 * mt + c;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) L.qk[mt][par] = row * (kRowChunks * 16) + swz(row, 4 * par + g) * 16;
+  }
+  const int r0 = 4 * g + (c >> 2);
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int row = r0 + 16 * rr;
+#pragma unroll
+    for (int m4 = 0; m4 < 4; ++m4)
+      L.pv[rr][m4] = row * (kRowChunks * 16) + 256 * w + swz(row, 2 * m4 + ((c & 3) >> 1)) * 16 + 8 * (c & 1);
+  }
+  return L;
+}
+
+struct State {
+  f32x4 oacc[kMv][4];  // PV role: O^T dims 128w + 16m + 4g + i, head 16 hb + c
+  float m_run;         // QK role: running reference max of head 16w + c (log2 domain)
+  float l_run;         // QK role: this lane's share of that head's running sum
+};
+
+__device__ __forceinline__ void init_state(State& st) {
+#pragma unroll
+  for (int m = 0; m < kMv; ++m)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      st.oacc[m][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+a"(st.oacc[m][hb]));
+    }
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+}
+
+// Q^T operand of the QK role: lane (g, c) holds q[16w + c][32s + 8g .. +8]
+// for k-step s. (Opaque after loading: otherwise the compiler re-loads these
+// read-only values from memory inside the tile loop instead of keeping them.)
+__device__ __forceinline__ void load_q(const uint16_t* qhead, int g, bf16x8 (&qreg)[kQSteps]) {
+  const uint16_t* qp = qhead + 8 * g;
+#pragma unroll
+  for (int s = 0; s < kQSteps; ++s) {
+    qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+    asm volatile("" : "+v"(qreg[s]));
+  }
+}
+
+// One 32-token tile: scores, online softmax update, P exchange, PV
+// accumulation. `nvalid` leading tokens of the tile are real. hook(s) runs
+// at the start of QK k-step s (the caller issues later tiles' loads there).
+// Contains one workgroup barrier (P visible to all waves); the caller's
+// barrier before the next tile orders the next P writes after these reads.
+template <bool kFp8, typename Hook>
+__device__ __forceinline__ void consume_tile(const char* tile, const float* scales, int nvalid, int w, int g, int c,
+                                             const LdsBases& L, const bf16x8 (&qreg)[kQSteps], float scale_log2,
+                                             State& st, const Lds& S, Hook&& hook) {
+  constexpr int kAhead = 4;   // K operands read ahead (k-steps)
+  constexpr int kAheadV = 4;  // V operands read ahead (m-tiles); the first ones load during QK
+  bf16x8 va[kMv];
+  auto load_v = [&](int m) {
+    va[m] = join_tr(lds_read_tr(tile + L.pv[0][m & 3] + 128 * (m >> 2)),
+                    lds_read_tr(tile + L.pv[1][m & 3] + 128 * (m >> 2)));
+  };
+  // ---- S^T = K Q^T: two 16-token blocks, chains interleaved ----
+  // K operands are read kAhead k-steps ahead of their MFMAs; a scheduling
+  // barrier closes every step so the reads cannot sink next to their use and
+  // LDS latency overlaps MFMA work.
+  f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  bf16x8 ka[kQSteps][2];
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      ka[s][mt] = *reinterpret_cast<const bf16x8*>(tile + L.qk[mt][s & 1] + 128 * (s >> 1));
+#pragma unroll
+  for (int s = 0; s < kQSteps; ++s) {
+    hook(s);
+    if (s + kAhead < kQSteps) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        ka[s + kAhead][mt] =
+            *reinterpret_cast<const bf16x8*>(tile + L.qk[mt][(s + kAhead) & 1] + 128 * ((s + kAhead) >> 1));
+    }
+    if (s >= kQSteps - kAheadV) load_v(s - (kQSteps - kAheadV));
+    sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s][0], qreg[s], sacc[0], 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s][1], qreg[s], sacc[1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // ---- online softmax of head 16w + c (log2 domain) ----
+  float x[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * mt + 4 * g + i;
+      float v = sacc[mt][i] * scale_log2;
+      if constexpr (kFp8) v *= scales[t];
+      v = (t < nvalid) ? v : -INFINITY;
+      x[4 * mt + i] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = max4_rows(mx);
+  float alpha = 1.f;
+  if (__any(mx > st.m_run + 8.f)) {  // rare: move the reference (always on the first tile)
+    const float m_new = fmaxf(st.m_run, mx);
+    alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);  // 0 on the first tile
+    st.m_run = m_new;
+    st.l_run *= alpha;
+  }
+  float psum = 0.f;
+  float pf[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = __builtin_amdgcn_exp2f(x[j] - st.m_run);
+    psum += p;
+    float pv = p;
+    if constexpr (kFp8) pv *= scales[16 * (j >> 2) + 4 * g + (j & 3)];
+    pf[j] = pv;
+  }
+  st.l_run += psum;
+  // P^T chunk of this lane: head 16w + c, k-elements 8g..8g+7 in score order
+  *reinterpret_cast<bf16x8*>(S.p + p_off(16 * w + c, g)) = pack8(pf);
+  if (g == 0) S.alpha[16 * w + c] = alpha;
+  __syncthreads();  // P and the rescale factors of all 64 heads visible
+
+  // ---- PV: O^T [dims 128w..+128][64 heads] += V^T P^T ----
+  float al[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) al[hb] = S.alpha[16 * hb + c];
+  if (__any(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
+#pragma unroll
+    for (int m = 0; m < kMv; ++m)
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        // (the opaque steps keep the AGPR -> VGPR copies inside this rare
+        // branch; otherwise they are hoisted into every tile)
+        asm volatile("" : "+a"(st.oacc[m][hb]));
+        st.oacc[m][hb] *= al[hb];
+        asm volatile("" : "+a"(st.oacc[m][hb]));
+      }
+  }
+  bf16x8 pb[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) pb[hb] = *reinterpret_cast<const bf16x8*>(S.p + p_off(16 * hb + c, g));
+#pragma unroll
+  for (int m = 0; m < kMv; ++m) {
+    if (m + kAheadV < kMv) load_v(m + kAheadV);
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      st.oacc[m][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb[hb], st.oacc[m][hb], 0, 0, 0);
+      // keep the accumulator in AGPRs across the tile loop
+      asm volatile("" : "+a"(st.oacc[m][hb]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  // at most `ahead` further tiles of N loads each may still be in flight
+  if (ahead >= 3) cpa::wait_vmcnt<3 * N>();
+  else if (ahead == 2) cpa::wait_vmcnt<2 * N>();
+  else if (ahead == 1) cpa::wait_vmcnt<N>();
+  else cpa::wait_vmcnt<0>();
+}
+
+// Tokens [t0, t1) of a bf16 latent cache (`base` = token 0, `c_t` elements
+// per token) through the core. Stage i % 4 holds tile i; tokens past t1 in
+// the last tile re-read token t1 - 1 and are masked.
+template <Policy P>
+__device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int64_t t0, int64_t t1, int w, int g,
+                                         int c, const LdsBases& L, const bf16x8 (&qreg)[kQSteps], float scale_log2,
+                                         State& st, const Lds& S) {
+  const int tid = threadIdx.x;
+  const int ntok = (int)(t1 - t0);
+  const int ntiles = (ntok + kBN - 1) / kBN;
+  uint32_t toff[kLdChunks];  // byte offset of this thread's chunks inside a full tile
+#pragma unroll
+  for (int k = 0; k < kLdChunks; ++k) {
+    const int Pc = tid + kThreads * k;
+    const int row = Pc / kRowChunks, pc = Pc % kRowChunks;
+    toff[k] = (uint32_t)((row * c_t + swz(row, pc) * 8) * 2);
+  }
+  auto stage = [&](int i) { return S.tiles + (i & 3) * kTileBytes + 64 * w * 16; };
+  auto issue = [&](int i) {
+    const int64_t tok0 = t0 + (int64_t)i * kBN;
+    char* dst0 = stage(i);
+    if (tok0 + kBN <= t1) {
+      const uint16_t* tb = base + tok0 * c_t;
+#pragma unroll
+      for (int k = 0; k < kLdChunks; ++k) lds_dma16_sbase<P>(tb, toff[k], lds_addr(dst0 + kThreads * k * 16));
+    } else {
+#pragma unroll
+      for (int k = 0; k < kLdChunks; ++k) {
+        const int Pc = tid + kThreads * k;
+        const int row = Pc / kRowChunks, pc = Pc % kRowChunks;
+        const int64_t tok = min(tok0 + row, t1 - 1);
+        lds_dma16<P>(base + tok * c_t + swz(row, pc) * 8, lds_addr(dst0 + kThreads * k * 16));
+      }
+    }
+  };
+  for (int i = 0; i < 3 && i < ntiles; ++i) issue(i);
+  for (int i = 0; i < ntiles; ++i) {
+    wait_ahead<kLdChunks>(min(2, ntiles - 1 - i));  // tile i landed
+    __syncthreads();  // tile i visible to all; every wave is done with tile i-1 and its P
+    // tile i+3 goes into the stage tile i-1 used: a full tile's loads are
+    // spread over the QK steps of tile i (one every other step), the
+    // clamped last tile is issued at once
+    const int64_t nxt0 = t0 + (int64_t)(i + 3) * kBN;
+    const bool spread = (i + 3 < ntiles) && (nxt0 + kBN <= t1);
+    if (i + 3 < ntiles && !spread) issue(i + 3);
+    const uint16_t* ntb = base + nxt0 * c_t;
+    char* ndst = stage(i + 3);
+    consume_tile<false>(S.tiles + (i & 3) * kTileBytes, nullptr, min(kBN, ntok - kBN * i), w, g, c, L, qreg,
+                        scale_log2, st, S, [&](int s) {
+                          if (spread && (s & 1) == 0 && (s >> 1) < kLdChunks)
+                            lds_dma16_sbase<P>(ntb, toff[s >> 1], lds_addr(ndst + kThreads * (s >> 1) * 16));
+                        });
+  }
+}
+
+// FP8 -> bf16 of one raw 32-token tile into a bf16 tile (swizzled layout),
+// each byte converted once per workgroup; the tile's scales travel with it.
+__device__ __forceinline__ void convert_tile(const char* raw, const float* sc_in, char* tile, float* sc_out) {
+  const int tid = threadIdx.x;
+  for (int Sx = tid; Sx < kBN * kFp8RowChunks; Sx += kThreads) {
+    const int row = Sx / kFp8RowChunks, sc16 = Sx % kFp8RowChunks;
+    const uint4 r = *reinterpret_cast<const uint4*>(raw + row * kDk + sc16 * 16);
+    const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[q], 1.0f, false));
+      o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[q], 1.0f, true));
+    }
+    char* rowp = tile + row * (kRowChunks * 16);
+    *reinterpret_cast<uint4*>(rowp + swz(row, 2 * sc16) * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(rowp + swz(row, 2 * sc16 + 1) * 16) = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+  if (tid < kBN) sc_out[tid] = sc_in[tid];
+}
+
+// Tokens [t0, t1) of an FP8 E4M3 latent cache with per-token scales.
+// Raw stage u % 4 holds the e4m3 bytes of tile u, bf16 tile u % 2 its
+// conversion; the per-token scale multiplies the score (s = scale_t q.e_t)
+// and P (p_t * scale_t multiplies e_t in PV), never K itself.
+__device__ __forceinline__ void run_fp8(const uint8_t* base, int64_t c_t, const float* sbase, int64_t s_t, int64_t t0,
+                                        int64_t t1, int w, int g, int c, const LdsBases& L,
+                                        const bf16x8 (&qreg)[kQSteps], float scale_log2, State& st, const Lds& S) {
+  const int lane = threadIdx.x & 63;
+  const int ntok = (int)(t1 - t0);
+  const int ntiles = (ntok + kBN - 1) / kBN;
+  char* raw = S.tiles;                     // 4 x 18 KB
+  char* btile = S.tiles + 4 * kRawBytes;   // 2 x 36 KB
+  // wave w issues the tile's wave-loads w, w+4, ... (5 for waves 0-1, 4 for 2-3)
+  // plus one load of the tile's scales: per-wave counts for the waits
+  const int n_mine = (kRawWaveLoads - w + 3) / 4;
+  uint32_t roff[5];  // byte offset of this lane's 16-byte pieces inside a full raw tile
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int Bx = (w + 4 * k) * 1024 + 16 * lane;  // LDS byte of the piece, row-major [32][576]
+    roff[k] = (uint32_t)((Bx / kDk) * c_t + (Bx % kDk));
+  }
+  auto issue = [&](int u) {
+    const int64_t tok0 = t0 + (int64_t)u * kBN;
+    char* dst = raw + (u & 3) * kRawBytes;
+    if (tok0 + kBN <= t1) {
+      const uint8_t* tb = base + tok0 * c_t;
+#pragma unroll
+      for (int k = 0; k < 5; ++k)
+        if (k < n_mine) lds_dma16_sbase<Policy::kStream>(tb, roff[k], lds_addr(dst + (w + 4 * k) * 1024));
+    } else {  // last tile: past the range, re-read its last token (masked)
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        if (k < n_mine) {
+          const int Bx = (w + 4 * k) * 1024 + 16 * lane;
+          const int64_t tok = min(tok0 + Bx / kDk, t1 - 1);
+          lds_dma16<Policy::kStream>(base + tok * c_t + (Bx % kDk), lds_addr(dst + (w + 4 * k) * 1024));
+        }
+      }
+    }
+    const int64_t tok = min(tok0 + lane, t1 - 1);
+    lds_dma4<Policy::kStream>(sbase + tok * s_t, lds_addr(&S.rscale[((u & 3) * 4 + w) * 64]));
+  };
+  auto wait_raw = [&](int ahead) {
+    if (w < 2) wait_ahead<6>(ahead);  // 5 cache loads + 1 scale load per tile
+    else wait_ahead<5>(ahead);
+  };
+  for (int u = 0; u < 4 && u < ntiles; ++u) issue(u);
+  if (ntiles > 0) {
+    wait_raw(min(3, ntiles - 1));  // raw 0 landed
+    __syncthreads();
+    convert_tile(raw, &S.rscale[0], btile, &S.bscale[0]);
+  }
+  for (int u = 0; u < ntiles; ++u) {
+    if (u + 1 < ntiles) wait_raw(min(u + 3, ntiles - 1) - (u + 1));  // raw u+1 landed
+    __syncthreads();  // bf16 tile u complete; raw u+1 visible; tile u-1, its P and raw u fully consumed
+    if (u + 4 < ntiles) issue(u + 4);  // into the raw stage of tile u
+    if (u + 1 < ntiles)
+      convert_tile(raw + ((u + 1) & 3) * kRawBytes, &S.rscale[((u + 1) & 3) * 256], btile + ((u + 1) & 1) * kTileBytes,
+                   &S.bscale[((u + 1) & 1) * kBN]);
+    consume_tile<true>(btile + (u & 1) * kTileBytes, &S.bscale[(u & 1) * kBN], min(kBN, ntok - kBN * u), w, g, c, L,
+                       qreg, scale_log2, st, S, [](int) {});
+  }
+}
+
+// Closes the range: the softmax sum of every head into S.lsum (one barrier).
+// Returns this lane's QK-role head total (head 16w + c).
+__device__ __forceinline__ float finish(const State& st, int w, int g, int c, const Lds& S) {
+  const float l = sum4_rows(st.l_run);
+  if (g == 0) S.lsum[16 * w + c] = l;
+  __syncthreads();
+  return l;
+}
+
+}  // namespace mla
+}  // namespace cpa
