@@ -63,7 +63,7 @@ def _src_digest(files):
 
 KERNEL_SOURCES = {
     "prefill_gqa_kernel": ("prefill.hip", "lds_dma.h"),
-    "decode_mla_kernel<bf16>": ("decode_mla.hip", "lds_dma.h"),
+    "decode_mla_kernel<bf16>": ("decode_mla.hip", "mla_core.h", "lds_dma.h"),
 }
 
 

@@ -178,15 +178,17 @@ __device__ __forceinline__ void init_state(State& st) {
 }
 
 // Q^T operand of the QK role: lane (g, c) holds q[16w + c][32s + 8g .. +8]
-// for k-step s. (Opaque after loading: otherwise the compiler re-loads these
-// read-only values from memory inside the tile loop instead of keeping them.)
+// for k-step s. All loads are issued before the first wait, so their
+// latencies overlap. The registers are then made opaque: otherwise the
+// compiler re-loads these read-only values inside the tile loop, or defers
+// the wait for them into the loop, where (not knowing the tile loads issued
+// from inline assembly) its vmcnt count would also wait for those.
 __device__ __forceinline__ void load_q(const uint16_t* qhead, int g, bf16x8 (&qreg)[kQSteps]) {
   const uint16_t* qp = qhead + 8 * g;
 #pragma unroll
-  for (int s = 0; s < kQSteps; ++s) {
-    qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
-    asm volatile("" : "+v"(qreg[s]));
-  }
+  for (int s = 0; s < kQSteps; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+#pragma unroll
+  for (int s = 0; s < kQSteps; ++s) asm volatile("" : "+v"(qreg[s]));
 }
 
 // One 32-token tile: scores, online softmax update, P exchange, PV

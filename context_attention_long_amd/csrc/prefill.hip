@@ -164,11 +164,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_gqa_kernel(Args a) {
   const int n_tiles = wg_last_pos / kBN + 1;
 
   // ---- Q^T operand: row r, dims 16s + 8g .. +8 ----
+  // (made opaque once loaded, so the wait for these loads happens here:
+  // deferred into the tile loop, the compiler's vmcnt count -- blind to the
+  // tile loads issued from inline assembly -- would also wait for those)
   bf16x8 qreg[kD / 16];
   {
     const uint16_t* qp = a.q + q_row * a.q_n + (int64_t)head * a.q_h + 8 * g;
 #pragma unroll
     for (int s = 0; s < kD / 16; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+#pragma unroll
+    for (int s = 0; s < kD / 16; ++s) asm volatile("" : "+v"(qreg[s]));
   }
 
   // ---- K/V tile loader: direct global -> LDS, 16 bytes per lane ----
