@@ -17,6 +17,11 @@ once, plus queries, partial outputs/LSEs and the merge).
 Also reported: the dominant kernel's roofline (live HIP-event timing on the
 launch stream) and the float64 CPU oracle timed on a bounded sample of the
 same workload on this host. All inputs are seeded and synthetic.
+
+Warmup: at least --warmup untimed steps per workload, continued until
+--warmup-ms of wall time have passed. The GPU's clock takes a few hundred
+milliseconds of load to reach its steady state; measured after 3 short steps
+the same kernels ran 10-15 % slower than in a sustained loop.
 """
 
 import argparse
@@ -79,11 +84,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _warm(torch, step, warmup, min_ms):
+    """At least `warmup` untimed steps, continued until `min_ms` of wall time
+    have passed: the GPU's clock needs a few hundred milliseconds of load to
+    settle, and a few short steps alone leave it below its steady state.
+    Returns the number of warmup steps run."""
+    n = 0
+    t0 = time.perf_counter()
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < min_ms:
+        step()
+        n += 1
+        if n % 4 == 0:  # keep the queue short, so elapsed wall time tracks GPU work
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def _events(torch, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
 
-def bench_prefill(cpa, torch, synth, steps, warmup):
+def bench_prefill(cpa, torch, synth, steps, warmup, warmup_ms):
     c = synth.config(2)
     plan = cpa.cp_plan_zigzag(c["C"], c["rank"], c["new_len"], c["prefix_len"])
     T = sum(c["new_len"])
@@ -105,9 +126,7 @@ def bench_prefill(cpa, torch, synth, steps, warmup):
         if ev is not None:
             ev[1].record()
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    nwarm = _warm(torch, step, warmup, warmup_ms)
     evs = _events(torch, steps)
     t0 = time.perf_counter()
     for i in range(steps):
@@ -115,11 +134,11 @@ def bench_prefill(cpa, torch, synth, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kms = [a.elapsed_time(b) for a, b in evs]
-    return dict(cfg=c, plan=plan, flops=flops, pairs=pairs, wall=wall, kernel_ms=kms,
+    return dict(cfg=c, plan=plan, flops=flops, pairs=pairs, wall=wall, kernel_ms=kms, warmup_steps=nwarm,
                 inputs=(q, k, v))
 
 
-def bench_prefill_config(cpa, torch, synth, k, steps, warmup):
+def bench_prefill_config(cpa, torch, synth, k, steps, warmup, warmup_ms):
     """One more prefill shard workload (config 4: MLA zigzag with a cached
     prefix; config 5: interleave over the ragged agentic batch), timed per
     launch with HIP events: algorithmic TFLOP/s."""
@@ -137,9 +156,8 @@ def bench_prefill_config(cpa, torch, synth, k, steps, warmup):
     # causal pairs per head: each local row attends to positions 0..pos (prefix included)
     pairs = int(np.sum(plan.pos_id.astype(np.int64) + 1))
     flops = pairs * c["Hq"] * 2 * (c["Dqk"] + c["Dv"])
-    for _ in range(warmup):
-        cpa.attn_prefill_shard(q, kk, v, plan.segments, c["scale"], out=out, lse=lse)
-    torch.cuda.synchronize()
+    _warm(torch, lambda: cpa.attn_prefill_shard(q, kk, v, plan.segments, c["scale"], out=out, lse=lse),
+          warmup, warmup_ms)
     evs = _events(torch, steps)
     for i in range(steps):
         evs[i][0].record()
@@ -154,7 +172,7 @@ def bench_prefill_config(cpa, torch, synth, k, steps, warmup):
             "kernel_ms": round(kms, 3), "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
-def bench_decode(cpa, torch, synth, steps, warmup):
+def bench_decode(cpa, torch, synth, steps, warmup, warmup_ms):
     c = synth.config(3)
     B, L, C, H = c["B"], c["L"], c["C"], c["Hq"]
     dev = torch.device("cuda:0")
@@ -189,9 +207,7 @@ def bench_decode(cpa, torch, synth, steps, warmup):
                     ev[i][1].record()
             cpa.attn_merge_states(po, pl, out=mo, lse_out=ml)
 
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
+        _warm(torch, step, warmup, warmup_ms)
         evs = [_events(torch, C) for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
@@ -253,8 +269,10 @@ def cpu_baseline(synth, prefill, seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--warmup-ms", type=float, default=300.0,
+                    help="keep warming up (untimed) until this much wall time has passed")
     ap.add_argument("--no-decode", action="store_true", help="skip the secondary MLA decode figures")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -290,12 +308,12 @@ def main():
         torch.cuda.empty_cache()
 
     if args.decode_only:
-        dec = bench_decode(cpa, torch, synth, args.steps, args.warmup)
+        dec = bench_decode(cpa, torch, synth, args.steps, args.warmup, args.warmup_ms)
         print(json.dumps({"decode": dec}), flush=True)
         return
 
     log("[bench] zigzag prefill shard ...")
-    pre = bench_prefill(cpa, torch, synth, args.steps, args.warmup)
+    pre = bench_prefill(cpa, torch, synth, args.steps, args.warmup, args.warmup_ms)
     ms = pre["wall"] / args.steps * 1e3
     value = pre["flops"] / (ms * 1e-3) / 1e12
     kms = float(np.mean(pre["kernel_ms"]))
@@ -308,7 +326,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": pre["warmup_steps"],
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -338,7 +356,7 @@ def main():
 
     if not args.no_decode:
         log("[bench] split-KV MLA decode (8 partial launches + merge) ...")
-        dec = bench_decode(cpa, torch, synth, max(3, args.steps // 2), args.warmup)
+        dec = bench_decode(cpa, torch, synth, max(3, args.steps // 2), args.warmup, args.warmup_ms)
         line["decode"] = {
             "workload": "MLA split-KV decode: batch 64, 64 heads, 576/512 latent, 131072-token context, "
                         "C=8 contiguous shards as 8 partial launches + merge",
@@ -359,7 +377,7 @@ def main():
     if not args.no_extra_prefill:
         for k, key in ((4, "prefill_mla_zigzag"), (5, "prefill_interleave")):
             log(f"[bench] {key} (config {k}) ...")
-            line[key] = bench_prefill_config(cpa, torch, synth, k, max(2, args.steps // 10), 1)
+            line[key] = bench_prefill_config(cpa, torch, synth, k, max(2, args.steps // 10), 1, args.warmup_ms)
             log(f"[bench] {key}: {line[key]['kernel_ms']} ms, {line[key]['tflops']} TFLOP/s")
 
     if not args.no_cpu_baseline:
