@@ -23,8 +23,8 @@ using namespace cpa::mla;
 template <bool kFp8>
 __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  __shared__ __attribute__((aligned(16))) char plds[kH * kPRowBytes];
-  __shared__ float alpha_s[kH], lsum_s[kH];
+  __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
+  __shared__ float alpha_s[2 * kH], lsum_s[kH];
   __shared__ float rscale[4 * 4 * 64];  // FP8: [raw stage][wave copy][token]
   __shared__ float bscale[2 * kBN];     // FP8: scales of the two bf16 tiles
   const Lds S{smem, plds, alpha_s, lsum_s, rscale, bscale};

@@ -71,8 +71,8 @@ static_assert(kRawWaveLoads * 1024 == kRawBytes && kDk % 16 == 0, "raw FP8 tile 
 // LDS the kernels declare and hand to the core.
 struct Lds {
   char* tiles;     // kSmemBytes: bf16 stages, or FP8 raw stages + 2 bf16 tiles
-  char* p;         // [64 heads][64 B] probabilities of the current tile
-  float* alpha;    // [64] rescale factor of each head for the current tile
+  char* p;         // [2 buffers][64 heads][64 B] probabilities of a tile
+  float* alpha;    // [2 buffers][64] rescale factor of each head for a tile
   float* lsum;     // [64] final softmax sum of each head
   float* rscale;   // FP8: [4 raw stages][4 wave copies][64 tokens]
   float* bscale;   // FP8: [2 bf16 tiles][32 tokens]
@@ -314,6 +314,171 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
 // Tokens [t0, t1) of a bf16 latent cache (`base` = token 0, `c_t` elements
 // per token) through the core. Stage i % 4 holds tile i; tokens past t1 in
 // the last tile re-read token t1 - 1 and are masked.
+// ---- bf16 pipeline: one barrier per tile ----
+// Step i, after the barrier that publishes P_i (and tile i+1):
+//   S_{i+1} = K_{i+1} Q^T                      (QK role, MFMA)
+//   O += V_i^T P_i, rescaled by alpha_i first   (PV role, MFMA)
+//   softmax(S_{i+1}) -> P_{i+1}, alpha_{i+1}    (VALU, placed between the PV
+//                                                MFMAs so it runs in their shadow)
+// P and alpha are double buffered (P_{i+1} goes to the buffer P_{i-1} used,
+// which every wave finished reading before the barrier), so one barrier per
+// tile orders everything: the tile stages, the P exchange and the reuse.
+
+// QK of one tile into sacc; hook(s) runs at k-step s; vpre(m) at the last
+// kAheadV steps issues the first V operand reads of the tile PV works on.
+template <typename Hook, typename VPre>
+__device__ __forceinline__ void qk_tile(const char* tile, const LdsBases& L, const bf16x8 (&qreg)[kQSteps],
+                                        f32x4 (&sacc)[2], Hook&& hook, VPre&& vpre) {
+  constexpr int kAhead = 4;
+  constexpr int kAheadV = 4;
+  sacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 ka[kQSteps][2];
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      ka[s][mt] = *reinterpret_cast<const bf16x8*>(tile + L.qk[mt][s & 1] + 128 * (s >> 1));
+#pragma unroll
+  for (int s = 0; s < kQSteps; ++s) {
+    hook(s);
+    if (s + kAhead < kQSteps) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        ka[s + kAhead][mt] =
+            *reinterpret_cast<const bf16x8*>(tile + L.qk[mt][(s + kAhead) & 1] + 128 * ((s + kAhead) >> 1));
+    }
+    if (s >= kQSteps - kAheadV) vpre(s - (kQSteps - kAheadV));
+    sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s][0], qreg[s], sacc[0], 0, 0, 0);
+    sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s][1], qreg[s], sacc[1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Online softmax of the QK-role head 16w + c over one tile, in pieces so the
+// pieces can sit between the MFMAs of the PV step. Branch free: a lane moves
+// its reference max only when a score exceeds it by more than 2^8 (always
+// on the first tile); alpha is the factor the head's O and sum take.
+struct Soft {
+  float x[8];
+  float mx, alpha, psum;
+  float pf[8];
+};
+
+__device__ __forceinline__ void soft_scores(Soft& sm, const f32x4 (&sacc)[2], int nvalid, int g, float scale_log2) {
+  sm.mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * mt + 4 * g + i;
+      const float v = (t < nvalid) ? sacc[mt][i] * scale_log2 : -INFINITY;
+      sm.x[4 * mt + i] = v;
+      sm.mx = fmaxf(sm.mx, v);
+    }
+}
+
+__device__ __forceinline__ void soft_ref(Soft& sm, State& st) {
+  const float mx = max4_rows(sm.mx);
+  const bool move = mx > st.m_run + 8.f;
+  const float m_new = move ? mx : st.m_run;
+  sm.alpha = move ? __builtin_amdgcn_exp2f(st.m_run - m_new) : 1.f;  // 0 on the first tile
+  st.m_run = m_new;
+  st.l_run *= sm.alpha;
+  sm.psum = 0.f;
+}
+
+template <int J0>
+__device__ __forceinline__ void soft_exp(Soft& sm, const State& st) {
+#pragma unroll
+  for (int j = J0; j < J0 + 4; ++j) {
+    const float p = __builtin_amdgcn_exp2f(sm.x[j] - st.m_run);
+    sm.psum += p;
+    sm.pf[j] = p;
+  }
+}
+
+__device__ __forceinline__ void soft_store(Soft& sm, State& st, char* pbuf, float* abuf, int w, int g, int c) {
+  st.l_run += sm.psum;
+  // P^T chunk of this lane: head 16w + c, k-elements 8g..8g+7 in score order
+  *reinterpret_cast<bf16x8*>(pbuf + p_off(16 * w + c, g)) = pack8(sm.pf);
+  if (g == 0) abuf[16 * w + c] = sm.alpha;
+}
+
+// Interleave `n` MFMAs of the current scheduling region with the VALU work
+// placed in it (1 MFMA, then up to `v` VALU instructions).
+template <int N, int V>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+  }
+}
+
+// One pipeline step (see above). kNext: tile nxt exists (QK + softmax of it).
+template <bool kNext, typename Hook>
+__device__ __forceinline__ void pipe_step(const char* cur, const char* nxt, int nvalid_nxt, int buf, int w, int g,
+                                          int c, const LdsBases& L, const bf16x8 (&qreg)[kQSteps], float scale_log2,
+                                          State& st, const Lds& S, Hook&& hook) {
+  constexpr int kAheadV = 4;
+  bf16x8 va[kMv];
+  auto load_v = [&](int m) {
+    va[m] = join_tr(lds_read_tr(cur + L.pv[0][m & 3] + 128 * (m >> 2)),
+                    lds_read_tr(cur + L.pv[1][m & 3] + 128 * (m >> 2)));
+  };
+  f32x4 sacc[2];
+  if constexpr (kNext) {
+    qk_tile(nxt, L, qreg, sacc, hook, load_v);
+  } else {
+#pragma unroll
+    for (int m = 0; m < kAheadV; ++m) load_v(m);
+  }
+  // ---- alpha_i: rescale O (rare) ----
+  const float* acur = S.alpha + kH * buf;
+  float al[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) al[hb] = acur[16 * hb + c];
+  if (__any(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
+#pragma unroll
+    for (int m = 0; m < kMv; ++m)
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        asm volatile("" : "+a"(st.oacc[m][hb]));
+        st.oacc[m][hb] *= al[hb];
+        asm volatile("" : "+a"(st.oacc[m][hb]));
+      }
+  }
+  const char* pcur = S.p + kH * kPRowBytes * buf;
+  bf16x8 pb[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) pb[hb] = *reinterpret_cast<const bf16x8*>(pcur + p_off(16 * hb + c, g));
+  // ---- PV_i with softmax_{i+1} in the MFMA shadows ----
+  Soft sm;
+#pragma unroll
+  for (int m = 0; m < kMv; ++m) {
+    if (m + kAheadV < kMv) load_v(m + kAheadV);
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      st.oacc[m][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb[hb], st.oacc[m][hb], 0, 0, 0);
+      asm volatile("" : "+a"(st.oacc[m][hb]));
+    }
+    if constexpr (kNext) {
+      if (m == 0) soft_scores(sm, sacc, nvalid_nxt, g, scale_log2);
+      if (m == 1) soft_ref(sm, st);
+      if (m == 2) soft_exp<0>(sm, st);
+      if (m == 3) soft_exp<4>(sm, st);
+      if (m == 4) soft_store(sm, st, S.p + kH * kPRowBytes * (buf ^ 1), S.alpha + kH * (buf ^ 1), w, g, c);
+      if (m <= 4) interleave_mfma_valu<4, 6>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Tokens [t0, t1) of a bf16 latent cache (`base` = token 0, `c_t` elements
+// per token) through the core. Stage i % 4 holds tile i; tokens past t1 in
+// the last tile re-read token t1 - 1 and are masked. Needs S.p and S.alpha
+// with room for two buffers.
 template <Policy P>
 __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int64_t t0, int64_t t1, int w, int g,
                                          int c, const LdsBases& L, const bf16x8 (&qreg)[kQSteps], float scale_log2,
@@ -321,6 +486,7 @@ __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int6
   const int tid = threadIdx.x;
   const int ntok = (int)(t1 - t0);
   const int ntiles = (ntok + kBN - 1) / kBN;
+  if (ntiles <= 0) return;
   uint32_t toff[kLdChunks];  // byte offset of this thread's chunks inside a full tile
 #pragma unroll
   for (int k = 0; k < kLdChunks; ++k) {
@@ -328,6 +494,7 @@ __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int6
     const int row = Pc / kRowChunks, pc = Pc % kRowChunks;
     toff[k] = (uint32_t)((row * c_t + swz(row, pc) * 8) * 2);
   }
+  auto tile_ptr = [&](int i) -> const char* { return S.tiles + (i & 3) * kTileBytes; };
   auto stage = [&](int i) { return S.tiles + (i & 3) * kTileBytes + 64 * w * 16; };
   auto issue = [&](int i) {
     const int64_t tok0 = t0 + (int64_t)i * kBN;
@@ -346,24 +513,42 @@ __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int6
       }
     }
   };
+  auto nvalid = [&](int i) { return min(kBN, ntok - kBN * i); };
   for (int i = 0; i < 3 && i < ntiles; ++i) issue(i);
-  for (int i = 0; i < ntiles; ++i) {
-    wait_ahead<kLdChunks>(min(2, ntiles - 1 - i));  // tile i landed
-    __syncthreads();  // tile i visible to all; every wave is done with tile i-1 and its P
+  // ---- prologue: S_0 and P_0 ----
+  wait_ahead<kLdChunks>(min(2, ntiles - 1));  // tile 0 landed
+  __syncthreads();
+  {
+    f32x4 sacc[2];
+    qk_tile(tile_ptr(0), L, qreg, sacc, [](int) {}, [](int) {});
+    Soft sm;
+    soft_scores(sm, sacc, nvalid(0), g, scale_log2);
+    soft_ref(sm, st);
+    soft_exp<0>(sm, st);
+    soft_exp<4>(sm, st);
+    soft_store(sm, st, S.p, S.alpha, w, g, c);
+  }
+  // ---- steady state ----
+  for (int i = 0; i + 1 < ntiles; ++i) {
+    wait_ahead<kLdChunks>(min(1, ntiles - 2 - i));  // tile i+1 landed
+    __syncthreads();  // P_i and tile i+1 visible; every wave is done with tile i-1 and P_{i-1}
     // tile i+3 goes into the stage tile i-1 used: a full tile's loads are
-    // spread over the QK steps of tile i (one every other step), the
+    // spread over the QK steps of tile i+1 (one every other step), the
     // clamped last tile is issued at once
     const int64_t nxt0 = t0 + (int64_t)(i + 3) * kBN;
     const bool spread = (i + 3 < ntiles) && (nxt0 + kBN <= t1);
     if (i + 3 < ntiles && !spread) issue(i + 3);
     const uint16_t* ntb = base + nxt0 * c_t;
     char* ndst = stage(i + 3);
-    consume_tile<false>(S.tiles + (i & 3) * kTileBytes, nullptr, min(kBN, ntok - kBN * i), w, g, c, L, qreg,
-                        scale_log2, st, S, [&](int s) {
-                          if (spread && (s & 1) == 0 && (s >> 1) < kLdChunks)
-                            lds_dma16_sbase<P>(ntb, toff[s >> 1], lds_addr(ndst + kThreads * (s >> 1) * 16));
-                        });
+    pipe_step<true>(tile_ptr(i), tile_ptr(i + 1), nvalid(i + 1), i & 1, w, g, c, L, qreg, scale_log2, st, S,
+                    [&](int s) {
+                      if (spread && (s & 1) == 0 && (s >> 1) < kLdChunks)
+                        lds_dma16_sbase<P>(ntb, toff[s >> 1], lds_addr(ndst + kThreads * (s >> 1) * 16));
+                    });
   }
+  __syncthreads();  // P of the last tile visible
+  pipe_step<false>(tile_ptr(ntiles - 1), nullptr, 0, (ntiles - 1) & 1, w, g, c, L, qreg, scale_log2, st, S,
+                   [](int) {});
 }
 
 // FP8 -> bf16 of one raw 32-token tile into a bf16 tile (swizzled layout),
