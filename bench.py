@@ -208,12 +208,24 @@ def bench_decode(cpa, torch, synth, steps, warmup, warmup_ms):
             cpa.attn_merge_states(po, pl, out=mo, lse_out=ml)
 
         _warm(torch, step, warmup, warmup_ms)
-        evs = [_events(torch, C) for _ in range(steps)]
+        # timed steps: events only at the step boundaries (an event between
+        # every pair of launches adds its own small gap to the stream)
+        sev = _events(torch, 1)[0]
         t0 = time.perf_counter()
+        sev[0].record()
         for i in range(steps):
-            step(evs[i])
+            step()
+        sev[1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        gpu_step_ms = sev[0].elapsed_time(sev[1]) / steps
+        # per-launch durations (roofline of the partial-launch kernel): a
+        # separate pass with events around every launch
+        nl = max(3, steps // 4)
+        evs = [_events(torch, C) for _ in range(nl)]
+        for i in range(nl):
+            step(evs[i])
+        torch.cuda.synchronize()
         launch_ms = [a.elapsed_time(b) for ev in evs for a, b in ev]
         kv_bytes = B * L * entry
         q_bytes = C * B * H * 576 * 2
@@ -223,6 +235,7 @@ def bench_decode(cpa, torch, synth, steps, warmup, warmup_ms):
         ms = wall / steps * 1e3
         lm = float(np.mean(launch_ms))
         res[name] = dict(ms_per_step=ms, gbs=step_bytes / (ms * 1e-3) / 1e9, algorithmic_bytes=step_bytes,
+                         gpu_ms_per_step=gpu_step_ms,
                          launch_ms=lm, launch_gbs=launch_bytes / (lm * 1e-3) / 1e9,
                          launch_bytes=launch_bytes)
     return res

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
             a.s_t, t0, t1, w, g, c, L, qreg, a.scale_log2, st, S);
   else
     run_bf16<cpa::Policy::kStream>(reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, t0, t1, w,
-                                   g, c, L, qreg, a.scale_log2, st, S);
+                                   g, c, L, qreg, a.scale_log2, st, S, blockIdx.x * 2654435761u >> 7);
 
   // ---- split result: LSE of the QK-role head, normalised O of the PV-role dims ----
   const float l = finish(st, w, g, c, S);

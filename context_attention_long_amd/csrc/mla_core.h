@@ -476,17 +476,23 @@ __device__ __forceinline__ void pipe_step(const char* cur, const char* nxt, int 
 }
 
 // Tokens [t0, t1) of a bf16 latent cache (`base` = token 0, `c_t` elements
-// per token) through the core. Stage i % 4 holds tile i; tokens past t1 in
-// the last tile re-read token t1 - 1 and are masked. Needs S.p and S.alpha
-// with room for two buffers.
+// per token) through the core. Step i consumes tile (i + rot) mod ntiles:
+// the softmax state does not depend on the order of the tiles, and a
+// workgroup-specific rotation keeps the many workgroups that stream equally
+// aligned ranges at the same rate from addressing the same HBM channels in
+// lockstep. Stage i % 4 holds step i's tile; tokens past t1 in the last tile
+// re-read token t1 - 1 and are masked. Needs S.p and S.alpha with room for
+// two buffers.
 template <Policy P>
 __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int64_t t0, int64_t t1, int w, int g,
                                          int c, const LdsBases& L, const bf16x8 (&qreg)[kQSteps], float scale_log2,
-                                         State& st, const Lds& S) {
+                                         State& st, const Lds& S, uint32_t rot_seed = 0) {
   const int tid = threadIdx.x;
   const int ntok = (int)(t1 - t0);
   const int ntiles = (ntok + kBN - 1) / kBN;
   if (ntiles <= 0) return;
+  const int rot = (int)(rot_seed % (uint32_t)ntiles);
+  auto phys = [&](int i) { const int t = i + rot; return t >= ntiles ? t - ntiles : t; };
   uint32_t toff[kLdChunks];  // byte offset of this thread's chunks inside a full tile
 #pragma unroll
   for (int k = 0; k < kLdChunks; ++k) {
@@ -497,7 +503,7 @@ __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int6
   auto tile_ptr = [&](int i) -> const char* { return S.tiles + (i & 3) * kTileBytes; };
   auto stage = [&](int i) { return S.tiles + (i & 3) * kTileBytes + 64 * w * 16; };
   auto issue = [&](int i) {
-    const int64_t tok0 = t0 + (int64_t)i * kBN;
+    const int64_t tok0 = t0 + (int64_t)phys(i) * kBN;
     char* dst0 = stage(i);
     if (tok0 + kBN <= t1) {
       const uint16_t* tb = base + tok0 * c_t;
@@ -513,7 +519,7 @@ __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int6
       }
     }
   };
-  auto nvalid = [&](int i) { return min(kBN, ntok - kBN * i); };
+  auto nvalid = [&](int i) { return min(kBN, ntok - kBN * phys(i)); };
   for (int i = 0; i < 3 && i < ntiles; ++i) issue(i);
   // ---- prologue: S_0 and P_0 ----
   wait_ahead<kLdChunks>(min(2, ntiles - 1));  // tile 0 landed
@@ -535,7 +541,7 @@ __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int6
     // tile i+3 goes into the stage tile i-1 used: a full tile's loads are
     // spread over the QK steps of tile i+1 (one every other step), the
     // clamped last tile is issued at once
-    const int64_t nxt0 = t0 + (int64_t)(i + 3) * kBN;
+    const int64_t nxt0 = t0 + (int64_t)phys(i + 3 < ntiles ? i + 3 : 0) * kBN;
     const bool spread = (i + 3 < ntiles) && (nxt0 + kBN <= t1);
     if (i + 3 < ntiles && !spread) issue(i + 3);
     const uint16_t* ntb = base + nxt0 * c_t;

@@ -192,3 +192,33 @@ def test_decode_mla_spiky_scores(cpa, fp8):
     _sync()
     ro, rl = att.decode_shard(q64, cache, beg, end, scale, dv=512, decode=dec, kv_scale=sc)
     H.check_lowp(H.host(o), H.host(l), ro, rl, "mla spiky")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_mla_workspace_reuse_ragged(cpa, fp8):
+    """One caller workspace (random bytes at first) reused by consecutive
+    calls with per-request ragged ranges: the split states and the per-call
+    arrival counters in it must never leak between calls. Request 0 is empty,
+    request 1 has a single key."""
+    import torch
+    B, L = 4, 1000
+    qb, cache, sc = _mla_inputs(B, L, fp8, 991 + fp8)
+    scale = 1.0 / math.sqrt(576)
+    qd = H.bf16_tensor(qb)
+    cd = H.u8_tensor(cache) if fp8 else H.bf16_tensor(cache)
+    sd = H.f32_tensor(sc) if fp8 else None
+    q64 = formats.bf16_bits_to_f64(qb)
+    dec = formats.e4m3_to_f64 if fp8 else formats.bf16_bits_to_f64
+    need = cpa.attn_decode_workspace_size(B, 64, 512, L)
+    ws = torch.from_numpy(np.random.default_rng(3).integers(0, 256, need, dtype=np.uint8)).to(H.dev())
+    for beg, end in (([5, 0, 10, 0], [5, 1, 700, 1000]),
+                     ([0, 3, 0, 999], [1000, 4, 1, 1000]),
+                     ([5, 0, 10, 0], [5, 1, 700, 1000])):
+        beg, end = np.array(beg, np.int32), np.array(end, np.int32)
+        o, l = cpa.attn_decode_shard(qd, cd, None, H.i32_tensor(beg), H.i32_tensor(end), L, scale,
+                                     kv_scale=sd, workspace=ws)
+        _sync()
+        ro, rl = att.decode_shard(q64, cache, beg, end, scale, dv=512, decode=dec, kv_scale=sc)
+        H.check_lowp(H.host(o), H.host(l), ro, rl, f"mla workspace reuse fp8={fp8}")
+        empty = beg == end
+        assert np.all(H.host(o)[empty] == 0) and np.all(np.isneginf(H.host(l)[empty]))
