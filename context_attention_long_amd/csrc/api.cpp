@@ -263,6 +263,8 @@ extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* k
     CPA_TRY(check_tensor(kv_scale, "decode kv_scale", 1u << CPA_F32, 2, 0));
     if (kv_scale->shape[0] != B || kv_scale->shape[1] != Lmax)
       return fail(CPA_E_INVAL, "decode: kv_scale must be f32 [B, Lmax]");
+    // the kernel addresses a 32-token tile's scales with 32-bit offsets
+    if (kv_scale->stride[1] > (int64_t)1 << 26) return fail(CPA_E_INVAL, "decode: kv_scale token stride too large");
   } else if (kv_scale != nullptr && kv_scale->data != nullptr) {
     return fail(CPA_E_INVAL, "decode: kv_scale is only for an FP8 cache");
   }

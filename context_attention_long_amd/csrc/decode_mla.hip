@@ -25,9 +25,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
   __shared__ float alpha_s[2 * kH], lsum_s[kH];
-  __shared__ float rscale[4 * 4 * 64];  // FP8: [raw stage][wave copy][token]
-  __shared__ float bscale[2 * kBN];     // FP8: scales of the two bf16 tiles
-  const Lds S{smem, plds, alpha_s, lsum_s, rscale, bscale};
+  const Lds S{smem, plds, alpha_s, lsum_s};
 
   const int split = blockIdx.x % a.nsplit;
   const int b = blockIdx.x / a.nsplit;
@@ -49,7 +47,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
 
   if constexpr (kFp8)
     run_fp8(reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, a.kv_scale + (int64_t)b * a.s_b,
-            a.s_t, t0, t1, w, g, c, L, qreg, a.scale_log2, st, S);
+            a.s_t, t0, t1, w, g, c, L, qreg, a.scale_log2, st, S, blockIdx.x * 2654435761u >> 7);
   else
     run_bf16<cpa::Policy::kStream>(reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, t0, t1, w,
                                    g, c, L, qreg, a.scale_log2, st, S, blockIdx.x * 2654435761u >> 7);

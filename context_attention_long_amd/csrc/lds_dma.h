@@ -65,6 +65,25 @@ __device__ __forceinline__ void lds_dma16_sbase(const void* sbase, uint32_t voff
                  : "memory");
 }
 
+// Same, with the base address and the LDS address already wavefront-uniform
+// values (SGPRs): no per-call readfirstlane, so a burst of loads that share
+// a base costs one SALU add per load.
+template <Policy P = Policy::kReuse>
+__device__ __forceinline__ void lds_dma16_s(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
+  if constexpr (P == Policy::kStream)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+}
+
+// Wavefront-uniform copy of a pointer (its SGPR form).
+__device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // One 4-byte load per lane into LDS at lds_base + 4 * lane.
 template <Policy P = Policy::kReuse>
 __device__ __forceinline__ void lds_dma4(const void* gsrc, uint32_t lds_base) {

@@ -35,6 +35,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "lds_dma.h"
 
 namespace cpa {
@@ -74,8 +76,6 @@ struct Lds {
   char* p;         // [2 buffers][64 heads][64 B] probabilities of a tile
   float* alpha;    // [2 buffers][64] rescale factor of each head for a tile
   float* lsum;     // [64] final softmax sum of each head
-  float* rscale;   // FP8: [4 raw stages][4 wave copies][64 tokens]
-  float* bscale;   // FP8: [2 bf16 tiles][32 tokens]
 };
 
 // Physical 16-byte chunk of logical chunk `c` in LDS row `r` (XOR inside the
@@ -191,117 +191,6 @@ __device__ __forceinline__ void load_q(const uint16_t* qhead, int g, bf16x8 (&qr
   for (int s = 0; s < kQSteps; ++s) asm volatile("" : "+v"(qreg[s]));
 }
 
-// One 32-token tile: scores, online softmax update, P exchange, PV
-// accumulation. `nvalid` leading tokens of the tile are real. hook(s) runs
-// at the start of QK k-step s (the caller issues later tiles' loads there).
-// Contains one workgroup barrier (P visible to all waves); the caller's
-// barrier before the next tile orders the next P writes after these reads.
-template <bool kFp8, typename Hook>
-__device__ __forceinline__ void consume_tile(const char* tile, const float* scales, int nvalid, int w, int g, int c,
-                                             const LdsBases& L, const bf16x8 (&qreg)[kQSteps], float scale_log2,
-                                             State& st, const Lds& S, Hook&& hook) {
-  constexpr int kAhead = 4;   // K operands read ahead (k-steps)
-  constexpr int kAheadV = 4;  // V operands read ahead (m-tiles); the first ones load during QK
-  bf16x8 va[kMv];
-  auto load_v = [&](int m) {
-    va[m] = join_tr(lds_read_tr(tile + L.pv[0][m & 3] + 128 * (m >> 2)),
-                    lds_read_tr(tile + L.pv[1][m & 3] + 128 * (m >> 2)));
-  };
-  // ---- S^T = K Q^T: two 16-token blocks, chains interleaved ----
-  // K operands are read kAhead k-steps ahead of their MFMAs; a scheduling
-  // barrier closes every step so the reads cannot sink next to their use and
-  // LDS latency overlaps MFMA work.
-  f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  bf16x8 ka[kQSteps][2];
-#pragma unroll
-  for (int s = 0; s < kAhead; ++s)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      ka[s][mt] = *reinterpret_cast<const bf16x8*>(tile + L.qk[mt][s & 1] + 128 * (s >> 1));
-#pragma unroll
-  for (int s = 0; s < kQSteps; ++s) {
-    hook(s);
-    if (s + kAhead < kQSteps) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        ka[s + kAhead][mt] =
-            *reinterpret_cast<const bf16x8*>(tile + L.qk[mt][(s + kAhead) & 1] + 128 * ((s + kAhead) >> 1));
-    }
-    if (s >= kQSteps - kAheadV) load_v(s - (kQSteps - kAheadV));
-    sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s][0], qreg[s], sacc[0], 0, 0, 0);
-    sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s][1], qreg[s], sacc[1], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // ---- online softmax of head 16w + c (log2 domain) ----
-  float x[8];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * mt + 4 * g + i;
-      float v = sacc[mt][i] * scale_log2;
-      if constexpr (kFp8) v *= scales[t];
-      v = (t < nvalid) ? v : -INFINITY;
-      x[4 * mt + i] = v;
-      mx = fmaxf(mx, v);
-    }
-  mx = max4_rows(mx);
-  float alpha = 1.f;
-  if (__any(mx > st.m_run + 8.f)) {  // rare: move the reference (always on the first tile)
-    const float m_new = fmaxf(st.m_run, mx);
-    alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);  // 0 on the first tile
-    st.m_run = m_new;
-    st.l_run *= alpha;
-  }
-  float psum = 0.f;
-  float pf[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float p = __builtin_amdgcn_exp2f(x[j] - st.m_run);
-    psum += p;
-    float pv = p;
-    if constexpr (kFp8) pv *= scales[16 * (j >> 2) + 4 * g + (j & 3)];
-    pf[j] = pv;
-  }
-  st.l_run += psum;
-  // P^T chunk of this lane: head 16w + c, k-elements 8g..8g+7 in score order
-  *reinterpret_cast<bf16x8*>(S.p + p_off(16 * w + c, g)) = pack8(pf);
-  if (g == 0) S.alpha[16 * w + c] = alpha;
-  __syncthreads();  // P and the rescale factors of all 64 heads visible
-
-  // ---- PV: O^T [dims 128w..+128][64 heads] += V^T P^T ----
-  float al[4];
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb) al[hb] = S.alpha[16 * hb + c];
-  if (__any(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
-#pragma unroll
-    for (int m = 0; m < kMv; ++m)
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) {
-        // (the opaque steps keep the AGPR -> VGPR copies inside this rare
-        // branch; otherwise they are hoisted into every tile)
-        asm volatile("" : "+a"(st.oacc[m][hb]));
-        st.oacc[m][hb] *= al[hb];
-        asm volatile("" : "+a"(st.oacc[m][hb]));
-      }
-  }
-  bf16x8 pb[4];
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb) pb[hb] = *reinterpret_cast<const bf16x8*>(S.p + p_off(16 * hb + c, g));
-#pragma unroll
-  for (int m = 0; m < kMv; ++m) {
-    if (m + kAheadV < kMv) load_v(m + kAheadV);
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-      st.oacc[m][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb[hb], st.oacc[m][hb], 0, 0, 0);
-      // keep the accumulator in AGPRs across the tile loop
-      asm volatile("" : "+a"(st.oacc[m][hb]));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 template <int N>
 __device__ __forceinline__ void wait_ahead(int ahead) {
   // at most `ahead` further tiles of N loads each may still be in flight
@@ -365,14 +254,26 @@ struct Soft {
   float pf[8];
 };
 
-__device__ __forceinline__ void soft_scores(Soft& sm, const f32x4 (&sacc)[2], int nvalid, int g, float scale_log2) {
+// FP8 cache: the per-token scales of the 8 tokens whose scores a lane holds
+// (element j: token 16 (j / 4) + 4g + j % 4 of the tile). The scale
+// multiplies the score (s = scale_t q.e_t) and P (p_t scale_t multiplies e_t
+// in PV); the bf16 path passes none.
+struct TokScale {
+  float v[8];
+};
+
+template <bool kFp8>
+__device__ __forceinline__ void soft_scores(Soft& sm, const f32x4 (&sacc)[2], int nvalid, int g, float scale_log2,
+                                            const TokScale& ts) {
   sm.mx = -INFINITY;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * mt + 4 * g + i;
-      const float v = (t < nvalid) ? sacc[mt][i] * scale_log2 : -INFINITY;
+      float v = sacc[mt][i] * scale_log2;
+      if constexpr (kFp8) v *= ts.v[4 * mt + i];
+      v = (t < nvalid) ? v : -INFINITY;
       sm.x[4 * mt + i] = v;
       sm.mx = fmaxf(sm.mx, v);
     }
@@ -388,13 +289,13 @@ __device__ __forceinline__ void soft_ref(Soft& sm, State& st) {
   sm.psum = 0.f;
 }
 
-template <int J0>
-__device__ __forceinline__ void soft_exp(Soft& sm, const State& st) {
+template <bool kFp8, int J0>
+__device__ __forceinline__ void soft_exp(Soft& sm, const State& st, const TokScale& ts) {
 #pragma unroll
   for (int j = J0; j < J0 + 4; ++j) {
     const float p = __builtin_amdgcn_exp2f(sm.x[j] - st.m_run);
     sm.psum += p;
-    sm.pf[j] = p;
+    sm.pf[j] = kFp8 ? p * ts.v[j] : p;
   }
 }
 
@@ -416,17 +317,29 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
-// One pipeline step (see above). kNext: tile nxt exists (QK + softmax of it).
-template <bool kNext, typename Hook>
+// One pipeline step (see above). kNext: tile nxt exists (QK + softmax of it);
+// ts: the token scales of tile nxt (FP8).
+template <bool kNext, bool kFp8 = false, typename Hook>
 __device__ __forceinline__ void pipe_step(const char* cur, const char* nxt, int nvalid_nxt, int buf, int w, int g,
                                           int c, const LdsBases& L, const bf16x8 (&qreg)[kQSteps], float scale_log2,
-                                          State& st, const Lds& S, Hook&& hook) {
+                                          State& st, const Lds& S, Hook&& hook, const TokScale& ts = TokScale{}) {
   constexpr int kAheadV = 4;
   bf16x8 va[kMv];
   auto load_v = [&](int m) {
     va[m] = join_tr(lds_read_tr(cur + L.pv[0][m & 3] + 128 * (m >> 2)),
                     lds_read_tr(cur + L.pv[1][m & 3] + 128 * (m >> 2)));
   };
+  // P_i and alpha_i are read first: their LDS latency then hides behind the
+  // QK MFMAs instead of stalling the start of PV
+  const float* acur = S.alpha + kH * buf;
+  const char* pcur = S.p + kH * kPRowBytes * buf;
+  float al[4];
+  bf16x8 pb[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    al[hb] = acur[16 * hb + c];
+    pb[hb] = *reinterpret_cast<const bf16x8*>(pcur + p_off(16 * hb + c, g));
+  }
   f32x4 sacc[2];
   if constexpr (kNext) {
     qk_tile(nxt, L, qreg, sacc, hook, load_v);
@@ -435,10 +348,6 @@ __device__ __forceinline__ void pipe_step(const char* cur, const char* nxt, int 
     for (int m = 0; m < kAheadV; ++m) load_v(m);
   }
   // ---- alpha_i: rescale O (rare) ----
-  const float* acur = S.alpha + kH * buf;
-  float al[4];
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb) al[hb] = acur[16 * hb + c];
   if (__any(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
 #pragma unroll
     for (int m = 0; m < kMv; ++m)
@@ -449,10 +358,6 @@ __device__ __forceinline__ void pipe_step(const char* cur, const char* nxt, int 
         asm volatile("" : "+a"(st.oacc[m][hb]));
       }
   }
-  const char* pcur = S.p + kH * kPRowBytes * buf;
-  bf16x8 pb[4];
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb) pb[hb] = *reinterpret_cast<const bf16x8*>(pcur + p_off(16 * hb + c, g));
   // ---- PV_i with softmax_{i+1} in the MFMA shadows ----
   Soft sm;
 #pragma unroll
@@ -464,10 +369,10 @@ __device__ __forceinline__ void pipe_step(const char* cur, const char* nxt, int 
       asm volatile("" : "+a"(st.oacc[m][hb]));
     }
     if constexpr (kNext) {
-      if (m == 0) soft_scores(sm, sacc, nvalid_nxt, g, scale_log2);
+      if (m == 0) soft_scores<kFp8>(sm, sacc, nvalid_nxt, g, scale_log2, ts);
       if (m == 1) soft_ref(sm, st);
-      if (m == 2) soft_exp<0>(sm, st);
-      if (m == 3) soft_exp<4>(sm, st);
+      if (m == 2) soft_exp<kFp8, 0>(sm, st, ts);
+      if (m == 3) soft_exp<kFp8, 4>(sm, st, ts);
       if (m == 4) soft_store(sm, st, S.p + kH * kPRowBytes * (buf ^ 1), S.alpha + kH * (buf ^ 1), w, g, c);
       if (m <= 4) interleave_mfma_valu<4, 6>();
     }
@@ -528,10 +433,11 @@ __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int6
     f32x4 sacc[2];
     qk_tile(tile_ptr(0), L, qreg, sacc, [](int) {}, [](int) {});
     Soft sm;
-    soft_scores(sm, sacc, nvalid(0), g, scale_log2);
+    const TokScale none{};
+    soft_scores<false>(sm, sacc, nvalid(0), g, scale_log2, none);
     soft_ref(sm, st);
-    soft_exp<0>(sm, st);
-    soft_exp<4>(sm, st);
+    soft_exp<false, 0>(sm, st, none);
+    soft_exp<false, 4>(sm, st, none);
     soft_store(sm, st, S.p, S.alpha, w, g, c);
   }
   // ---- steady state ----
@@ -544,12 +450,12 @@ __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int6
     const int64_t nxt0 = t0 + (int64_t)phys(i + 3 < ntiles ? i + 3 : 0) * kBN;
     const bool spread = (i + 3 < ntiles) && (nxt0 + kBN <= t1);
     if (i + 3 < ntiles && !spread) issue(i + 3);
-    const uint16_t* ntb = base + nxt0 * c_t;
-    char* ndst = stage(i + 3);
+    const uint64_t ntb = uniform_ptr(base + nxt0 * c_t);
+    const uint32_t ndst = __builtin_amdgcn_readfirstlane(lds_addr(stage(i + 3)));
     pipe_step<true>(tile_ptr(i), tile_ptr(i + 1), nvalid(i + 1), i & 1, w, g, c, L, qreg, scale_log2, st, S,
                     [&](int s) {
                       if (spread && (s & 1) == 0 && (s >> 1) < kLdChunks)
-                        lds_dma16_sbase<P>(ntb, toff[s >> 1], lds_addr(ndst + kThreads * (s >> 1) * 16));
+                        lds_dma16_s<P>(ntb, toff[s >> 1], ndst + kThreads * (s >> 1) * 16);
                     });
   }
   __syncthreads();  // P of the last tile visible
@@ -557,89 +463,130 @@ __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int6
                    [](int) {});
 }
 
-// FP8 -> bf16 of one raw 32-token tile into a bf16 tile (swizzled layout),
-// each byte converted once per workgroup; the tile's scales travel with it.
-__device__ __forceinline__ void convert_tile(const char* raw, const float* sc_in, char* tile, float* sc_out) {
-  const int tid = threadIdx.x;
-  for (int Sx = tid; Sx < kBN * kFp8RowChunks; Sx += kThreads) {
-    const int row = Sx / kFp8RowChunks, sc16 = Sx % kFp8RowChunks;
-    const uint4 r = *reinterpret_cast<const uint4*>(raw + row * kDk + sc16 * 16);
-    const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
-    uint32_t o[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[q], 1.0f, false));
-      o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[q], 1.0f, true));
-    }
-    char* rowp = tile + row * (kRowChunks * 16);
-    *reinterpret_cast<uint4*>(rowp + swz(row, 2 * sc16) * 16) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(rowp + swz(row, 2 * sc16 + 1) * 16) = make_uint4(o[4], o[5], o[6], o[7]);
-  }
-  if (tid < kBN) sc_out[tid] = sc_in[tid];
-}
-
-// Tokens [t0, t1) of an FP8 E4M3 latent cache with per-token scales.
-// Raw stage u % 4 holds the e4m3 bytes of tile u, bf16 tile u % 2 its
-// conversion; the per-token scale multiplies the score (s = scale_t q.e_t)
-// and P (p_t * scale_t multiplies e_t in PV), never K itself.
+// Tokens [t0, t1) of an FP8 E4M3 latent cache with one fp32 scale per token
+// (entry = e4m3 * scale_t), through the same pipeline as bf16. The cache
+// bytes stream into registers two tiles ahead of use (nontemporal vector
+// loads: each thread holds 9 units of 8 bytes of a tile); during the QK
+// MFMAs of step i each unit of tile i+2 is converted to bf16 exactly
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and written to its swizzled LDS
+// position, and its register is refilled with tile i+4. Three bf16 stages:
+// tile i (PV), tile i+1 (QK), tile i+2 (being written). The scales are
+// loaded into registers one step ahead of the softmax that folds them in.
+// Tile order rotated as in run_bf16.
 __device__ __forceinline__ void run_fp8(const uint8_t* base, int64_t c_t, const float* sbase, int64_t s_t, int64_t t0,
                                         int64_t t1, int w, int g, int c, const LdsBases& L,
-                                        const bf16x8 (&qreg)[kQSteps], float scale_log2, State& st, const Lds& S) {
-  const int lane = threadIdx.x & 63;
+                                        const bf16x8 (&qreg)[kQSteps], float scale_log2, State& st, const Lds& S,
+                                        uint32_t rot_seed = 0) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const int tid = threadIdx.x;
   const int ntok = (int)(t1 - t0);
   const int ntiles = (ntok + kBN - 1) / kBN;
-  char* raw = S.tiles;                     // 4 x 18 KB
-  char* btile = S.tiles + 4 * kRawBytes;   // 2 x 36 KB
-  // wave w issues the tile's wave-loads w, w+4, ... (5 for waves 0-1, 4 for 2-3)
-  // plus one load of the tile's scales: per-wave counts for the waits
-  const int n_mine = (kRawWaveLoads - w + 3) / 4;
-  uint32_t roff[5];  // byte offset of this lane's 16-byte pieces inside a full raw tile
+  if (ntiles <= 0) return;
+  const int rot = (int)(rot_seed % (uint32_t)ntiles);
+  auto phys = [&](int i) { const int t = i + rot; return t >= ntiles ? t - ntiles : t; };
+  auto nvalid = [&](int i) { return min(kBN, ntok - kBN * phys(i)); };
+  auto stage = [&](int i) -> char* { return S.tiles + (i % 3) * kTileBytes; };
+  // unit j of this thread: 8 cache bytes of row u / 72, chunk u % 72 (u = tid + 256 j)
+  uint32_t goff[kLdChunks], loff[kLdChunks];
+  int urow[kLdChunks];
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    const int Bx = (w + 4 * k) * 1024 + 16 * lane;  // LDS byte of the piece, row-major [32][576]
-    roff[k] = (uint32_t)((Bx / kDk) * c_t + (Bx % kDk));
+  for (int j = 0; j < kLdChunks; ++j) {
+    const int u = tid + kThreads * j;
+    const int row = u / kRowChunks, ch = u % kRowChunks;
+    urow[j] = row;
+    goff[j] = (uint32_t)(ch * 8);
+    loff[j] = (uint32_t)(row * (kRowChunks * 16) + swz(row, ch) * 16);
   }
-  auto issue = [&](int u) {
-    const int64_t tok0 = t0 + (int64_t)u * kBN;
-    char* dst = raw + (u & 3) * kRawBytes;
-    if (tok0 + kBN <= t1) {
-      const uint8_t* tb = base + tok0 * c_t;
-#pragma unroll
-      for (int k = 0; k < 5; ++k)
-        if (k < n_mine) lds_dma16_sbase<Policy::kStream>(tb, roff[k], lds_addr(dst + (w + 4 * k) * 1024));
-    } else {  // last tile: past the range, re-read its last token (masked)
-#pragma unroll
-      for (int k = 0; k < 5; ++k) {
-        if (k < n_mine) {
-          const int Bx = (w + 4 * k) * 1024 + 16 * lane;
-          const int64_t tok = min(tok0 + Bx / kDk, t1 - 1);
-          lds_dma16<Policy::kStream>(base + tok * c_t + (Bx % kDk), lds_addr(dst + (w + 4 * k) * 1024));
-        }
-      }
-    }
-    const int64_t tok = min(tok0 + lane, t1 - 1);
-    lds_dma4<Policy::kStream>(sbase + tok * s_t, lds_addr(&S.rscale[((u & 3) * 4 + w) * 64]));
+  u32x2 raw[2][kLdChunks];
+  TokScale tsc[2];
+  // Addresses: a wavefront-uniform tile base plus a 32-bit lane offset; rows
+  // past the range's last token re-read it (lim = last valid row). The host
+  // bounds the token stride so that 32 rows fit 32-bit offsets.
+  const uint32_t ct32 = (uint32_t)c_t, st32 = (uint32_t)s_t;
+  auto load_unit = [&](int i, int j, u32x2& r) {
+    const int64_t tok0 = t0 + (int64_t)phys(i) * kBN;
+    const int lim = (int)min((int64_t)(kBN - 1), t1 - 1 - tok0);
+    const uint8_t* tb = base + tok0 * c_t;
+    const uint32_t off = (uint32_t)min(urow[j], lim) * ct32 + goff[j];
+    r = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tb + off));
   };
-  auto wait_raw = [&](int ahead) {
-    if (w < 2) wait_ahead<6>(ahead);  // 5 cache loads + 1 scale load per tile
-    else wait_ahead<5>(ahead);
+  auto load_scales = [&](int i, TokScale& ts) {
+    const int64_t tok0 = t0 + (int64_t)phys(i) * kBN;
+    const int lim = (int)min((int64_t)(kBN - 1), t1 - 1 - tok0);
+    const float* sb = sbase + tok0 * s_t;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ts.v[j] = __builtin_nontemporal_load(sb + (uint32_t)min(16 * (j >> 2) + 4 * g + (j & 3), lim) * st32);
   };
-  for (int u = 0; u < 4 && u < ntiles; ++u) issue(u);
-  if (ntiles > 0) {
-    wait_raw(min(3, ntiles - 1));  // raw 0 landed
-    __syncthreads();
-    convert_tile(raw, &S.rscale[0], btile, &S.bscale[0]);
+  auto convert_unit = [&](const u32x2& r, int j, char* tile) {
+    const uint32_t o0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, false));
+    const uint32_t o1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, true));
+    const uint32_t o2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, false));
+    const uint32_t o3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, true));
+    *reinterpret_cast<uint4*>(tile + loff[j]) = make_uint4(o0, o1, o2, o3);
+  };
+
+  // ---- prologue: tiles 0, 1 converted; tiles 2, 3 in flight; S_0 and P_0 ----
+  auto clampt = [&](int i) { return min(i, ntiles - 1); };
+#pragma unroll
+  for (int j = 0; j < kLdChunks; ++j) load_unit(0, j, raw[0][j]);
+  load_scales(0, tsc[0]);
+#pragma unroll
+  for (int j = 0; j < kLdChunks; ++j) load_unit(clampt(1), j, raw[1][j]);
+  load_scales(clampt(1), tsc[1]);
+#pragma unroll
+  for (int j = 0; j < kLdChunks; ++j) {
+    convert_unit(raw[0][j], j, stage(0));
+    load_unit(clampt(2), j, raw[0][j]);
   }
-  for (int u = 0; u < ntiles; ++u) {
-    if (u + 1 < ntiles) wait_raw(min(u + 3, ntiles - 1) - (u + 1));  // raw u+1 landed
-    __syncthreads();  // bf16 tile u complete; raw u+1 visible; tile u-1, its P and raw u fully consumed
-    if (u + 4 < ntiles) issue(u + 4);  // into the raw stage of tile u
-    if (u + 1 < ntiles)
-      convert_tile(raw + ((u + 1) & 3) * kRawBytes, &S.rscale[((u + 1) & 3) * 256], btile + ((u + 1) & 1) * kTileBytes,
-                   &S.bscale[((u + 1) & 1) * kBN]);
-    consume_tile<true>(btile + (u & 1) * kTileBytes, &S.bscale[(u & 1) * kBN], min(kBN, ntok - kBN * u), w, g, c, L,
-                       qreg, scale_log2, st, S, [](int) {});
+#pragma unroll
+  for (int j = 0; j < kLdChunks; ++j) {
+    convert_unit(raw[1][j], j, stage(1));
+    load_unit(clampt(3), j, raw[1][j]);
   }
+  __syncthreads();
+  {
+    f32x4 sacc[2];
+    qk_tile(stage(0), L, qreg, sacc, [](int) {}, [](int) {});
+    Soft sm;
+    soft_scores<true>(sm, sacc, nvalid(0), g, scale_log2, tsc[0]);
+    soft_ref(sm, st);
+    soft_exp<true, 0>(sm, st, tsc[0]);
+    soft_exp<true, 4>(sm, st, tsc[0]);
+    soft_store(sm, st, S.p, S.alpha, w, g, c);
+  }
+  // ---- steady state, two steps per trip so the register sets are static ----
+  // The loads and conversions of a step are unconditional (past the last
+  // tile they re-read the last tile and write a stage nobody reads again):
+  // loads under a branch make the compiler's wait placement fall back to
+  // waiting for every outstanding load, which would drain the stream.
+  auto step = [&](int i, auto parity) {
+    constexpr int P = decltype(parity)::value;  // i & 1
+    __syncthreads();  // P_i and bf16 tile i+1 visible; every wave is done with tile i-1 and P_{i-1}
+    const int conv_t = min(i + 2, ntiles - 1), refill_t = min(i + 4, ntiles - 1);
+    char* dst = stage(i + 2);
+    pipe_step<true, true>(stage(i), stage(i + 1), nvalid(i + 1), P, w, g, c, L, qreg, scale_log2, st, S,
+                          [&](int s) {
+                            if (s == 1) load_scales(conv_t, tsc[P]);  // tile i's scales are spent
+                            if ((s & 1) == 0 && (s >> 1) < kLdChunks) {
+                              const int j = s >> 1;
+                              convert_unit(raw[P][j], j, dst);
+                              load_unit(refill_t, j, raw[P][j]);
+                            }
+                          },
+                          tsc[P ^ 1]);
+  };
+  int i = 0;
+  for (; i + 2 < ntiles; i += 2) {
+    step(i, std::integral_constant<int, 0>{});
+    step(i + 1, std::integral_constant<int, 1>{});
+  }
+  if (i + 1 < ntiles) {
+    step(i, std::integral_constant<int, 0>{});
+    ++i;
+  }
+  __syncthreads();  // P of the last tile visible
+  pipe_step<false>(stage(ntiles - 1), nullptr, 0, (ntiles - 1) & 1, w, g, c, L, qreg, scale_log2, st, S, [](int) {});
 }
 
 // Closes the range: the softmax sum of every head into S.lsum (one barrier).

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mla_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
   __shared__ float alpha_s[2 * kH], lsum_s[kH];
-  const Lds S{smem, plds, alpha_s, lsum_s, nullptr, nullptr};
+  const Lds S{smem, plds, alpha_s, lsum_s};
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
