@@ -319,10 +319,13 @@ __device__ __forceinline__ void interleave_mfma_valu() {
 
 // One pipeline step (see above). kNext: tile nxt exists (QK + softmax of it);
 // ts: the token scales of tile nxt (FP8).
-template <bool kNext, bool kFp8 = false, typename Hook>
+// pv_hook(m) runs in PV m-step m (the FP8 path converts its next tile there,
+// where the LDS is far less busy than during QK).
+template <bool kNext, bool kFp8 = false, typename Hook, typename PvHook>
 __device__ __forceinline__ void pipe_step(const char* cur, const char* nxt, int nvalid_nxt, int buf, int w, int g,
                                           int c, const LdsBases& L, const bf16x8 (&qreg)[kQSteps], float scale_log2,
-                                          State& st, const Lds& S, Hook&& hook, const TokScale& ts = TokScale{}) {
+                                          State& st, const Lds& S, Hook&& hook, PvHook&& pv_hook,
+                                          const TokScale& ts = TokScale{}) {
   constexpr int kAheadV = 4;
   bf16x8 va[kMv];
   auto load_v = [&](int m) {
@@ -376,6 +379,7 @@ __device__ __forceinline__ void pipe_step(const char* cur, const char* nxt, int 
       if (m == 4) soft_store(sm, st, S.p + kH * kPRowBytes * (buf ^ 1), S.alpha + kH * (buf ^ 1), w, g, c);
       if (m <= 4) interleave_mfma_valu<4, 6>();
     }
+    pv_hook(m);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -456,17 +460,18 @@ __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int6
                     [&](int s) {
                       if (spread && (s & 1) == 0 && (s >> 1) < kLdChunks)
                         lds_dma16_s<P>(ntb, toff[s >> 1], ndst + kThreads * (s >> 1) * 16);
-                    });
+                    },
+                    [](int) {});
   }
   __syncthreads();  // P of the last tile visible
   pipe_step<false>(tile_ptr(ntiles - 1), nullptr, 0, (ntiles - 1) & 1, w, g, c, L, qreg, scale_log2, st, S,
-                   [](int) {});
+                   [](int) {}, [](int) {});
 }
 
 // Tokens [t0, t1) of an FP8 E4M3 latent cache with one fp32 scale per token
 // (entry = e4m3 * scale_t), through the same pipeline as bf16. The cache
 // bytes stream into registers two tiles ahead of use (nontemporal vector
-// loads: each thread holds 9 units of 8 bytes of a tile); during the QK
+// loads: each thread holds 9 units of 8 bytes of a tile); during the PV
 // MFMAs of step i each unit of tile i+2 is converted to bf16 exactly
 // (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and written to its swizzled LDS
 // position, and its register is refilled with tile i+4. Three bf16 stages:
@@ -568,8 +573,10 @@ __device__ __forceinline__ void run_fp8(const uint8_t* base, int64_t c_t, const 
     pipe_step<true, true>(stage(i), stage(i + 1), nvalid(i + 1), P, w, g, c, L, qreg, scale_log2, st, S,
                           [&](int s) {
                             if (s == 1) load_scales(conv_t, tsc[P]);  // tile i's scales are spent
-                            if ((s & 1) == 0 && (s >> 1) < kLdChunks) {
-                              const int j = s >> 1;
+                          },
+                          [&](int m) {  // units 0-1 at m-step 0, one per m-step after
+#pragma unroll
+                            for (int j = (m == 0 ? 0 : m + 1); j <= m + 1; ++j) {
                               convert_unit(raw[P][j], j, dst);
                               load_unit(refill_t, j, raw[P][j]);
                             }
@@ -586,7 +593,8 @@ __device__ __forceinline__ void run_fp8(const uint8_t* base, int64_t c_t, const 
     ++i;
   }
   __syncthreads();  // P of the last tile visible
-  pipe_step<false>(stage(ntiles - 1), nullptr, 0, (ntiles - 1) & 1, w, g, c, L, qreg, scale_log2, st, S, [](int) {});
+  pipe_step<false>(stage(ntiles - 1), nullptr, 0, (ntiles - 1) & 1, w, g, c, L, qreg, scale_log2, st, S, [](int) {},
+                   [](int) {});
 }
 
 // Closes the range: the softmax sum of every head into S.lsum (one barrier).
