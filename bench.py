@@ -47,13 +47,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # they were measured at; after any change the field is null until re-measured.
 TRAFFIC = {
     # profiles/prefill_gqa_zigzag_16k_c4_rank1.md
-    "prefill_gqa_kernel": dict(digest="f4c5284df440642f", fetch_kib=59977.3, write_kib=33792.3,
+    "prefill_gqa_kernel": dict(digest="a05c63901c15906f", fetch_kib=64744.4, write_kib=33792.0,
                                fetch_scale=1.99994, write_scale=1.0,
-                               fetch_bytes=122830013, write_bytes=34603352),
+                               fetch_bytes=132592851, write_bytes=34603008),
     # profiles/decode_mla_b64_h64_ctx131072_c8.md
-    "decode_mla_kernel<bf16>": dict(digest="ae03b88e197884f1", fetch_kib=599161.1, write_kib=32832.0,
+    "decode_mla_kernel<bf16>": dict(digest="07a06633a6828157", fetch_kib=599186.3, write_kib=32832.2,
                                     fetch_scale=1.99994, write_scale=1.0,
-                                    fetch_bytes=1227047643, write_bytes=33619968),
+                                    fetch_bytes=1227099488, write_bytes=33620173),
 }
 
 
