@@ -162,3 +162,50 @@ def causal_pairs(plan):
     """(query, key) pairs a rank's queries read, diagonal included: a query at
     position p reads p + 1 keys (*Long Context* 1.1 and 2.2)."""
     return int(np.sum(plan.pos_id.astype(np.int64) + 1))
+
+
+# ---------------------------------------------------------------- round robin
+#
+# Decode CP with round-robin storage -- *Long Context* 3.1: with C GPUs,
+# token (slot) p of a request is stored on GPU p mod C, as row p // C of
+# that GPU's cache ("slot 9 on 4 GPUs is row 2 on GPU 1"); the
+# "DeepSeek-V4 Attention Inference Systems" notes, section 5, write the same
+# owner rule as owner(j) = j mod P, and 5.3 adds that entries replicated on
+# every rank (a local window, attention sinks) must add their probability
+# mass once: only a designated rank includes them.
+#
+# Local cache layout taken here (the pages leave it open): a rank's cache
+# for one request holds the n_repl replicated entries in rows [0, n_repl)
+# and its own tokens rank, rank + C, rank + 2C, ... in rows n_repl,
+# n_repl + 1, ... (ascending slot), so a new token is appended at the end.
+# The rank's decode range is rows [0, n_repl + n_own) on the designated
+# rank and [n_repl, n_repl + n_own) on the others.
+
+def round_robin_slot(slot, C):
+    """(gpu, row) of a slot: gpu = slot mod C, row = slot // C."""
+    if C < 1 or slot < 0:
+        raise ValueError("bad slot or C")
+    return slot % C, slot // C
+
+
+def round_robin_own_tokens(L, C, rank):
+    """The slots of an L-token request that rank `rank` stores, in local
+    row order."""
+    if C < 1 or not (0 <= rank < C) or L < 0:
+        raise ValueError("bad L, C or rank")
+    return list(range(rank, L, C))
+
+
+def plan_round_robin(C, rank, ctx_len, n_repl=0, repl_rank=0):
+    """Decode range of rank `rank` in its local cache, per request:
+    (kv_begin [n_req], kv_end [n_req]) as int32 arrays."""
+    if C < 1 or not (0 <= rank < C) or n_repl < 0 or not (0 <= repl_rank < C):
+        raise ValueError("bad C, rank or replication")
+    beg, end = [], []
+    for L in ctx_len:
+        if L < 0:
+            raise ValueError("negative length")
+        n_own = len(round_robin_own_tokens(int(L), C, rank))
+        beg.append(0 if rank == repl_rank else n_repl)
+        end.append(n_repl + n_own)
+    return np.array(beg, np.int32), np.array(end, np.int32)
