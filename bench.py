@@ -238,7 +238,63 @@ def bench_decode(cpa, torch, synth, steps, warmup, warmup_ms):
                          gpu_ms_per_step=gpu_step_ms,
                          launch_ms=lm, launch_gbs=launch_bytes / (lm * 1e-3) / 1e9,
                          launch_bytes=launch_bytes)
+    del cache_fp8, sc
+    torch.cuda.empty_cache()
+    res["round_robin_bf16"] = bench_round_robin(cpa, torch, c, q, cache_bf16, steps, warmup, warmup_ms)
     return res
+
+
+def bench_round_robin(cpa, torch, c, q, cache, steps, warmup, warmup_ms):
+    """Round-robin decode storage at the same shape: slot p of every request
+    on rank p mod C as row p // C. The C local caches are written from the
+    full cache by the slot-translating cache write (timed once, bytes read +
+    written), then a step is C partial launches over them plus the merge."""
+    B, L, C, H = c["B"], c["L"], c["C"], c["Hq"]
+    dev = cache.device
+    full = cache[:, :, 0, :]
+    src = full.reshape(B * L, -1)
+    slot = torch.arange(L, dtype=torch.int64, device=dev).repeat(B)
+    req = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(L)
+    plans = [cpa.cp_plan_round_robin(C, r, [L] * B) for r in range(C)]
+    rows = max(p[2] for p in plans)
+    locals_ = [torch.empty((B, rows, 1, cache.shape[-1]), dtype=cache.dtype, device=dev) for _ in range(C)]
+    ev = _events(torch, 1)[0]
+    ev[0].record()
+    for r in range(C):
+        cpa.attn_cache_write_round_robin(C, r, src, slot, req, locals_[r][:, :, 0, :])
+    ev[1].record()
+    torch.cuda.synchronize()
+    write_ms = ev[0].elapsed_time(ev[1])
+    write_bytes = 2 * B * L * cache.shape[-1] * cache.element_size() + C * B * L * 12
+    begins = [torch.from_numpy(p[0]).to(dev) for p in plans]
+    ends = [torch.from_numpy(p[1]).to(dev) for p in plans]
+    max_len = max(int((p[1] - p[0]).max()) for p in plans)
+    po = torch.empty((C, B, H, 512), dtype=torch.float32, device=dev)
+    pl = torch.empty((C, B, H), dtype=torch.float32, device=dev)
+    mo = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    ml = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, cpa.attn_decode_workspace_size(B, H, 512, max_len)), dtype=torch.uint8, device=dev)
+
+    def step():
+        for r in range(C):
+            cpa.attn_decode_shard(q, locals_[r], None, begins[r], ends[r], max_len, c["scale"],
+                                  o_part=po[r], lse_part=pl[r], workspace=ws)
+        cpa.attn_merge_states(po, pl, out=mo, lse_out=ml)
+
+    _warm(torch, step, warmup, warmup_ms)
+    sev = _events(torch, 1)[0]
+    sev[0].record()
+    for _ in range(steps):
+        step()
+    sev[1].record()
+    torch.cuda.synchronize()
+    ms = sev[0].elapsed_time(sev[1]) / steps
+    step_bytes = B * L * 1152 + C * B * H * 576 * 2 + 2 * C * B * H * (512 + 1) * 4 + B * H * (512 + 1) * 4
+    del locals_
+    torch.cuda.empty_cache()
+    return dict(gpu_ms_per_step=ms, gbs=step_bytes / (ms * 1e-3) / 1e9, algorithmic_bytes=step_bytes,
+                cache_write_ms=write_ms, cache_write_gbs=write_bytes / (write_ms * 1e-3) / 1e9,
+                cache_write_bytes=write_bytes)
 
 
 def cpu_baseline(synth, prefill, seconds):
@@ -383,9 +439,12 @@ def main():
                 "traffic": traffic("decode_mla_kernel<bf16>")[0],
                 "traffic_detail": traffic("decode_mla_kernel<bf16>")[1],
             },
-            "frac_of_hbm_peak_step": {k: round(dec[k]["gbs"] / PEAK_HBM_GBS, 4) for k in ("bf16", "fp8")},
+            "round_robin_bf16": {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["round_robin_bf16"].items()},
+            "frac_of_hbm_peak_step": {k: round(dec[k]["gbs"] / PEAK_HBM_GBS, 4) for k in ("bf16", "fp8", "round_robin_bf16")},
         }
-        log(f"[bench] decode bf16 {dec['bf16']['gbs']:.0f} GB/s/step, fp8 {dec['fp8']['gbs']:.0f} GB/s/step")
+        log(f"[bench] decode bf16 {dec['bf16']['gbs']:.0f} GB/s/step, fp8 {dec['fp8']['gbs']:.0f} GB/s/step, "
+            f"round-robin bf16 {dec['round_robin_bf16']['gbs']:.0f} GB/s/step "
+            f"(cache write {dec['round_robin_bf16']['cache_write_gbs']:.0f} GB/s)")
 
     if not args.no_extra_prefill:
         for k, key in ((4, "prefill_mla_zigzag"), (5, "prefill_interleave")):

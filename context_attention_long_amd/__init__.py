@@ -54,7 +54,8 @@ assert SEGMENT_DTYPE.itemsize == ctypes.sizeof(CpaSegment) == 32
 
 # exported symbols of include/cpattn.h
 SYMBOLS = ("cpa_last_error", "cpa_abi_version", "cp_plan_zigzag", "cp_plan_interleave", "cp_decode_shards",
-           "attn_prefill_shard", "attn_decode_workspace_size", "attn_decode_shard", "attn_merge_states")
+           "attn_prefill_shard", "attn_decode_workspace_size", "attn_decode_shard", "attn_merge_states",
+           "cp_round_robin_slot", "cp_plan_round_robin", "attn_cache_write_round_robin")
 
 _lib_handle = None
 
@@ -86,6 +87,15 @@ def lib():
         L.attn_decode_shard.argtypes = [P(CpaTensor), P(CpaTensor), P(CpaTensor), P(CpaTensor), ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, P(CpaTensor),
                                         P(CpaTensor), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.cp_round_robin_slot.restype = ctypes.c_int
+        L.cp_round_robin_slot.argtypes = [ctypes.c_int64, ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int64)]
+        L.cp_plan_round_robin.restype = ctypes.c_int
+        L.cp_plan_round_robin.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int64),
+                                          ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int32),
+                                          P(ctypes.c_int64)]
+        L.attn_cache_write_round_robin.restype = ctypes.c_int
+        L.attn_cache_write_round_robin.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(CpaTensor),
+                                                   ctypes.c_void_p, ctypes.c_void_p, P(CpaTensor), ctypes.c_void_p]
         L.attn_merge_states.restype = ctypes.c_int
         L.attn_merge_states.argtypes = [ctypes.c_int32, P(CpaTensor), P(CpaTensor), P(CpaTensor), P(CpaTensor),
                                         ctypes.c_void_p]
@@ -157,6 +167,28 @@ def cp_decode_shards(L, C):
     e = (ctypes.c_int64 * C)()
     _check(lib().cp_decode_shards(int(L), int(C), b, e))
     return list(zip(list(b), list(e)))
+
+
+def cp_round_robin_slot(slot, C):
+    """(rank, row) of a slot in round-robin decode storage."""
+    r = ctypes.c_int32()
+    row = ctypes.c_int64()
+    _check(lib().cp_round_robin_slot(int(slot), int(C), ctypes.byref(r), ctypes.byref(row)))
+    return r.value, row.value
+
+
+def cp_plan_round_robin(C, rank, ctx_len, n_repl=0, repl_rank=0):
+    """Per-request decode range of `rank` in its round-robin local cache:
+    (kv_begin int32 array, kv_end int32 array, rows a local cache needs)."""
+    n = len(ctx_len)
+    cl = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in ctx_len])
+    beg = np.zeros(n, np.int32)
+    end = np.zeros(n, np.int32)
+    mx = ctypes.c_int64()
+    _check(lib().cp_plan_round_robin(int(C), int(rank), n, cl, int(n_repl), int(repl_rank),
+                                     beg.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     end.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(mx)))
+    return beg, end, mx.value
 
 
 # ------------------------------------------------------------------ tensors
@@ -265,3 +297,20 @@ def attn_merge_states(o_parts, lse_parts, out=None, lse_out=None, out_dtype=None
     _check(lib().attn_merge_states(S, ctypes.byref(do), ctypes.byref(dl), ctypes.byref(dout), ctypes.byref(dlo),
                                    _stream(stream)))
     return out, lse_out
+
+
+def attn_cache_write_round_robin(C, rank, src, slot, req, dst, n_repl=0, stream=None, dtype=None):
+    """Write rows of src [n, W] into rank `rank`'s round-robin local cache
+    dst [B, Lmax_local, W] (row n_repl + slot // C of request req) where
+    slot % C == rank. slot: int64 device tensor [n]; req: int32 device [n].
+    dtype overrides the cpa dtype (raw FP8 bytes as torch.uint8)."""
+    torch = _torch()
+    if slot.dtype != torch.int64 or req.dtype != torch.int32 or not slot.is_contiguous() or not req.is_contiguous():
+        raise TypeError("slot must be a contiguous int64 tensor and req a contiguous int32 tensor")
+    if slot.numel() != src.shape[0] or req.numel() != src.shape[0]:
+        raise ValueError("slot and req need one entry per source row")
+    ds, dd = tensor_desc(src, dtype), tensor_desc(dst, dtype)
+    _check(lib().attn_cache_write_round_robin(int(C), int(rank), int(n_repl), ctypes.byref(ds),
+                                              ctypes.c_void_p(slot.data_ptr()), ctypes.c_void_p(req.data_ptr()),
+                                              ctypes.byref(dd), _stream(stream)))
+    return dst

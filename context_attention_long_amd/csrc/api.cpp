@@ -473,3 +473,44 @@ extern "C" cpa_status attn_prefill_shard(const cpa_tensor* q, const cpa_tensor* 
   a.scale_log2 = softmax_scale * kLog2e;
   return hip_status(cpa::launch_prefill_mla(a, seg, n_seg, stream), "prefill launch");
 }
+
+// ------------------------------------------------------ round-robin cache write
+
+extern "C" cpa_status attn_cache_write_round_robin(int32_t C, int32_t rank, int32_t n_repl, const cpa_tensor* src,
+                                                   const int64_t* slot, const int32_t* req, const cpa_tensor* dst,
+                                                   void* stream) {
+  cpa::clear_error();
+  if (C < 1 || rank < 0 || rank >= C) return fail(CPA_E_INVAL, "cache write: bad C = %d or rank = %d", C, rank);
+  if (n_repl < 0) return fail(CPA_E_INVAL, "cache write: n_repl < 0");
+  const unsigned any = (1u << CPA_F32) | (1u << CPA_BF16) | (1u << CPA_FP8_E4M3);
+  CPA_TRY(check_tensor(src, "cache write src", any, 2, 4));
+  CPA_TRY(check_tensor(dst, "cache write dst", any, 3, 4));
+  if (src->dtype != dst->dtype) return fail(CPA_E_INVAL, "cache write: src and dst dtypes differ");
+  if (src->shape[1] != dst->shape[2]) return fail(CPA_E_INVAL, "cache write: src rows and dst rows differ in width");
+  const int64_t es = elem_size(src->dtype);
+  const int64_t row_bytes = src->shape[1] * es;
+  if (row_bytes % 4) return fail(CPA_E_INVAL, "cache write: row of %lld bytes is not a multiple of 4", (long long)row_bytes);
+  const int64_t n = src->shape[0];
+  if (n == 0 || dst->shape[0] == 0 || dst->shape[1] == 0) return CPA_OK;
+  if (slot == nullptr || req == nullptr) return fail(CPA_E_INVAL, "cache write: slot / req is NULL");
+  if (((uintptr_t)slot) % 8 || ((uintptr_t)req) % 4) return fail(CPA_E_INVAL, "cache write: slot / req misaligned");
+  if (dst->shape[0] > INT32_MAX) return fail(CPA_E_INVAL, "cache write: too many requests");
+  cpa::CacheWriteArgs a{};
+  a.src = static_cast<const char*>(src->data);
+  a.slot = slot;
+  a.req = req;
+  a.dst = static_cast<char*>(dst->data);
+  a.n = n;
+  a.src_row = src->stride[0] * es;
+  a.dst_b = dst->stride[0] * es;
+  a.dst_row = dst->stride[1] * es;
+  a.row_bytes = row_bytes;
+  a.C = C;
+  a.rank = rank;
+  a.n_repl = n_repl;
+  a.B = (int32_t)dst->shape[0];
+  a.Lmax = dst->shape[1];
+  a.vec16 = row_bytes % 16 == 0 && a.src_row % 16 == 0 && a.dst_b % 16 == 0 && a.dst_row % 16 == 0 &&
+            ((uintptr_t)src->data) % 16 == 0 && ((uintptr_t)dst->data) % 16 == 0;
+  return hip_status(cpa::launch_cache_write_rr(a, stream), "cache write launch");
+}

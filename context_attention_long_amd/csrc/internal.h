@@ -86,11 +86,23 @@ struct PrefillMlaArgs {
   float scale_log2;
 };
 
+struct CacheWriteArgs {
+  const char* src;      // [n, row] bytes
+  const int64_t* slot;  // [n]
+  const int32_t* req;   // [n]
+  char* dst;            // [B, Lmax, row] bytes
+  int64_t n, src_row, dst_b, dst_row, row_bytes;  // byte strides and row size
+  int32_t C, rank, n_repl, B;
+  int64_t Lmax;
+  int32_t vec16;        // 16-byte lanes (row size and strides multiples of 16)
+};
+
 // ---- launchers (return hipSuccess or the launch error) ----
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_decode_gqa(const DecodeGqaArgs& a, void* stream);
 int launch_decode_mla(const DecodeMlaArgs& a, void* stream);
 int launch_prefill_gqa(const PrefillGqaArgs& a, const cpa_segment* seg, int n_seg, void* stream);
 int launch_prefill_mla(const PrefillMlaArgs& a, const cpa_segment* seg, int n_seg, void* stream);
+int launch_cache_write_rr(const CacheWriteArgs& a, void* stream);
 
 }  // namespace cpa

@@ -186,3 +186,44 @@ extern "C" cpa_status cp_decode_shards(int64_t L, int32_t C, int64_t* begin, int
   }
   return CPA_OK;
 }
+
+// Round-robin decode storage -- "How GPUs Share a Long Context During LLM
+// Inference", 3.1: slot p of a request lives on rank p mod C as row p / C;
+// "DeepSeek-V4 Attention Inference Systems" notes, 5.3: entries replicated
+// on every rank add their probability mass on one designated rank only.
+// Local cache layout: rows [0, n_repl) replicated entries, then the rank's
+// own slots in ascending order.
+extern "C" cpa_status cp_round_robin_slot(int64_t slot, int32_t C, int32_t* rank, int64_t* row) {
+  cpa::clear_error();
+  if (C < 1 || slot < 0) return cpa::fail(CPA_E_INVAL, "round robin: bad slot %lld or C = %d", (long long)slot, C);
+  if (!rank || !row) return cpa::fail(CPA_E_INVAL, "round robin: NULL output");
+  *rank = (int32_t)(slot % C);
+  *row = slot / C;
+  return CPA_OK;
+}
+
+extern "C" cpa_status cp_plan_round_robin(int32_t C, int32_t rank, int32_t n_req, const int64_t* ctx_len,
+                                          int32_t n_repl, int32_t repl_rank, int32_t* kv_begin, int32_t* kv_end,
+                                          int64_t* max_local_rows) {
+  cpa::clear_error();
+  if (C < 1) return cpa::fail(CPA_E_INVAL, "round robin plan: C = %d must be >= 1", C);
+  if (rank < 0 || rank >= C) return cpa::fail(CPA_E_INVAL, "round robin plan: rank %d not in [0, %d)", rank, C);
+  if (repl_rank < 0 || repl_rank >= C)
+    return cpa::fail(CPA_E_INVAL, "round robin plan: repl_rank %d not in [0, %d)", repl_rank, C);
+  if (n_req < 0 || n_repl < 0) return cpa::fail(CPA_E_INVAL, "round robin plan: negative n_req or n_repl");
+  if (n_req > 0 && (!ctx_len || !kv_begin || !kv_end))
+    return cpa::fail(CPA_E_INVAL, "round robin plan: NULL array");
+  int64_t mx = n_repl;
+  for (int32_t b = 0; b < n_req; ++b) {
+    const int64_t L = ctx_len[b];
+    if (L < 0) return cpa::fail(CPA_E_INVAL, "round robin plan: request %d has a negative length", b);
+    const int64_t own = L > rank ? (L - rank + C - 1) / C : 0;
+    const int64_t end = n_repl + own;
+    if (end > INT32_MAX) return cpa::fail(CPA_E_INVAL, "round robin plan: request %d needs more than 2^31-1 rows", b);
+    kv_begin[b] = rank == repl_rank ? 0 : n_repl;
+    kv_end[b] = (int32_t)end;
+    mx = end > mx ? end : mx;
+  }
+  if (max_local_rows) *max_local_rows = mx;
+  return CPA_OK;
+}

@@ -210,6 +210,56 @@ cpa_status attn_merge_states(int32_t n_states, const cpa_tensor* o_parts,
                              const cpa_tensor* lse_parts, const cpa_tensor* out,
                              const cpa_tensor* lse_out, void* stream);
 
+/*
+ * Round-robin decode storage (Long Context 3.1: "it stores token p of a
+ * request on GPU p mod C"; the reading and writing code translates a slot
+ * into gpu = slot % C and row = slot / C; DeepSeek-V4 notes, section 5:
+ * owner(j) = j mod P).
+ *
+ * cp_round_robin_slot: host, pure. *rank = slot % C, *row = slot / C.
+ * CPA_E_INVAL if slot < 0, C < 1 or an output is NULL.
+ */
+cpa_status cp_round_robin_slot(int64_t slot, int32_t C, int32_t* rank, int64_t* row);
+
+/*
+ * cp_plan_round_robin: host, pure. The decode range of rank `rank` in its
+ * round-robin local cache, per request. Local cache layout: rows
+ * [0, n_repl) hold n_repl entries replicated on every rank (a local
+ * window, attention sinks), rows n_repl, n_repl + 1, ... the rank's own
+ * slots rank, rank + C, ... of the request in ascending order. Replicated
+ * entries must add their probability mass once (DeepSeek-V4 notes, 5.3):
+ * only repl_rank includes them.
+ *   ctx_len  [n_req] int64  slots stored for each request (>= 0)
+ *   kv_begin [n_req] int32  out: 0 on repl_rank, n_repl elsewhere
+ *   kv_end   [n_req] int32  out: n_repl + number of own slots
+ *   max_local_rows          out (may be NULL): rows a local cache needs
+ * The ranges feed attn_decode_shard on that rank's local cache; the C
+ * partial states merged with attn_merge_states equal attention over the
+ * n_repl replicated entries and all ctx_len slots. CPA_E_INVAL on bad C,
+ * rank, repl_rank, a negative count, NULL arrays or a range past 2^31-1.
+ */
+cpa_status cp_plan_round_robin(int32_t C, int32_t rank, int32_t n_req, const int64_t* ctx_len,
+                               int32_t n_repl, int32_t repl_rank, int32_t* kv_begin, int32_t* kv_end,
+                               int64_t* max_local_rows);
+
+/*
+ * attn_cache_write_round_robin: device, asynchronous. Writes entries into
+ * rank `rank`'s round-robin local cache (Long Context 3.1: the cache write
+ * translates a slot into a GPU and a row). Entry i (row i of src) of
+ * request req[i] at slot slot[i] is copied to dst[req[i], n_repl + slot[i] / C]
+ * when slot[i] % C == rank; entries owned by other ranks, with a negative
+ * slot or request, a request >= B, or a row past Lmax_local are skipped.
+ *   src  [n, W]                any dtype (bytes are copied)
+ *   slot [n] int64, req [n] int32: device arrays, 8- and 4-byte aligned
+ *   dst  [B, Lmax_local, W]    same dtype as src
+ * Row size and row strides must be multiples of 4 bytes (16 bytes gives
+ * 16-byte copies). The FP8 cache's per-token scales are written by a second
+ * call with W = 1 f32 rows. Entries with equal (req, slot) race.
+ */
+cpa_status attn_cache_write_round_robin(int32_t C, int32_t rank, int32_t n_repl, const cpa_tensor* src,
+                                        const int64_t* slot, const int32_t* req, const cpa_tensor* dst,
+                                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

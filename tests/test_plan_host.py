@@ -54,3 +54,30 @@ def test_decode_shards_bit_exact():
     for L in (0, 1, 7, 4096, 131072, 1001):
         for C in (1, 2, 3, 4, 8, 16):
             assert cpa.cp_decode_shards(L, C) == plans.contiguous_shards(L, C)
+
+
+def test_round_robin_plan_bit_exact():
+    import context_attention_long_amd as cpa
+    from oracle import plans
+    ctx = [0, 1, 2, 7, 31, 100]
+    for C in (1, 2, 3, 4, 8):
+        for n_repl in (0, 2):
+            for owner in range(min(C, 2)):
+                for r in range(C):
+                    beg, end, mx = cpa.cp_plan_round_robin(C, r, ctx, n_repl, owner)
+                    rb, re = plans.plan_round_robin(C, r, ctx, n_repl, owner)
+                    assert np.array_equal(beg, rb) and np.array_equal(end, re)
+                    assert mx == max([n_repl] + list(re))
+        for slot in range(0, 40):
+            assert cpa.cp_round_robin_slot(slot, C) == plans.round_robin_slot(slot, C)
+
+
+def test_round_robin_plan_rejects_bad_arguments():
+    import context_attention_long_amd as cpa
+    for args in ((0, 0, [3]), (2, 2, [3]), (2, -1, [3]), (2, 0, [-1])):
+        with pytest.raises(cpa.CpaError):
+            cpa.cp_plan_round_robin(*args)
+    with pytest.raises(cpa.CpaError):
+        cpa.cp_plan_round_robin(2, 0, [3], 1, 2)
+    with pytest.raises(cpa.CpaError):
+        cpa.cp_round_robin_slot(-1, 4)
