@@ -174,6 +174,22 @@ def decode_shard(q, kcache, begin, end, scale, vcache=None, dv=None, decode=None
     return O, L
 
 
+def decode_shard_mq(q, kcache, begin, end, scale, vcache=None, dv=None, decode=None,
+                    kv_scale=None, batch=None):
+    """Multi-query decode on one shard: request b has Q query rows, and row k
+    attends cache rows [begin_b, end[b*Q + k]) exactly as decode_shard
+    attends a single query (the causal ends come from plan_multi_query).
+
+    q [B, Q, Hq, Dqk]; begin [B]; end [B * Q]; the rest as decode_shard.
+    Returns O [B, Q, Hq, Dv], LSE [B, Q, Hq]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Q = q.shape[:2]
+    end = np.asarray(end).reshape(B, Q)
+    outs = [decode_shard(q[:, k], kcache, begin, end[:, k], scale, vcache=vcache, dv=dv, decode=decode,
+                         kv_scale=kv_scale, batch=batch) for k in range(Q)]
+    return np.stack([o for o, _ in outs], axis=1), np.stack([l for _, l in outs], axis=1)
+
+
 def merge_states(o_parts, lse_parts):
     """Exact LSE merge of S partial states. o_parts [S, ..., Dv],
     lse_parts [S, ...]. A state with lse = -inf carries no mass; if every

@@ -209,3 +209,47 @@ def plan_round_robin(C, rank, ctx_len, n_repl=0, repl_rank=0):
         beg.append(0 if rank == repl_rank else n_repl)
         end.append(n_repl + n_own)
     return np.array(beg, np.int32), np.array(end, np.int32)
+
+
+# ------------------------------------------------------- multi-query decode
+#
+# Speculative / MTP decode under decode CP (*Long Context* section 9 names
+# it; the DeepSeek-V4 notes, section 11, sweep the query/spec width 1, 2, 4,
+# 8): a request carries Q query rows, its last Q slots, whose keys are
+# already in the cache. Attention is causal (*Long Context* 1.1), so row k at
+# slot p = L - Q + k reads slots 0..p. The reading taken here (the pages do
+# not spell it out): on a rank, row k reads the part of 0..p that the rank
+# stores; replicated rows of a round-robin cache are seen by every row.
+
+def plan_multi_query(layout, C, rank, ctx_len, Q, n_repl=0, repl_rank=0):
+    """Per-row decode ranges of rank `rank` in its local cache:
+    (kv_begin int32 [n_req], kv_end int32 [n_req * Q]).
+
+    layout "contiguous": the local cache holds the rank's chunk of
+    contiguous_shards(L, C) from row 0. layout "round_robin": local cache as
+    in plan_round_robin. Rows are found by listing the slots the rank stores
+    and counting those at or below each query slot."""
+    if Q < 1 or C < 1 or not (0 <= rank < C):
+        raise ValueError("bad Q, C or rank")
+    if layout == "contiguous" and (n_repl or repl_rank):
+        raise ValueError("contiguous shards take no replicated rows")
+    beg, end = [], []
+    for L in ctx_len:
+        L = int(L)
+        if L < Q:
+            raise ValueError("a request stores fewer than Q slots")
+        if layout == "contiguous":
+            s0, s1 = contiguous_shards(L, C)[rank]
+            stored = list(range(s0, s1))     # local row i holds slot s0 + i
+            first = 0
+        elif layout == "round_robin":
+            stored = round_robin_own_tokens(L, C, rank)   # local row n_repl + i
+            first = n_repl
+            beg_b = 0 if rank == repl_rank else n_repl
+        else:
+            raise ValueError("unknown layout")
+        beg.append(0 if layout == "contiguous" else beg_b)
+        for k in range(Q):
+            p = L - Q + k
+            end.append(first + sum(1 for t in stored if t <= p))
+    return np.array(beg, np.int32), np.array(end, np.int32)
