@@ -241,7 +241,50 @@ def bench_decode(cpa, torch, synth, steps, warmup, warmup_ms):
     del cache_fp8, sc
     torch.cuda.empty_cache()
     res["round_robin_bf16"] = bench_round_robin(cpa, torch, c, q, cache_bf16, steps, warmup, warmup_ms)
+    res["multi_query_bf16"] = bench_multi_query(cpa, torch, synth, c, cache_bf16, 4, steps, warmup, warmup_ms)
     return res
+
+
+def bench_multi_query(cpa, torch, synth, c, cache, Q, steps, warmup, warmup_ms):
+    """Multi-query (MTP: one verified token + three drafts = 4 query rows)
+    decode at the same shape: contiguous shards, every query row causal over
+    its request; a step is C partial launches plus the merge of B * Q rows."""
+    B, L, C, H = c["B"], c["L"], c["C"], c["Hq"]
+    dev = cache.device
+    qb = synth.bf16_normal(3, 4, (B, Q, H, c["Dqk"]))
+    q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(dev)
+    shards = cpa.cp_decode_shards(L, C)
+    plans = [cpa.cp_plan_multi_query(cpa.CPA_LAYOUT_CONTIGUOUS, C, r, [L] * B, Q) for r in range(C)]
+    begins = [torch.from_numpy(p[0]).to(dev) for p in plans]
+    ends = [torch.from_numpy(p[1]).to(dev) for p in plans]
+    max_len = max(p[2] for p in plans)
+    po = torch.empty((C, B, Q, H, 512), dtype=torch.float32, device=dev)
+    pl = torch.empty((C, B, Q, H), dtype=torch.float32, device=dev)
+    mo = torch.empty((B * Q, H, 512), dtype=torch.float32, device=dev)
+    ml = torch.empty((B * Q, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, cpa.attn_decode_workspace_size(B * Q, H, 512, max_len)), dtype=torch.uint8, device=dev)
+
+    def step():
+        for r, (s0, s1) in enumerate(shards):
+            cpa.attn_decode_shard_mq(q, cache[:, s0:s1], None, begins[r], ends[r], max_len, c["scale"],
+                                     o_part=po[r], lse_part=pl[r], workspace=ws)
+        cpa.attn_merge_states(po.view(C, B * Q, H, 512), pl.view(C, B * Q, H), out=mo, lse_out=ml)
+
+    _warm(torch, step, warmup, warmup_ms)
+    sev = _events(torch, 1)[0]
+    sev[0].record()
+    for _ in range(steps):
+        step()
+    sev[1].record()
+    torch.cuda.synchronize()
+    ms = sev[0].elapsed_time(sev[1]) / steps
+    rows = B * Q
+    step_bytes = B * L * 1152 + C * rows * H * 576 * 2 + 2 * C * rows * H * (512 + 1) * 4 + rows * H * (512 + 1) * 4
+    # key reads of the query rows: row k of a request sees L - Q + k + 1 keys
+    keys = B * sum(L - Q + k + 1 for k in range(Q))
+    flops = keys * H * 2 * (576 + 512)
+    return dict(Q=Q, gpu_ms_per_step=ms, gbs=step_bytes / (ms * 1e-3) / 1e9, algorithmic_bytes=step_bytes,
+                tflops=flops / (ms * 1e-3) / 1e12, flops=flops)
 
 
 def bench_round_robin(cpa, torch, c, q, cache, steps, warmup, warmup_ms):
@@ -441,10 +484,17 @@ def main():
             },
             "round_robin_bf16": {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["round_robin_bf16"].items()},
             "frac_of_hbm_peak_step": {k: round(dec[k]["gbs"] / PEAK_HBM_GBS, 4) for k in ("bf16", "fp8", "round_robin_bf16")},
+            "multi_query_bf16": dict(
+                {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["multi_query_bf16"].items()},
+                workload="4 query rows per request (MTP3), causal among them; same cache and shards",
+                frac_of_hbm_peak=round(dec["multi_query_bf16"]["gbs"] / PEAK_HBM_GBS, 4),
+                frac_of_bf16_mfma_peak=round(dec["multi_query_bf16"]["tflops"] / PEAK_BF16_TFLOPS, 4)),
         }
         log(f"[bench] decode bf16 {dec['bf16']['gbs']:.0f} GB/s/step, fp8 {dec['fp8']['gbs']:.0f} GB/s/step, "
             f"round-robin bf16 {dec['round_robin_bf16']['gbs']:.0f} GB/s/step "
-            f"(cache write {dec['round_robin_bf16']['cache_write_gbs']:.0f} GB/s)")
+            f"(cache write {dec['round_robin_bf16']['cache_write_gbs']:.0f} GB/s), "
+            f"multi-query Q=4 {dec['multi_query_bf16']['gbs']:.0f} GB/s/step, "
+            f"{dec['multi_query_bf16']['tflops']:.0f} TFLOP/s")
 
     if not args.no_extra_prefill:
         for k, key in ((4, "prefill_mla_zigzag"), (5, "prefill_interleave")):

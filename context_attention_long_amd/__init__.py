@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libcpattn.so")
 
 CPA_OK, CPA_E_INVAL, CPA_E_UNSUPPORTED, CPA_E_CAPACITY, CPA_E_HIP = range(5)
 CPA_F32, CPA_BF16, CPA_FP8_E4M3 = 0, 1, 2
+CPA_LAYOUT_CONTIGUOUS, CPA_LAYOUT_ROUND_ROBIN = 0, 1
 
 _STATUS = {1: "CPA_E_INVAL", 2: "CPA_E_UNSUPPORTED", 3: "CPA_E_CAPACITY", 4: "CPA_E_HIP"}
 
@@ -55,7 +56,8 @@ assert SEGMENT_DTYPE.itemsize == ctypes.sizeof(CpaSegment) == 32
 # exported symbols of include/cpattn.h
 SYMBOLS = ("cpa_last_error", "cpa_abi_version", "cp_plan_zigzag", "cp_plan_interleave", "cp_decode_shards",
            "attn_prefill_shard", "attn_decode_workspace_size", "attn_decode_shard", "attn_merge_states",
-           "cp_round_robin_slot", "cp_plan_round_robin", "attn_cache_write_round_robin")
+           "cp_round_robin_slot", "cp_plan_round_robin", "attn_cache_write_round_robin",
+           "attn_decode_shard_mq", "cp_plan_multi_query")
 
 _lib_handle = None
 
@@ -87,6 +89,12 @@ def lib():
         L.attn_decode_shard.argtypes = [P(CpaTensor), P(CpaTensor), P(CpaTensor), P(CpaTensor), ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, P(CpaTensor),
                                         P(CpaTensor), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.attn_decode_shard_mq.restype = ctypes.c_int
+        L.attn_decode_shard_mq.argtypes = L.attn_decode_shard.argtypes
+        L.cp_plan_multi_query.restype = ctypes.c_int
+        L.cp_plan_multi_query.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          P(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          P(ctypes.c_int32), P(ctypes.c_int32), P(ctypes.c_int64)]
         L.cp_round_robin_slot.restype = ctypes.c_int
         L.cp_round_robin_slot.argtypes = [ctypes.c_int64, ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int64)]
         L.cp_plan_round_robin.restype = ctypes.c_int
@@ -191,6 +199,22 @@ def cp_plan_round_robin(C, rank, ctx_len, n_repl=0, repl_rank=0):
     return beg, end, mx.value
 
 
+def cp_plan_multi_query(layout, C, rank, ctx_len, Q, n_repl=0, repl_rank=0):
+    """Per-row decode ranges of `rank` for Q query rows per request (the last
+    Q slots of each request): (kv_begin int32 [n_req], kv_end int32
+    [n_req * Q], rows a local cache needs). layout: CPA_LAYOUT_CONTIGUOUS or
+    CPA_LAYOUT_ROUND_ROBIN."""
+    n = len(ctx_len)
+    cl = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in ctx_len])
+    beg = np.zeros(n, np.int32)
+    end = np.zeros(max(n * int(Q), 0), np.int32)
+    mx = ctypes.c_int64()
+    _check(lib().cp_plan_multi_query(int(layout), int(C), int(rank), n, cl, int(Q), int(n_repl), int(repl_rank),
+                                     beg.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     end.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(mx)))
+    return beg, end, mx.value
+
+
 # ------------------------------------------------------------------ tensors
 
 def _torch():
@@ -281,6 +305,39 @@ def attn_decode_shard(q, kcache, vcache, kv_begin, kv_end, max_shard_len, softma
                                    ctypes.c_void_p(kv_begin.data_ptr()), ctypes.c_void_p(kv_end.data_ptr()),
                                    int(max_shard_len), float(softmax_scale), ctypes.byref(do), ctypes.byref(dl),
                                    ctypes.c_void_p(ws_ptr), ws_bytes, _stream(stream)))
+    return o_part, lse_part
+
+
+def attn_decode_shard_mq(q, kcache, vcache, kv_begin, kv_end, max_shard_len, softmax_scale, kv_scale=None,
+                         o_part=None, lse_part=None, workspace=None, stream=None, kcache_dtype=None):
+    """Multi-query split-KV decode of one shard. q [B, Q, Hq, Dqk]; kv_begin
+    int32 [B], kv_end int32 [B * Q] (device); the rest as attn_decode_shard.
+    Returns (o_part [B, Q, Hq, Dv], lse_part [B, Q, Hq])."""
+    torch = _torch()
+    B, Q, Hq = q.shape[0], q.shape[1], q.shape[2]
+    Dv = vcache.shape[-1] if vcache is not None else 512
+    if o_part is None:
+        o_part = torch.empty((B, Q, Hq, Dv), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Q, Hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace_size(B * Q, Hq, Dv, max_shard_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    dq, dk = tensor_desc(q), tensor_desc(kcache, kcache_dtype)
+    dv = tensor_desc(vcache) if vcache is not None else None
+    ds = tensor_desc(kv_scale) if kv_scale is not None else None
+    do, dl = tensor_desc(o_part), tensor_desc(lse_part)
+    for t, n in ((kv_begin, B), (kv_end, B * Q)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != q.device:
+            raise TypeError("kv_begin / kv_end must be contiguous int32 tensors on the query's device")
+        if t.numel() != n:
+            raise ValueError("kv_begin needs B entries and kv_end B * Q")
+    _check(lib().attn_decode_shard_mq(ctypes.byref(dq), ctypes.byref(dk), _ptr(dv), _ptr(ds),
+                                      ctypes.c_void_p(kv_begin.data_ptr()), ctypes.c_void_p(kv_end.data_ptr()),
+                                      int(max_shard_len), float(softmax_scale), ctypes.byref(do), ctypes.byref(dl),
+                                      ctypes.c_void_p(ws_ptr), ws_bytes, _stream(stream)))
     return o_part, lse_part
 
 

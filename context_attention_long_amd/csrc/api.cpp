@@ -191,37 +191,27 @@ extern "C" cpa_status attn_merge_states(int32_t n_states, const cpa_tensor* o_pa
 
 namespace {
 
-cpa_status decode_plan(const cpa_tensor* q, const cpa_tensor* kcache, const cpa_tensor* vcache,
-                       int64_t max_len, DecodePlan* p) {
-  const int64_t B = q->shape[0], Hq = q->shape[1];
+// rows = query rows of the launch (requests x query rows per request)
+cpa_status decode_plan(int64_t rows, const cpa_tensor* kcache, const cpa_tensor* vcache, int64_t max_len,
+                       DecodePlan* p) {
   const int64_t Hkv = kcache->shape[2];
   p->mla = vcache == nullptr;
   if (p->mla) {
-    p->nsplit = mla_nsplit(B, max_len);
+    p->nsplit = mla_nsplit(rows, max_len);
   } else {
-    p->nsplit = gqa_nsplit(B * Hkv, max_len);
+    p->nsplit = gqa_nsplit(rows * Hkv, max_len);
   }
-  (void)Hq;
   return CPA_OK;
 }
 
-}  // namespace
-
-extern "C" size_t attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t head_dim_v,
-                                             int64_t max_shard_len) {
-  // MLA is recognised by its value width; GQA uses the general split rule
-  // (the GQA rule picks fewer splits for more kv heads, so Hkv = 1 bounds it)
-  const int ns = head_dim_v == 512 ? mla_nsplit(batch, max_shard_len) : gqa_nsplit(batch, max_shard_len);
-  return decode_ws_bytes(batch, n_heads_q, head_dim_v, ns);
-}
-
-extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* kcache,
-                                        const cpa_tensor* vcache, const cpa_tensor* kv_scale,
-                                        const int32_t* kv_begin, const int32_t* kv_end,
-                                        int64_t max_shard_len, float softmax_scale,
-                                        const cpa_tensor* o_part, const cpa_tensor* lse_part,
-                                        void* workspace, size_t ws_bytes, void* stream) {
-  cpa::clear_error();
+// Shared decode path. q is the [B, Hq, Dqk] view of query row 0 of every
+// request; a request has Q query rows, q_q elements apart. o_part / lse_part
+// are [B * Q, Hq, Dv] / [B * Q, Hq] (row b * Q + k) and kv_end has B * Q
+// entries; kv_begin has B.
+cpa_status decode_impl(const cpa_tensor* q, int64_t Q, int64_t q_q, const cpa_tensor* kcache,
+                       const cpa_tensor* vcache, const cpa_tensor* kv_scale, const int32_t* kv_begin,
+                       const int32_t* kv_end, int64_t max_shard_len, float softmax_scale, const cpa_tensor* o_part,
+                       const cpa_tensor* lse_part, void* workspace, size_t ws_bytes, void* stream) {
   CPA_TRY(check_tensor(q, "decode q", (1u << CPA_F32) | (1u << CPA_BF16), 3));
   CPA_TRY(check_tensor(kcache, "decode kcache", (1u << CPA_F32) | (1u << CPA_BF16) | (1u << CPA_FP8_E4M3), 4));
   CPA_TRY(check_tensor(o_part, "decode o_part", 1u << CPA_F32, 3));
@@ -231,7 +221,8 @@ extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* k
   if (kcache->shape[0] != B || kcache->shape[3] != Dqk)
     return fail(CPA_E_INVAL, "decode: kcache must be [B, Lmax, Hkv, Dqk] matching q");
   if (Hkv < 1 || Hq % Hkv) return fail(CPA_E_INVAL, "decode: Hq = %lld not a multiple of Hkv = %lld", (long long)Hq, (long long)Hkv);
-  if (Lmax > INT32_MAX || B > INT32_MAX) return fail(CPA_E_INVAL, "decode: sizes too large");
+  if (Lmax > INT32_MAX || B * Q > INT32_MAX) return fail(CPA_E_INVAL, "decode: sizes too large");
+  const int64_t R = B * Q;  // output rows
   if (max_shard_len < 0) return fail(CPA_E_INVAL, "decode: max_shard_len < 0");
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(CPA_E_INVAL, "decode: softmax_scale must be finite and > 0");
@@ -268,20 +259,25 @@ extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* k
   } else if (kv_scale != nullptr && kv_scale->data != nullptr) {
     return fail(CPA_E_INVAL, "decode: kv_scale is only for an FP8 cache");
   }
-  if (o_part->shape[0] != B || o_part->shape[1] != Hq || o_part->shape[2] != Dv)
-    return fail(CPA_E_INVAL, "decode: o_part must be [B, Hq, Dv]");
-  if (lse_part->shape[0] != B || lse_part->shape[1] != Hq) return fail(CPA_E_INVAL, "decode: lse_part must be [B, Hq]");
+  if (o_part->shape[0] != R || o_part->shape[1] != Hq || o_part->shape[2] != Dv)
+    return fail(CPA_E_INVAL, "decode: o_part must be [B, (Q,) Hq, Dv]");
+  if (lse_part->shape[0] != R || lse_part->shape[1] != Hq)
+    return fail(CPA_E_INVAL, "decode: lse_part must be [B, (Q,) Hq]");
   if (B == 0 || Hq == 0) return CPA_OK;
 
   DecodePlan p{};
-  CPA_TRY(decode_plan(q, kcache, vcache, max_shard_len, &p));
-  const size_t need = decode_ws_bytes(B, Hq, Dv, p.nsplit);
+  CPA_TRY(decode_plan(R, kcache, vcache, max_shard_len, &p));
+  // workgroups: (row, split) for MLA (rounded up to whole groups of 8 units),
+  // (row, kv head, split) for GQA
+  const int64_t n_wg = p.mla ? ((B * p.nsplit + 7) / 8 * 8 * Q) : R * Hkv * p.nsplit;
+  if (n_wg > INT32_MAX) return fail(CPA_E_INVAL, "decode: %lld workgroups exceed the grid limit", (long long)n_wg);
+  const size_t need = decode_ws_bytes(R, Hq, Dv, p.nsplit);
   if (ws_bytes < need || (need > 0 && workspace == nullptr))
     return fail(CPA_E_CAPACITY, "decode: workspace of %zu bytes needed, %zu given", need, ws_bytes);
   if (need > 0 && ((uintptr_t)workspace) % 256) return fail(CPA_E_INVAL, "decode: workspace must be 256-byte aligned");
 
   // partial-state destination: the caller's buffers directly, or the split
-  // scratch [nsplit, B, Hq, Dv] + [nsplit, B, Hq] followed by a merge
+  // scratch [nsplit, B * Q, Hq, Dv] + [nsplit, B * Q, Hq] followed by a merge
   float* po;
   float* pl;
   int64_t po_s, po_b, po_h, pl_s, pl_b, pl_h;
@@ -292,10 +288,10 @@ extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* k
     pl_s = 0, pl_b = lse_part->stride[0], pl_h = lse_part->stride[1];
   } else {
     po = static_cast<float*>(workspace);
-    const size_t o_bytes = (size_t)p.nsplit * B * Hq * Dv * sizeof(float);
+    const size_t o_bytes = (size_t)p.nsplit * R * Hq * Dv * sizeof(float);
     pl = reinterpret_cast<float*>(static_cast<char*>(workspace) + (o_bytes + 255) / 256 * 256);
-    po_h = Dv, po_b = Hq * Dv, po_s = B * Hq * Dv;
-    pl_h = 1, pl_b = Hq, pl_s = B * Hq;
+    po_h = Dv, po_b = Hq * Dv, po_s = R * Hq * Dv;
+    pl_h = 1, pl_b = Hq, pl_s = R * Hq;
   }
 
   int err;
@@ -322,6 +318,8 @@ extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* k
     a.nsplit = p.nsplit;
     a.fp8 = fp8;
     a.scale_log2 = softmax_scale * kLog2e;
+    a.Q = (int32_t)Q;
+    a.q_q = q_q;
     err = cpa::launch_decode_mla(a, stream);
   } else {
     cpa::DecodeGqaArgs a{};
@@ -347,6 +345,8 @@ extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* k
     a.q_bf16 = q->dtype == CPA_BF16;
     a.kv_dtype = kcache->dtype;
     a.scale_log2 = softmax_scale * kLog2e;
+    a.Q = (int32_t)Q;
+    a.q_q = q_q;
     err = cpa::launch_decode_gqa(a, stream);
   }
   CPA_TRY(hip_status(err, "decode launch"));
@@ -361,13 +361,69 @@ extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* k
     m.out_n = o_part->stride[0], m.out_h = o_part->stride[1];
     m.lo_n = lse_part->stride[0], m.lo_h = lse_part->stride[1];
     m.S = p.nsplit;
-    m.N = (int32_t)B;
+    m.N = (int32_t)R;
     m.H = (int32_t)Hq;
     m.Dv = (int32_t)Dv;
     m.out_bf16 = 0;
     CPA_TRY(hip_status(cpa::launch_merge(m, stream), "decode split merge launch"));
   }
   return CPA_OK;
+}
+
+}  // namespace
+
+extern "C" size_t attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t head_dim_v,
+                                             int64_t max_shard_len) {
+  // MLA is recognised by its value width; GQA uses the general split rule
+  // (the GQA rule picks fewer splits for more kv heads, so Hkv = 1 bounds it)
+  const int ns = head_dim_v == 512 ? mla_nsplit(batch, max_shard_len) : gqa_nsplit(batch, max_shard_len);
+  return decode_ws_bytes(batch, n_heads_q, head_dim_v, ns);
+}
+
+extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* kcache,
+                                        const cpa_tensor* vcache, const cpa_tensor* kv_scale,
+                                        const int32_t* kv_begin, const int32_t* kv_end,
+                                        int64_t max_shard_len, float softmax_scale,
+                                        const cpa_tensor* o_part, const cpa_tensor* lse_part,
+                                        void* workspace, size_t ws_bytes, void* stream) {
+  cpa::clear_error();
+  return decode_impl(q, 1, 0, kcache, vcache, kv_scale, kv_begin, kv_end, max_shard_len, softmax_scale, o_part,
+                     lse_part, workspace, ws_bytes, stream);
+}
+
+extern "C" cpa_status attn_decode_shard_mq(const cpa_tensor* q, const cpa_tensor* kcache,
+                                           const cpa_tensor* vcache, const cpa_tensor* kv_scale,
+                                           const int32_t* kv_begin, const int32_t* kv_end,
+                                           int64_t max_shard_len, float softmax_scale,
+                                           const cpa_tensor* o_part, const cpa_tensor* lse_part,
+                                           void* workspace, size_t ws_bytes, void* stream) {
+  cpa::clear_error();
+  CPA_TRY(check_tensor(q, "decode_mq q", (1u << CPA_F32) | (1u << CPA_BF16), 4));
+  CPA_TRY(check_tensor(o_part, "decode_mq o_part", 1u << CPA_F32, 4));
+  CPA_TRY(check_tensor(lse_part, "decode_mq lse_part", 1u << CPA_F32, 3, 0));
+  const int64_t B = q->shape[0], Q = q->shape[1];
+  if (Q < 1 || Q > 64) return fail(CPA_E_INVAL, "decode_mq: Q = %lld query rows per request, must be in [1, 64]", (long long)Q);
+  if (o_part->shape[0] != B || o_part->shape[1] != Q || lse_part->shape[0] != B || lse_part->shape[1] != Q)
+    return fail(CPA_E_INVAL, "decode_mq: o_part / lse_part must be [B, Q, ...] matching q");
+  // (request, query row) of the outputs collapse into one row index b * Q + k
+  const int64_t o_row = Q > 1 ? o_part->stride[1] : o_part->stride[0];
+  const int64_t l_row = Q > 1 ? lse_part->stride[1] : lse_part->stride[0];
+  if (B > 1 && Q > 1 && (o_part->stride[0] != Q * o_row || lse_part->stride[0] != Q * l_row))
+    return fail(CPA_E_INVAL, "decode_mq: o_part / lse_part must have stride[0] == Q * stride[1]");
+  cpa_tensor q3 = *q, o3 = *o_part, l2 = *lse_part;
+  q3.ndim = 3;
+  q3.shape[1] = q->shape[2], q3.shape[2] = q->shape[3];
+  q3.stride[1] = q->stride[2], q3.stride[2] = q->stride[3];
+  o3.ndim = 3;
+  o3.shape[0] = B * Q, o3.shape[1] = o_part->shape[2], o3.shape[2] = o_part->shape[3];
+  o3.stride[0] = o_row, o3.stride[1] = o_part->stride[2], o3.stride[2] = o_part->stride[3];
+  o3.stride[3] = 0;
+  l2.ndim = 2;
+  l2.shape[0] = B * Q, l2.shape[1] = lse_part->shape[2];
+  l2.stride[0] = l_row, l2.stride[1] = lse_part->stride[2];
+  // query rows of one request may sit at any (aligned) stride from each other
+  return decode_impl(&q3, Q, Q > 1 ? q->stride[1] : 0, kcache, vcache, kv_scale, kv_begin, kv_end, max_shard_len, softmax_scale,
+                     &o3, &l2, workspace, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------- prefill

@@ -6,8 +6,9 @@
 // Parallelism", 4.1 and 5.4: the GQA kv heads are broadcast to their query
 // heads. Query head h reads kv head h / (Hq / Hkv).
 //
-// One workgroup per (request, kv head, split): the G query heads of the
-// group share every K/V tile staged in LDS. Scores, the running max / sum
+// One workgroup per (query row, kv head, split): the G query heads of the
+// group share every K/V tile staged in LDS. A request has Q >= 1 query rows
+// (speculative / MTP decode), each with its own end of range. Scores, the running max / sum
 // and the output accumulators are fp32; the running statistics are kept in
 // the log2 domain (scores pre-multiplied by scale * log2 e) and converted
 // back to a natural-log LSE at the end. A split covers an even share of the
@@ -46,10 +47,11 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(cpa::DecodeGqaArgs
 
   const int split = blockIdx.x % a.nsplit;
   const int kvh = (blockIdx.x / a.nsplit) % a.Hkv;
-  const int b = blockIdx.x / (a.nsplit * a.Hkv);
+  const int row = blockIdx.x / (a.nsplit * a.Hkv);  // output row: query row k of request b
+  const int b = row / a.Q, k = row % a.Q;
   const int tid = threadIdx.x;
 
-  int64_t beg = a.kv_begin[b], end = a.kv_end[b];
+  int64_t beg = a.kv_begin[b], end = a.kv_end[row];
   beg = beg < 0 ? 0 : (beg > a.Lmax ? a.Lmax : beg);
   end = end < beg ? beg : (end > a.Lmax ? a.Lmax : end);
   const int64_t len = end - beg;
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(cpa::DecodeGqaArgs
 
   for (int i = tid; i < G * D; i += kThreads) {
     const int g = i / D, d = i % D;
-    qs[i] = load_elem<kQBf16>(a.q, b * a.q_b + (int64_t)(kvh * G + g) * a.q_h + d);
+    qs[i] = load_elem<kQBf16>(a.q, b * a.q_b + k * a.q_q + (int64_t)(kvh * G + g) * a.q_h + d);
   }
   for (int g = tid; g < G; g += kThreads) {
     m_s[g] = -INFINITY;
@@ -135,14 +137,14 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(cpa::DecodeGqaArgs
       const int g = e / D, d = e % D;
       const float l = l_s[g];
       const int h = kvh * G + g;
-      a.o[split * a.o_s + (int64_t)b * a.o_b + (int64_t)h * a.o_h + d] = l > 0.f ? acc[i] / l : 0.f;
+      a.o[split * a.o_s + (int64_t)row * a.o_b + (int64_t)h * a.o_h + d] = l > 0.f ? acc[i] / l : 0.f;
     }
   }
   for (int g = tid; g < G; g += kThreads) {
     const float l = l_s[g];
     const int h = kvh * G + g;
     // natural-log LSE from the log2-domain statistics
-    a.lse[split * a.l_s + (int64_t)b * a.l_b + (int64_t)h * a.l_h] =
+    a.lse[split * a.l_s + (int64_t)row * a.l_b + (int64_t)h * a.l_h] =
         l > 0.f ? (m_s[g] + log2f(l)) * 0.69314718055994531f : -INFINITY;
   }
 }
@@ -155,7 +157,7 @@ int launch_decode_gqa(const DecodeGqaArgs& a, void* stream) {
   const int G = a.Hq / a.Hkv;
   const size_t smem = sizeof(float) * ((size_t)G * a.D + 2 * (size_t)kTile * (a.D + 1) +
                                        (size_t)G * kTile + 3 * (size_t)G);
-  const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * a.nsplit));
+  const dim3 grid((unsigned)((int64_t)a.B * a.Q * a.Hkv * a.nsplit));
   hipStream_t st = (hipStream_t)stream;
   auto go = [&](auto kernel) {
     if (smem > 65536) {

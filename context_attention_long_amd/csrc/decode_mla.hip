@@ -20,19 +20,29 @@ namespace {
 
 using namespace cpa::mla;
 
-template <bool kFp8>
+// kP: kStream (one query row per request: every cache byte is read once) or
+// kReuse (several query rows read each tile through the shared L2).
+template <bool kFp8, cpa::Policy kP>
 __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
   __shared__ float alpha_s[2 * kH], lsum_s[kH];
   const Lds S{smem, plds, alpha_s, lsum_s};
 
-  const int split = blockIdx.x % a.nsplit;
-  const int b = blockIdx.x / a.nsplit;
+  // unit u = (request, split); its Q query rows run as Q workgroups with
+  // block indices 8 apart, so they share an XCD (block index mod 8) and its
+  // L2, start together and walk the tiles in the same (rotated) order: one
+  // fetch of a tile from HBM serves all rows
+  const int u = (int)(blockIdx.x / (8 * a.Q)) * 8 + (int)(blockIdx.x % 8);
+  const int k = (int)(blockIdx.x / 8) % a.Q;
+  if (u >= a.B * a.nsplit) return;
+  const int split = u % a.nsplit;
+  const int b = u / a.nsplit;
+  const int row = b * a.Q + k;  // output row
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
 
-  int64_t beg = a.kv_begin[b], end = a.kv_end[b];
+  int64_t beg = a.kv_begin[b], end = a.kv_end[row];
   beg = beg < 0 ? 0 : (beg > a.Lmax ? a.Lmax : beg);
   end = end < beg ? beg : (end > a.Lmax ? a.Lmax : end);
   const int64_t len = end - beg;
@@ -40,29 +50,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
   const int64_t t1 = beg + len * (split + 1) / a.nsplit;
 
   bf16x8 qreg[kQSteps];
-  load_q(a.q + (int64_t)b * a.q_b + (int64_t)(16 * w + c) * a.q_h, g, qreg);
+  load_q(a.q + (int64_t)b * a.q_b + (int64_t)k * a.q_q + (int64_t)(16 * w + c) * a.q_h, g, qreg);
   State st;
   init_state(st);
   const LdsBases L = lds_bases(w, g, c);
 
   if constexpr (kFp8)
-    run_fp8(reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, a.kv_scale + (int64_t)b * a.s_b,
-            a.s_t, t0, t1, w, g, c, L, qreg, a.scale_log2, st, S, blockIdx.x * 2654435761u >> 7);
+    run_fp8<kP>(reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, a.kv_scale + (int64_t)b * a.s_b,
+            a.s_t, t0, t1, w, g, c, L, qreg, a.scale_log2, st, S, (unsigned)u * 2654435761u >> 7);
   else
-    run_bf16<cpa::Policy::kStream>(reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, t0, t1, w,
-                                   g, c, L, qreg, a.scale_log2, st, S, blockIdx.x * 2654435761u >> 7);
+    run_bf16<kP>(reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, t0, t1, w, g, c, L, qreg,
+                 a.scale_log2, st, S, (unsigned)u * 2654435761u >> 7);
 
   // ---- split result: LSE of the QK-role head, normalised O of the PV-role dims ----
   const float l = finish(st, w, g, c, S);
   if (g == 0)
-    a.lse[(int64_t)split * a.l_s + (int64_t)b * a.l_b + (int64_t)(16 * w + c) * a.l_h] =
+    a.lse[(int64_t)split * a.l_s + (int64_t)row * a.l_b + (int64_t)(16 * w + c) * a.l_h] =
         l > 0.f ? (st.m_run + log2f(l)) * kLn2 : -INFINITY;
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
     const int head = 16 * hb + c;
     const float lh = lsum_s[head];
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
-    float* op = a.o + (int64_t)split * a.o_s + (int64_t)b * a.o_b + (int64_t)head * a.o_h + 128 * w + 4 * g;
+    float* op = a.o + (int64_t)split * a.o_s + (int64_t)row * a.o_b + (int64_t)head * a.o_h + 128 * w + 4 * g;
 #pragma unroll
     for (int m = 0; m < kMv; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = st.oacc[m][hb] * inv;
   }
@@ -73,11 +83,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
 namespace cpa {
 
 int launch_decode_mla(const DecodeMlaArgs& a, void* stream) {
-  const dim3 grid((unsigned)((int64_t)a.B * a.nsplit));
-  if (a.fp8)
-    hipLaunchKernelGGL(decode_mla_kernel<true>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
+  const dim3 grid((unsigned)(((int64_t)a.B * a.nsplit + 7) / 8 * 8 * a.Q));
+  constexpr auto kS = Policy::kStream, kR = Policy::kReuse;
+  hipStream_t st = (hipStream_t)stream;
+  if (a.fp8 && a.Q == 1)
+    hipLaunchKernelGGL((decode_mla_kernel<true, kS>), grid, dim3(kThreads), 0, st, a);
+  else if (a.fp8)
+    hipLaunchKernelGGL((decode_mla_kernel<true, kR>), grid, dim3(kThreads), 0, st, a);
+  else if (a.Q == 1)
+    hipLaunchKernelGGL((decode_mla_kernel<false, kS>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(decode_mla_kernel<false>, grid, dim3(kThreads), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((decode_mla_kernel<false, kR>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -45,6 +45,11 @@ struct DecodeGqaArgs {
   int32_t B, Hq, Hkv, D, Lmax, nsplit;
   int32_t q_bf16, kv_dtype;
   float scale_log2;             // softmax scale * log2(e)
+  // Q query rows per request (speculative / MTP decode): row k of request b
+  // is q + b*q_b + k*q_q, reads [kv_begin[b], kv_end[b*Q + k]) and writes
+  // output row b*Q + k (strides o_b / l_b then step one row).
+  int32_t Q;
+  int64_t q_q;
 };
 
 struct DecodeMlaArgs {
@@ -63,6 +68,9 @@ struct DecodeMlaArgs {
   int32_t B, H, Lmax, nsplit;
   int32_t fp8;
   float scale_log2;
+  // Q query rows per request, as in DecodeGqaArgs.
+  int32_t Q;
+  int64_t q_q;
 };
 
 struct PrefillGqaArgs {

@@ -477,7 +477,10 @@ __device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int6
 // position, and its register is refilled with tile i+4. Three bf16 stages:
 // tile i (PV), tile i+1 (QK), tile i+2 (being written). The scales are
 // loaded into registers one step ahead of the softmax that folds them in.
-// Tile order rotated as in run_bf16.
+// Tile order rotated as in run_bf16. kPol = kStream marks the loads
+// nontemporal (a range read once), kReuse leaves them cached (a range other
+// workgroups read too).
+template <Policy kPol = Policy::kStream>
 __device__ __forceinline__ void run_fp8(const uint8_t* base, int64_t c_t, const float* sbase, int64_t s_t, int64_t t0,
                                         int64_t t1, int w, int g, int c, const LdsBases& L,
                                         const bf16x8 (&qreg)[kQSteps], float scale_log2, State& st, const Lds& S,
@@ -513,7 +516,10 @@ __device__ __forceinline__ void run_fp8(const uint8_t* base, int64_t c_t, const 
     const int lim = (int)min((int64_t)(kBN - 1), t1 - 1 - tok0);
     const uint8_t* tb = base + tok0 * c_t;
     const uint32_t off = (uint32_t)min(urow[j], lim) * ct32 + goff[j];
-    r = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tb + off));
+    if constexpr (kPol == Policy::kStream)
+      r = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tb + off));
+    else
+      r = *reinterpret_cast<const u32x2*>(tb + off);
   };
   auto load_scales = [&](int i, TokScale& ts) {
     const int64_t tok0 = t0 + (int64_t)phys(i) * kBN;
@@ -521,7 +527,10 @@ __device__ __forceinline__ void run_fp8(const uint8_t* base, int64_t c_t, const 
     const float* sb = sbase + tok0 * s_t;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      ts.v[j] = __builtin_nontemporal_load(sb + (uint32_t)min(16 * (j >> 2) + 4 * g + (j & 3), lim) * st32);
+      if constexpr (kPol == Policy::kStream)
+        ts.v[j] = __builtin_nontemporal_load(sb + (uint32_t)min(16 * (j >> 2) + 4 * g + (j & 3), lim) * st32);
+      else
+        ts.v[j] = sb[(uint32_t)min(16 * (j >> 2) + 4 * g + (j & 3), lim) * st32];
   };
   auto convert_unit = [&](const u32x2& r, int j, char* tile) {
     const uint32_t o0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, false));

@@ -227,3 +227,56 @@ extern "C" cpa_status cp_plan_round_robin(int32_t C, int32_t rank, int32_t n_req
   if (max_local_rows) *max_local_rows = mx;
   return CPA_OK;
 }
+
+// Multi-query decode ranges: the Q query rows of a request are its last Q
+// slots (draft tokens already stored in the cache), and row k at slot
+// p = L - Q + k reads the slots [0, p] (causal attention, "How GPUs Share a
+// Long Context During LLM Inference", 1.1). On a rank this is the part of
+// [0, p] the rank stores: for contiguous shards ("Decode Context
+// Parallelism" post, 4) the prefix of the rank's chunk up to p, for
+// round-robin storage (Long Context 3.1) its own slots <= p after the
+// replicated rows, which every row sees.
+extern "C" cpa_status cp_plan_multi_query(int32_t layout, int32_t C, int32_t rank, int32_t n_req,
+                                          const int64_t* ctx_len, int32_t Q, int32_t n_repl, int32_t repl_rank,
+                                          int32_t* kv_begin, int32_t* kv_end, int64_t* max_local_rows) {
+  cpa::clear_error();
+  if (layout != CPA_LAYOUT_CONTIGUOUS && layout != CPA_LAYOUT_ROUND_ROBIN)
+    return cpa::fail(CPA_E_INVAL, "multi-query plan: unknown layout %d", layout);
+  if (C < 1) return cpa::fail(CPA_E_INVAL, "multi-query plan: C = %d must be >= 1", C);
+  if (rank < 0 || rank >= C) return cpa::fail(CPA_E_INVAL, "multi-query plan: rank %d not in [0, %d)", rank, C);
+  if (Q < 1) return cpa::fail(CPA_E_INVAL, "multi-query plan: Q = %d must be >= 1", Q);
+  if (n_req < 0 || n_repl < 0) return cpa::fail(CPA_E_INVAL, "multi-query plan: negative n_req or n_repl");
+  if (layout == CPA_LAYOUT_CONTIGUOUS && (n_repl != 0 || repl_rank != 0))
+    return cpa::fail(CPA_E_INVAL, "multi-query plan: contiguous shards take no replicated rows");
+  if (repl_rank < 0 || repl_rank >= C)
+    return cpa::fail(CPA_E_INVAL, "multi-query plan: repl_rank %d not in [0, %d)", repl_rank, C);
+  if (n_req > 0 && (!ctx_len || !kv_begin || !kv_end)) return cpa::fail(CPA_E_INVAL, "multi-query plan: NULL array");
+  int64_t mx = layout == CPA_LAYOUT_ROUND_ROBIN ? n_repl : 0;
+  for (int32_t b = 0; b < n_req; ++b) {
+    const int64_t L = ctx_len[b];
+    if (L < Q) return cpa::fail(CPA_E_INVAL, "multi-query plan: request %d stores %lld < Q slots", b, (long long)L);
+    int64_t rows;  // local rows this request needs
+    if (layout == CPA_LAYOUT_CONTIGUOUS) {
+      const int64_t base = L / C, rem = L % C;
+      const int64_t s = rank * base + (rank < rem ? rank : rem);
+      const int64_t e = s + base + (rank < rem ? 1 : 0);
+      rows = e - s;
+      kv_begin[b] = 0;
+      for (int32_t k = 0; k < Q; ++k) {
+        const int64_t lim = L - Q + k + 1;  // slots [0, lim) are visible
+        kv_end[(int64_t)b * Q + k] = (int32_t)((lim < s ? s : (lim > e ? e : lim)) - s);
+      }
+    } else {
+      rows = n_repl + (L > rank ? (L - rank + C - 1) / C : 0);
+      kv_begin[b] = rank == repl_rank ? 0 : n_repl;
+      for (int32_t k = 0; k < Q; ++k) {
+        const int64_t lim = L - Q + k + 1;
+        kv_end[(int64_t)b * Q + k] = (int32_t)(n_repl + (lim > rank ? (lim - rank + C - 1) / C : 0));
+      }
+    }
+    if (rows > INT32_MAX) return cpa::fail(CPA_E_INVAL, "multi-query plan: request %d needs more than 2^31-1 rows", b);
+    mx = rows > mx ? rows : mx;
+  }
+  if (max_local_rows) *max_local_rows = mx;
+  return CPA_OK;
+}

@@ -197,6 +197,36 @@ cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* kcache, cons
                              size_t ws_bytes, void* stream);
 
 /*
+ * Multi-query split-KV decode (speculative / MTP decode under decode CP:
+ * Long Context 9 lists it; DeepSeek-V4 notes, 11, sweeps the query/spec
+ * width 1, 2, 4, 8). Request b has Q query rows; row k attends cache rows
+ * [kv_begin[b], kv_end[b*Q + k]) of its request -- causal among the draft
+ * rows when the ends come from cp_plan_multi_query -- exactly as
+ * attn_decode_shard attends its single query.
+ *   q        [B, Q, Hq, Dqk]       bf16 or f32 (strides free, 16-byte aligned)
+ *   kcache, vcache, kv_scale, max_shard_len, softmax_scale: as for
+ *                                  attn_decode_shard
+ *   kv_begin [B] int32, kv_end [B*Q] int32   DEVICE arrays, clamped to
+ *                                  [0, Lmax]; an empty range gives O = 0,
+ *                                  LSE = -inf
+ *   o_part   [B, Q, Hq, Dv] f32, lse_part [B, Q, Hq] f32; for B > 1 and
+ *            Q > 1 stride[0] must equal Q * stride[1] (the (b, k) pair is
+ *            addressed as one row b*Q + k)
+ *   workspace / ws_bytes           at least attn_decode_workspace_size(B*Q,
+ *                                  Hq, Dv, max_shard_len) bytes
+ * 1 <= Q <= 64. For MLA the Q rows of one (request, split) run as Q
+ * workgroups on one XCD and read each cache tile through its shared L2, so
+ * HBM traffic stays that of one query row. Q = 1 gives the same results as
+ * attn_decode_shard. Errors as for attn_decode_shard, plus CPA_E_INVAL for a
+ * bad Q or mismatched output shapes or strides.
+ */
+cpa_status attn_decode_shard_mq(const cpa_tensor* q, const cpa_tensor* kcache, const cpa_tensor* vcache,
+                                const cpa_tensor* kv_scale, const int32_t* kv_begin,
+                                const int32_t* kv_end, int64_t max_shard_len, float softmax_scale,
+                                const cpa_tensor* o_part, const cpa_tensor* lse_part, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/*
  * Exact LSE merge of S partial states (Long Context 3.3; DeepSeek-V4 notes,
  * section 5): lse = log sum_c exp(lse_c), O = sum_c exp(lse_c - lse) O_c.
  *   o_parts   [S, N, H, Dv] f32
@@ -240,6 +270,35 @@ cpa_status cp_round_robin_slot(int64_t slot, int32_t C, int32_t* rank, int64_t* 
  */
 cpa_status cp_plan_round_robin(int32_t C, int32_t rank, int32_t n_req, const int64_t* ctx_len,
                                int32_t n_repl, int32_t repl_rank, int32_t* kv_begin, int32_t* kv_end,
+                               int64_t* max_local_rows);
+
+/* Cache layouts of decode CP. */
+#define CPA_LAYOUT_CONTIGUOUS 0  /* rank c holds the c-th contiguous chunk (cp_decode_shards) */
+#define CPA_LAYOUT_ROUND_ROBIN 1 /* slot p on rank p % C, row p / C (cp_plan_round_robin) */
+
+/*
+ * cp_plan_multi_query: host, pure. Per-row decode ranges of rank `rank` for
+ * multi-query (speculative / MTP) decode. A request stores ctx_len[b] slots
+ * whose last Q are its query rows (draft tokens already written to the
+ * cache); row k sits at slot p = ctx_len[b] - Q + k and, attention being
+ * causal (Long Context 1.1), sees slots [0, p].
+ *   layout   CPA_LAYOUT_CONTIGUOUS: the rank's local cache holds slots
+ *            [begin, end) of cp_decode_shards(ctx_len[b], C) from row 0;
+ *            kv_begin = 0, kv_end[b*Q + k] = rows of that chunk below p + 1.
+ *            n_repl and repl_rank must be 0.
+ *            CPA_LAYOUT_ROUND_ROBIN: local cache as for cp_plan_round_robin;
+ *            kv_begin as there, kv_end[b*Q + k] = n_repl + own slots <= p
+ *            (replicated rows are seen by every query row).
+ *   ctx_len  [n_req] int64 (>= Q)
+ *   kv_begin [n_req] int32, kv_end [n_req * Q] int32 (out, host)
+ *   max_local_rows  out (may be NULL): rows a local cache needs
+ * Merging the C ranks' attn_decode_shard_mq states with attn_merge_states
+ * gives each query row causal attention over its request. CPA_E_INVAL on a
+ * bad layout, C, rank, Q < 1, repl_rank, a length below Q, NULL arrays or a
+ * range past 2^31-1.
+ */
+cpa_status cp_plan_multi_query(int32_t layout, int32_t C, int32_t rank, int32_t n_req, const int64_t* ctx_len,
+                               int32_t Q, int32_t n_repl, int32_t repl_rank, int32_t* kv_begin, int32_t* kv_end,
                                int64_t* max_local_rows);
 
 /*

@@ -81,3 +81,29 @@ def test_round_robin_plan_rejects_bad_arguments():
         cpa.cp_plan_round_robin(2, 0, [3], 1, 2)
     with pytest.raises(cpa.CpaError):
         cpa.cp_round_robin_slot(-1, 4)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "round_robin"])
+def test_multi_query_plan_bit_exact(layout):
+    code = cpa.CPA_LAYOUT_CONTIGUOUS if layout == "contiguous" else cpa.CPA_LAYOUT_ROUND_ROBIN
+    for Q in (1, 2, 3, 4, 8):
+        ctx = [Q, Q + 1, Q + 6, 31 + Q, 100]
+        for C in (1, 2, 3, 4, 8):
+            for n_repl, owner in ([(0, 0)] if layout == "contiguous" else [(0, 0), (2, 0), (3, 1)]):
+                if owner >= C:
+                    continue
+                for r in range(C):
+                    beg, end, mx = cpa.cp_plan_multi_query(code, C, r, ctx, Q, n_repl, owner)
+                    rb, re = plans.plan_multi_query(layout, C, r, ctx, Q, n_repl, owner)
+                    assert np.array_equal(beg, rb) and np.array_equal(end, re)
+                    # the last row sees the whole local request: its end bounds the cache rows
+                    assert mx == max([n_repl] + list(re.reshape(len(ctx), Q)[:, -1]))
+
+
+def test_multi_query_plan_rejects_bad_arguments():
+    C_, R_ = cpa.CPA_LAYOUT_CONTIGUOUS, cpa.CPA_LAYOUT_ROUND_ROBIN
+    for args in ((C_, 2, 0, [3], 4), (C_, 2, 0, [8], 0), (C_, 2, 0, [8], 2, 1), (C_, 2, 0, [8], 2, 0, 1),
+                 (7, 2, 0, [8], 2), (R_, 2, 2, [8], 2), (R_, 2, 0, [8], 2, 1, 2), (R_, 0, 0, [8], 2),
+                 (R_, 2, 0, [8], 2, -1)):
+        with pytest.raises(cpa.CpaError):
+            cpa.cp_plan_multi_query(*args)
