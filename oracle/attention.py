@@ -190,6 +190,51 @@ def decode_shard_mq(q, kcache, begin, end, scale, vcache=None, dv=None, decode=N
     return np.stack([o for o, _ in outs], axis=1), np.stack([l for _, l in outs], axis=1)
 
 
+def sparse_mla(q, cache, idx, scale, n_idx=None, req=None, dv=512, decode=None, kv_scale=None, rows=None):
+    """Sparse (top-k index list) MLA attention: query n attends only the
+    cache rows its list names -- *Long Context* 2.4: every query of a sparse
+    attention model comes with its own list of selected tokens; vLLM GLM-5.3
+    post, footnote 1: each query reads its 2,048 selected latent rows (QK over
+    576 dims, PV over 512) for all heads.
+
+    q      [N, H, 576]
+    cache  [B, Lmax, 1, 576] (decode turns stored bits into float64;
+           kv_scale [B, Lmax] multiplies FP8 entries, as in decode_shard)
+    idx    [N, K] integer rows of request req[n]'s cache (req=None: n)
+    n_idx  [N] or None: only the first n_idx[n] entries of row n count
+    Reading taken where the pages are silent: an entry outside [0, Lmax) is
+    no selection (padding) and is skipped; an entry listed twice counts twice
+    (a top-k list has none). Returns O [N, H, dv], LSE [N, H]."""
+    q = np.asarray(q, dtype=np.float64)
+    N, Hq, _ = q.shape
+    Lmax = cache.shape[1]
+    idx = np.asarray(idx)
+    O = np.zeros((N, Hq, dv))
+    L = np.full((N, Hq), _NEG_INF)
+    for n in (range(N) if rows is None else rows):
+        b = n if req is None else int(req[n])
+        k = idx.shape[1] if n_idx is None else max(0, min(int(n_idx[n]), idx.shape[1]))
+        sel = [int(t) for t in idx[n, :k] if 0 <= int(t) < Lmax]
+        if not sel:
+            continue
+        keys = _f64(cache[b, sel], decode)[:, 0, :]           # [n_sel, 576]
+        if kv_scale is not None:
+            keys = keys * np.asarray(kv_scale[b, sel], np.float32).astype(np.float64)[:, None]
+        for h in range(Hq):
+            O[n, h], L[n, h] = attend(q[n, h], keys, keys[:, :dv], scale)
+    return O, L
+
+
+def sparse_mla_cost(k_rows, heads, row_bytes, q_out_bytes_per_head=2176, flops_per_row_head=2176):
+    """Per-query work of sparse MLA attention as the vLLM GLM-5.3 post,
+    footnote 1, counts it: k_rows selected rows of row_bytes each (cache entry
+    plus its index), q_out_bytes_per_head of BF16 query and output per head,
+    flops_per_row_head FLOPs per row and head. Returns (flops, bytes)."""
+    flops = k_rows * heads * flops_per_row_head
+    nbytes = k_rows * row_bytes + heads * q_out_bytes_per_head
+    return flops, nbytes
+
+
 def merge_states(o_parts, lse_parts):
     """Exact LSE merge of S partial states. o_parts [S, ..., Dv],
     lse_parts [S, ...]. A state with lse = -inf carries no mass; if every
