@@ -203,8 +203,9 @@ def sparse_mla(q, cache, idx, scale, n_idx=None, req=None, dv=512, decode=None, 
     idx    [N, K] integer rows of request req[n]'s cache (req=None: n)
     n_idx  [N] or None: only the first n_idx[n] entries of row n count
     Reading taken where the pages are silent: an entry outside [0, Lmax) is
-    no selection (padding) and is skipped; an entry listed twice counts twice
-    (a top-k list has none). Returns O [N, H, dv], LSE [N, H]."""
+    no selection (padding) and is skipped, and so is every entry of a query
+    whose request is outside [0, B); an entry listed twice counts twice (a
+    top-k list has none). Returns O [N, H, dv], LSE [N, H]."""
     q = np.asarray(q, dtype=np.float64)
     N, Hq, _ = q.shape
     Lmax = cache.shape[1]
@@ -214,7 +215,7 @@ def sparse_mla(q, cache, idx, scale, n_idx=None, req=None, dv=512, decode=None, 
     for n in (range(N) if rows is None else rows):
         b = n if req is None else int(req[n])
         k = idx.shape[1] if n_idx is None else max(0, min(int(n_idx[n]), idx.shape[1]))
-        sel = [int(t) for t in idx[n, :k] if 0 <= int(t) < Lmax]
+        sel = [int(t) for t in idx[n, :k] if 0 <= int(t) < Lmax] if 0 <= b < cache.shape[0] else []
         if not sel:
             continue
         keys = _f64(cache[b, sel], decode)[:, 0, :]           # [n_sel, 576]

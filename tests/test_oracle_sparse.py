@@ -120,3 +120,11 @@ def test_owner_local_lists_merge_to_the_full_list(C):
         ls_.append(pl)
     mo, ml = att.merge_states(np.stack(os_), np.stack(ls_))
     assert np.allclose(mo, o, atol=1e-12) and np.allclose(ml, l, atol=1e-12)
+
+
+def test_query_of_an_unknown_request_selects_nothing():
+    rng, q, cache = _rand(7, 2, 2, 20)
+    idx = np.tile(np.arange(20), (2, 1))
+    o, l = att.sparse_mla(q, cache, idx, 0.1, req=[1, 5])
+    ro, rl = att.sparse_mla(q[:1], cache[1:], idx[:1], 0.1)
+    assert np.allclose(o[0], ro[0]) and np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
