@@ -242,7 +242,57 @@ def bench_decode(cpa, torch, synth, steps, warmup, warmup_ms):
     torch.cuda.empty_cache()
     res["round_robin_bf16"] = bench_round_robin(cpa, torch, c, q, cache_bf16, steps, warmup, warmup_ms)
     res["multi_query_bf16"] = bench_multi_query(cpa, torch, synth, c, cache_bf16, 4, steps, warmup, warmup_ms)
+    res["sparse_bf16"] = bench_sparse(cpa, torch, synth, c, cache_bf16, steps, warmup, warmup_ms)
     return res
+
+
+SPARSE_K = 2048
+
+
+def bench_sparse(cpa, torch, synth, c, cache, steps, warmup, warmup_ms):
+    """Sparse (top-k index list) MLA attention on the same latent cache:
+    (a) decode: one query per request, 2,048 rows drawn from its 131072;
+    (b) prefill: 4,096 queries of request 0 at positions 8j (j = 12288 ..
+    16383, an interleave rank's share), each with 2,048 rows drawn from the
+    rows at or below its position. Algorithmic bytes per query: the listed
+    rows (1,152 B) and their 4-byte indices, plus per head the bf16 query
+    (1,152 B), the f32 output (2,048 B) and its LSE; FLOPs: 2,176 per row
+    and head (QK over 576, PV over 512)."""
+    B, L, H = c["B"], c["L"], c["Hq"]
+    dev = cache.device
+    out = {}
+    cases = (("decode", B, None, None), ("prefill", 4096, np.zeros(4096, np.int32),
+                                         8 * np.arange(12288, 16384, dtype=np.int64)))
+    for name, N, req, pos in cases:
+        qb = synth.bf16_normal(3, 5, (N, H, c["Dqk"]))
+        q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(dev)
+        idx, cnt = synth.topk_lists(3, 6 if name == "decode" else 7, N, L, SPARSE_K,
+                                    limit=None if pos is None else pos + 1)
+        idx_d = torch.from_numpy(idx).to(dev)
+        req_d = torch.from_numpy(req).to(dev) if req is not None else None
+        o = torch.empty((N, H, 512), dtype=torch.float32, device=dev)
+        l = torch.empty((N, H), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, cpa.attn_sparse_mla_workspace_size(N, SPARSE_K)), dtype=torch.uint8, device=dev)
+
+        def step():
+            cpa.attn_sparse_mla(q, cache, idx_d, c["scale"], req=req_d, out=o, lse=l, workspace=ws)
+
+        _warm(torch, step, warmup, warmup_ms)
+        n_steps = steps if name == "decode" else max(3, steps // 4)
+        sev = _events(torch, 1)[0]
+        sev[0].record()
+        for _ in range(n_steps):
+            step()
+        sev[1].record()
+        torch.cuda.synchronize()
+        ms = sev[0].elapsed_time(sev[1]) / n_steps
+        rows = int(cnt.sum())
+        nbytes = rows * (1152 + 4) + N * H * (1152 + 2048 + 4)
+        flops = rows * H * 2176
+        out[name] = dict(queries=N, k=SPARSE_K, ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9,
+                         tflops=flops / (ms * 1e-3) / 1e12, algorithmic_bytes=nbytes, flops=flops)
+        del q, idx_d, o, l, ws
+    return out
 
 
 def bench_multi_query(cpa, torch, synth, c, cache, Q, steps, warmup, warmup_ms):
@@ -484,6 +534,9 @@ def main():
             },
             "round_robin_bf16": {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["round_robin_bf16"].items()},
             "frac_of_hbm_peak_step": {k: round(dec[k]["gbs"] / PEAK_HBM_GBS, 4) for k in ("bf16", "fp8", "round_robin_bf16")},
+            "sparse_bf16": {k: dict({kk: round(vv, 4) if isinstance(vv, float) else vv for kk, vv in v.items()},
+                                    frac_of_hbm_peak=round(v["gbs"] / PEAK_HBM_GBS, 4))
+                            for k, v in dec["sparse_bf16"].items()},
             "multi_query_bf16": dict(
                 {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["multi_query_bf16"].items()},
                 workload="4 query rows per request (MTP3), causal among them; same cache and shards",
@@ -494,7 +547,8 @@ def main():
             f"round-robin bf16 {dec['round_robin_bf16']['gbs']:.0f} GB/s/step "
             f"(cache write {dec['round_robin_bf16']['cache_write_gbs']:.0f} GB/s), "
             f"multi-query Q=4 {dec['multi_query_bf16']['gbs']:.0f} GB/s/step, "
-            f"{dec['multi_query_bf16']['tflops']:.0f} TFLOP/s")
+            f"{dec['multi_query_bf16']['tflops']:.0f} TFLOP/s; sparse top-2048 decode "
+            f"{dec['sparse_bf16']['decode']['gbs']:.0f} GB/s, prefill {dec['sparse_bf16']['prefill']['gbs']:.0f} GB/s")
 
     if not args.no_extra_prefill:
         for k, key in ((4, "prefill_mla_zigzag"), (5, "prefill_interleave")):

@@ -57,7 +57,7 @@ assert SEGMENT_DTYPE.itemsize == ctypes.sizeof(CpaSegment) == 32
 SYMBOLS = ("cpa_last_error", "cpa_abi_version", "cp_plan_zigzag", "cp_plan_interleave", "cp_decode_shards",
            "attn_prefill_shard", "attn_decode_workspace_size", "attn_decode_shard", "attn_merge_states",
            "cp_round_robin_slot", "cp_plan_round_robin", "attn_cache_write_round_robin",
-           "attn_decode_shard_mq", "cp_plan_multi_query")
+           "attn_decode_shard_mq", "cp_plan_multi_query", "attn_sparse_mla_workspace_size", "attn_sparse_mla")
 
 _lib_handle = None
 
@@ -95,6 +95,12 @@ def lib():
         L.cp_plan_multi_query.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           P(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           P(ctypes.c_int32), P(ctypes.c_int32), P(ctypes.c_int64)]
+        L.attn_sparse_mla_workspace_size.restype = ctypes.c_size_t
+        L.attn_sparse_mla_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32]
+        L.attn_sparse_mla.restype = ctypes.c_int
+        L.attn_sparse_mla.argtypes = [P(CpaTensor), P(CpaTensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, P(CpaTensor), P(CpaTensor),
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.cp_round_robin_slot.restype = ctypes.c_int
         L.cp_round_robin_slot.argtypes = [ctypes.c_int64, ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int64)]
         L.cp_plan_round_robin.restype = ctypes.c_int
@@ -339,6 +345,43 @@ def attn_decode_shard_mq(q, kcache, vcache, kv_begin, kv_end, max_shard_len, sof
                                       int(max_shard_len), float(softmax_scale), ctypes.byref(do), ctypes.byref(dl),
                                       ctypes.c_void_p(ws_ptr), ws_bytes, _stream(stream)))
     return o_part, lse_part
+
+
+def attn_sparse_mla_workspace_size(n_queries, k):
+    return int(lib().attn_sparse_mla_workspace_size(int(n_queries), int(k)))
+
+
+def attn_sparse_mla(q, cache, idx, softmax_scale, n_idx=None, req=None, out=None, lse=None, workspace=None,
+                    stream=None):
+    """Sparse MLA attention: query n of q [N, 64, 576] bf16 attends the rows
+    idx[n, :n_idx[n]] of request req[n] of cache [B, Lmax, 1, 576] bf16.
+    idx: int32 device tensor [N, k] (last dim contiguous); n_idx / req:
+    int32 device tensors [N] or None. Returns (out [N, 64, 512] f32,
+    lse [N, 64] f32)."""
+    torch = _torch()
+    N = q.shape[0]
+    if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != N or (idx.shape[1] > 1 and idx.stride(1) != 1):
+        raise TypeError("idx must be an int32 tensor [N, k] with a contiguous last dim")
+    for t in (n_idx, req):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != N):
+            raise TypeError("n_idx / req must be contiguous int32 tensors [N]")
+    k = idx.shape[1]
+    if out is None:
+        out = torch.empty((N, 64, 512), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((N, 64), dtype=torch.float32, device=q.device)
+    need = attn_sparse_mla_workspace_size(N, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    dq, dc, do, dl = tensor_desc(q), tensor_desc(cache), tensor_desc(out), tensor_desc(lse)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+    _check(lib().attn_sparse_mla(ctypes.byref(dq), ctypes.byref(dc), ptr(req), ptr(idx),
+                                 int(idx.stride(0)) if N > 0 else int(k), int(k), ptr(n_idx), float(softmax_scale),
+                                 ctypes.byref(do), ctypes.byref(dl), ctypes.c_void_p(ws_ptr), ws_bytes,
+                                 _stream(stream)))
+    return out, lse
 
 
 def attn_merge_states(o_parts, lse_parts, out=None, lse_out=None, out_dtype=None, stream=None):

@@ -426,6 +426,96 @@ extern "C" cpa_status attn_decode_shard_mq(const cpa_tensor* q, const cpa_tensor
                      &o3, &l2, workspace, ws_bytes, stream);
 }
 
+// ----------------------------------------------------------- sparse (top-k)
+
+extern "C" size_t attn_sparse_mla_workspace_size(int64_t n_queries, int32_t k) {
+  return decode_ws_bytes(n_queries, 64, 512, mla_nsplit(n_queries, k));
+}
+
+extern "C" cpa_status attn_sparse_mla(const cpa_tensor* q, const cpa_tensor* cache, const int32_t* req,
+                                      const int32_t* idx, int64_t idx_stride, int32_t k, const int32_t* n_idx,
+                                      float softmax_scale, const cpa_tensor* out, const cpa_tensor* lse,
+                                      void* workspace, size_t ws_bytes, void* stream) {
+  cpa::clear_error();
+  CPA_TRY(check_tensor(q, "sparse q", 1u << CPA_BF16, 3));
+  CPA_TRY(check_tensor(cache, "sparse cache", 1u << CPA_BF16, 4));
+  CPA_TRY(check_tensor(out, "sparse out", 1u << CPA_F32, 3));
+  CPA_TRY(check_tensor(lse, "sparse lse", 1u << CPA_F32, 2, 0));
+  const int64_t N = q->shape[0], B = cache->shape[0], Lmax = cache->shape[1];
+  if (q->shape[1] != 64 || q->shape[2] != 576)
+    return fail(CPA_E_UNSUPPORTED, "sparse: q must be [N, 64, 576] (the MLA kernel's shape)");
+  if (cache->shape[2] != 1 || cache->shape[3] != 576) return fail(CPA_E_INVAL, "sparse: cache must be [B, Lmax, 1, 576]");
+  if (out->shape[0] != N || out->shape[1] != 64 || out->shape[2] != 512)
+    return fail(CPA_E_INVAL, "sparse: out must be [N, 64, 512]");
+  if (lse->shape[0] != N || lse->shape[1] != 64) return fail(CPA_E_INVAL, "sparse: lse must be [N, 64]");
+  if (k < 0 || idx_stride < k) return fail(CPA_E_INVAL, "sparse: k = %d, idx_stride = %lld", k, (long long)idx_stride);
+  if (N > INT32_MAX || B > INT32_MAX || Lmax > INT32_MAX) return fail(CPA_E_INVAL, "sparse: sizes too large");
+  if (N > 0 && k > 0 && idx == nullptr) return fail(CPA_E_INVAL, "sparse: idx is NULL");
+  if (req == nullptr && N > B && Lmax > 0) return fail(CPA_E_INVAL, "sparse: without req, query n uses request n < B");
+  if ((uintptr_t)idx % 4) return fail(CPA_E_INVAL, "sparse: idx must be 4-byte aligned");
+  // rows are addressed with 32-bit byte offsets from the request's base
+  if (Lmax > 0 && (Lmax - 1) * cache->stride[1] * 2 + 2 * 576 > (int64_t)UINT32_MAX)
+    return fail(CPA_E_INVAL, "sparse: a request's cache spans more than 4 GiB");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(CPA_E_INVAL, "sparse: softmax_scale must be finite and > 0");
+  if (N == 0) return CPA_OK;
+  const int ns = mla_nsplit(N, k);
+  if (N * ns > INT32_MAX) return fail(CPA_E_INVAL, "sparse: too many workgroups");
+  const size_t need = decode_ws_bytes(N, 64, 512, ns);
+  if (ws_bytes < need || (need > 0 && workspace == nullptr))
+    return fail(CPA_E_CAPACITY, "sparse: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (need > 0 && ((uintptr_t)workspace) % 256) return fail(CPA_E_INVAL, "sparse: workspace must be 256-byte aligned");
+
+  cpa::SparseMlaArgs a{};
+  float* po;
+  float* pl;
+  if (ns == 1) {
+    po = static_cast<float*>(out->data);
+    pl = static_cast<float*>(lse->data);
+    a.o_s = 0, a.o_n = out->stride[0], a.o_h = out->stride[1];
+    a.l_s = 0, a.l_n = lse->stride[0], a.l_h = lse->stride[1];
+  } else {
+    po = static_cast<float*>(workspace);
+    const size_t o_bytes = (size_t)ns * N * 64 * 512 * sizeof(float);
+    pl = reinterpret_cast<float*>(static_cast<char*>(workspace) + (o_bytes + 255) / 256 * 256);
+    a.o_s = N * 64 * 512, a.o_n = 64 * 512, a.o_h = 512;
+    a.l_s = N * 64, a.l_n = 64, a.l_h = 1;
+  }
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.cache = cache->data;
+  a.req = req;
+  a.idx = idx;
+  a.n_idx = n_idx;
+  a.o = po;
+  a.lse = pl;
+  a.q_n = q->stride[0], a.q_h = q->stride[1];
+  a.c_b = cache->stride[0], a.c_t = cache->stride[1];
+  a.i_n = idx_stride;
+  a.N = (int32_t)N, a.B = (int32_t)B, a.K = k, a.Lmax = (int32_t)Lmax, a.nsplit = ns;
+  // one query per request reads its rows once; several share them through L2
+  a.reuse = req != nullptr;
+  a.scale_log2 = softmax_scale * kLog2e;
+  CPA_TRY(hip_status(cpa::launch_sparse_mla(a, stream), "sparse launch"));
+  if (ns > 1) {
+    cpa::MergeArgs m{};
+    m.o = po;
+    m.lse = pl;
+    m.out = out->data;
+    m.lse_out = static_cast<float*>(lse->data);
+    m.o_s = a.o_s, m.o_n = a.o_n, m.o_h = a.o_h;
+    m.l_s = a.l_s, m.l_n = a.l_n, m.l_h = a.l_h;
+    m.out_n = out->stride[0], m.out_h = out->stride[1];
+    m.lo_n = lse->stride[0], m.lo_h = lse->stride[1];
+    m.S = ns;
+    m.N = (int32_t)N;
+    m.H = 64;
+    m.Dv = 512;
+    m.out_bf16 = 0;
+    CPA_TRY(hip_status(cpa::launch_merge(m, stream), "sparse split merge launch"));
+  }
+  return CPA_OK;
+}
+
 // ------------------------------------------------------------------- prefill
 
 namespace {

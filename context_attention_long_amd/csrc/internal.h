@@ -73,6 +73,24 @@ struct DecodeMlaArgs {
   int64_t q_q;
 };
 
+struct SparseMlaArgs {
+  const uint16_t* q;      // [N, 64, 576] bf16
+  const void* cache;      // [B, Lmax, 576] bf16 words (one kv head)
+  const int32_t* req;     // [N] request of each query, or null (query n -> request n)
+  const int32_t* idx;     // [N, K] selected cache rows
+  const int32_t* n_idx;   // [N] entries that count, or null (all K)
+  float* o;               // [nsplit, N, 64, 512]
+  float* lse;             // [nsplit, N, 64]
+  int64_t q_n, q_h;
+  int64_t c_b, c_t;       // cache strides (elements)
+  int64_t i_n;            // idx row stride (entries)
+  int64_t o_s, o_n, o_h;
+  int64_t l_s, l_n, l_h;
+  int32_t N, B, K, Lmax, nsplit;
+  int32_t reuse;          // several queries share a request's rows: cached loads
+  float scale_log2;
+};
+
 struct PrefillGqaArgs {
   const uint16_t* q;    // [n_local, Hq, 128] bf16
   const uint16_t* k;    // [T_kv, Hkv, 128]
@@ -112,5 +130,6 @@ int launch_decode_mla(const DecodeMlaArgs& a, void* stream);
 int launch_prefill_gqa(const PrefillGqaArgs& a, const cpa_segment* seg, int n_seg, void* stream);
 int launch_prefill_mla(const PrefillMlaArgs& a, const cpa_segment* seg, int n_seg, void* stream);
 int launch_cache_write_rr(const CacheWriteArgs& a, void* stream);
+int launch_sparse_mla(const SparseMlaArgs& a, void* stream);
 
 }  // namespace cpa

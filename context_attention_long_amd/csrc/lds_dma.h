@@ -99,6 +99,16 @@ __device__ __forceinline__ void lds_dma4(const void* gsrc, uint32_t lds_base) {
                  : "memory");
 }
 
+// Same, addressed as a wavefront-uniform base (SGPRs) plus a per-lane 32-bit
+// byte offset.
+template <Policy P = Policy::kReuse>
+__device__ __forceinline__ void lds_dma4_s(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
+  if constexpr (P == Policy::kStream)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1 nt" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+}
+
 // Wait until at most N vector-memory operations of this wavefront are
 // outstanding.
 template <int N>

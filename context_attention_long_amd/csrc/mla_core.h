@@ -262,9 +262,11 @@ struct TokScale {
   float v[8];
 };
 
-template <bool kFp8>
+// kMask: bit t of vmask says whether token t of the tile is a selection
+// (index-list attention); without it the first nvalid tokens are.
+template <bool kFp8, bool kMask = false>
 __device__ __forceinline__ void soft_scores(Soft& sm, const f32x4 (&sacc)[2], int nvalid, int g, float scale_log2,
-                                            const TokScale& ts) {
+                                            const TokScale& ts, uint32_t vmask = 0xffffffffu) {
   sm.mx = -INFINITY;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -273,7 +275,10 @@ __device__ __forceinline__ void soft_scores(Soft& sm, const f32x4 (&sacc)[2], in
       const int t = 16 * mt + 4 * g + i;
       float v = sacc[mt][i] * scale_log2;
       if constexpr (kFp8) v *= ts.v[4 * mt + i];
-      v = (t < nvalid) ? v : -INFINITY;
+      if constexpr (kMask)
+        v = (t < nvalid && ((vmask >> t) & 1u)) ? v : -INFINITY;
+      else
+        v = (t < nvalid) ? v : -INFINITY;
       sm.x[4 * mt + i] = v;
       sm.mx = fmaxf(sm.mx, v);
     }
@@ -289,11 +294,14 @@ __device__ __forceinline__ void soft_ref(Soft& sm, State& st) {
   sm.psum = 0.f;
 }
 
-template <bool kFp8, int J0>
+// kMask: a head may have seen no selected token yet (reference max still
+// -inf, every score -inf); its probabilities are then 0, not -inf - -inf.
+template <bool kFp8, int J0, bool kMask = false>
 __device__ __forceinline__ void soft_exp(Soft& sm, const State& st, const TokScale& ts) {
+  const float mref = (kMask && st.m_run == -INFINITY) ? 0.f : st.m_run;
 #pragma unroll
   for (int j = J0; j < J0 + 4; ++j) {
-    const float p = __builtin_amdgcn_exp2f(sm.x[j] - st.m_run);
+    const float p = __builtin_amdgcn_exp2f(sm.x[j] - mref);
     sm.psum += p;
     sm.pf[j] = kFp8 ? p * ts.v[j] : p;
   }
@@ -321,11 +329,12 @@ __device__ __forceinline__ void interleave_mfma_valu() {
 // ts: the token scales of tile nxt (FP8).
 // pv_hook(m) runs in PV m-step m (the FP8 path converts its next tile there,
 // where the LDS is far less busy than during QK).
-template <bool kNext, bool kFp8 = false, typename Hook, typename PvHook>
+// kMask / vmask: selection bits of tile nxt (see soft_scores).
+template <bool kNext, bool kFp8 = false, bool kMask = false, typename Hook, typename PvHook>
 __device__ __forceinline__ void pipe_step(const char* cur, const char* nxt, int nvalid_nxt, int buf, int w, int g,
                                           int c, const LdsBases& L, const bf16x8 (&qreg)[kQSteps], float scale_log2,
                                           State& st, const Lds& S, Hook&& hook, PvHook&& pv_hook,
-                                          const TokScale& ts = TokScale{}) {
+                                          const TokScale& ts = TokScale{}, uint32_t vmask = 0xffffffffu) {
   constexpr int kAheadV = 4;
   bf16x8 va[kMv];
   auto load_v = [&](int m) {
@@ -372,10 +381,10 @@ __device__ __forceinline__ void pipe_step(const char* cur, const char* nxt, int 
       asm volatile("" : "+a"(st.oacc[m][hb]));
     }
     if constexpr (kNext) {
-      if (m == 0) soft_scores<kFp8>(sm, sacc, nvalid_nxt, g, scale_log2, ts);
+      if (m == 0) soft_scores<kFp8, kMask>(sm, sacc, nvalid_nxt, g, scale_log2, ts, vmask);
       if (m == 1) soft_ref(sm, st);
-      if (m == 2) soft_exp<kFp8, 0>(sm, st, ts);
-      if (m == 3) soft_exp<kFp8, 4>(sm, st, ts);
+      if (m == 2) soft_exp<kFp8, 0, kMask>(sm, st, ts);
+      if (m == 3) soft_exp<kFp8, 4, kMask>(sm, st, ts);
       if (m == 4) soft_store(sm, st, S.p + kH * kPRowBytes * (buf ^ 1), S.alpha + kH * (buf ^ 1), w, g, c);
       if (m <= 4) interleave_mfma_valu<4, 6>();
     }
@@ -604,6 +613,133 @@ __device__ __forceinline__ void run_fp8(const uint8_t* base, int64_t c_t, const 
   __syncthreads();  // P of the last tile visible
   pipe_step<false>(stage(ntiles - 1), nullptr, 0, (ntiles - 1) & 1, w, g, c, L, qreg, scale_log2, st, S, [](int) {},
                    [](int) {});
+}
+
+// ---- index-list (sparse) attention ----
+// The tokens are the cache rows named by entries [0, ntok) of an index list
+// (Long Context 2.4: a sparse-attention query brings its own list). Entry
+// values outside [0, nrows) are no selection: their scores are masked and
+// their loads read row 0. Each wavefront copies the entries of a tile into
+// its own LDS ring slot with one 4-byte-per-lane direct load (lane l: entry
+// l mod 32), five tiles ahead of use, so the index values never pass through
+// registers the compiler would have to wait for. Per step i, in this order:
+// the entries of tile i+5, then the nine row loads of tile i+3 (addresses
+// from the ring, spread over the QK steps of tile i+1). Since vector-memory
+// loads complete in issue order, the wait at the top of step i for tile i+1
+// (at most 1 + 9 loads issued after it) also covers the entries of tiles up
+// to i+3; the ring slot of tile i is rewritten (step i) only after its last
+// readers (the address reads of step i-3, the selection mask of step i-1).
+constexpr int kIdxSlots = 5;
+constexpr int kIdxSlotBytes = 256;                          // 64 lanes x 4 B
+constexpr int kIdxRingBytes = 4 * kIdxSlots * kIdxSlotBytes;  // per workgroup (4 waves)
+
+template <Policy P>
+__device__ __forceinline__ void run_bf16_gather(const uint16_t* base, int64_t c_t, const int32_t* ilist, int ntok,
+                                                int nrows, int w, int g, int c, const LdsBases& L,
+                                                const bf16x8 (&qreg)[kQSteps], float scale_log2, State& st,
+                                                const Lds& S, char* ring, uint32_t rot_seed = 0) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int ntiles = (ntok + kBN - 1) / kBN;
+  if (ntiles <= 0) return;
+  const int rot = (int)(rot_seed % (uint32_t)ntiles);
+  auto phys = [&](int i) { const int t = i + rot; return t >= ntiles ? t - ntiles : t; };
+  auto nvalid = [&](int i) { return min(kBN, ntok - kBN * phys(i)); };
+  const uint32_t rowbytes = (uint32_t)c_t * 2u;  // the host bounds nrows * rowbytes below 2^32
+  // this thread's chunks of a tile: tile row (high half) and swizzled source byte offset
+  uint32_t rinfo[kLdChunks];
+#pragma unroll
+  for (int k = 0; k < kLdChunks; ++k) {
+    const int Pc = tid + kThreads * k;
+    const int row = Pc / kRowChunks, pc = Pc % kRowChunks;
+    rinfo[k] = ((uint32_t)row << 16) | (uint32_t)(swz(row, pc) * 16);
+  }
+  const char* wring = ring + w * (kIdxSlots * kIdxSlotBytes);
+  const uint32_t wring_lds = __builtin_amdgcn_readfirstlane(lds_addr(wring));
+  const uint64_t ibase = uniform_ptr(ilist), cbase = uniform_ptr(base);
+  auto slot = [&](int T) { return (T % kIdxSlots) * kIdxSlotBytes; };
+  auto issue_idx = [&](int T) {
+    const int Tc = T < ntiles ? T : ntiles - 1;  // past the end: re-read the last tile's entries
+    const int e = min(kBN * phys(Tc) + (lane & 31), ntok - 1);
+    lds_dma4_s<Policy::kReuse>(ibase, (uint32_t)e * 4u, wring_lds + (uint32_t)slot(T));
+  };
+  auto row_of = [&](int T, int row) -> uint32_t {
+    const int v = *reinterpret_cast<const int*>(wring + slot(T) + 4 * row);
+    return (uint32_t)v < (uint32_t)nrows ? (uint32_t)v : 0u;
+  };
+  auto offsets = [&](int T, uint32_t (&voff)[kLdChunks]) {
+#pragma unroll
+    for (int k = 0; k < kLdChunks; ++k) voff[k] = row_of(T, (int)(rinfo[k] >> 16)) * rowbytes + (rinfo[k] & 0xffffu);
+  };
+  auto tile_mask = [&](int T) -> uint32_t {
+    const int v = *reinterpret_cast<const int*>(wring + slot(T) + 4 * (lane & 31));
+    return (uint32_t)__ballot((uint32_t)v < (uint32_t)nrows);
+  };
+  auto tile_ptr = [&](int i) -> const char* { return S.tiles + (i & 3) * kTileBytes; };
+  auto dst = [&](int i) {
+    return __builtin_amdgcn_readfirstlane(lds_addr(S.tiles + (i & 3) * kTileBytes + 64 * w * 16));
+  };
+  auto issue_tile = [&](int T) {
+    uint32_t voff[kLdChunks];
+    offsets(T, voff);
+    const uint32_t d = dst(T);
+#pragma unroll
+    for (int k = 0; k < kLdChunks; ++k) lds_dma16_s<P>(cbase, voff[k], d + kThreads * k * 16);
+  };
+  // ---- prologue: entries of tiles 0..4, rows of tiles 0..2 ----
+  issue_idx(0);
+  issue_idx(1);
+  issue_idx(2);
+  cpa::wait_vmcnt<2>();  // entries of tile 0
+  issue_tile(0);
+  issue_idx(3);
+  if (ntiles > 1) {
+    cpa::wait_vmcnt<11>();  // entries of tile 1 (then: 2, rows 0, 3)
+    issue_tile(1);
+  }
+  issue_idx(4);
+  if (ntiles > 2) {
+    cpa::wait_vmcnt<20>();  // entries of tile 2 (then: rows 0, 3, rows 1, 4)
+    issue_tile(2);
+  }
+  // rows of tile 0 landed (after them: entries 3, rows 1, entries 4, rows 2)
+  if (ntiles > 2) cpa::wait_vmcnt<20>();
+  else if (ntiles == 2) cpa::wait_vmcnt<11>();
+  else cpa::wait_vmcnt<2>();
+  __syncthreads();
+  {
+    f32x4 sacc[2];
+    qk_tile(tile_ptr(0), L, qreg, sacc, [](int) {}, [](int) {});
+    Soft sm;
+    const TokScale none{};
+    soft_scores<false, true>(sm, sacc, nvalid(0), g, scale_log2, none, tile_mask(0));
+    soft_ref(sm, st);
+    soft_exp<false, 0, true>(sm, st, none);
+    soft_exp<false, 4, true>(sm, st, none);
+    soft_store(sm, st, S.p, S.alpha, w, g, c);
+  }
+  // ---- steady state ----
+  for (int i = 0; i + 1 < ntiles; ++i) {
+    // rows of tile i+1 landed: after them only the entries of tile i+4 and the rows of tile i+2
+    if (i + 2 < ntiles) cpa::wait_vmcnt<10>();
+    else cpa::wait_vmcnt<1>();
+    __syncthreads();  // P_i and tile i+1 visible; every wave is done with tile i-1 and P_{i-1}
+    issue_idx(i + 5);
+    const bool more = i + 3 < ntiles;
+    uint32_t voff[kLdChunks];
+    offsets(i + 3, voff);
+    const uint32_t ndst = dst(i + 3);
+    pipe_step<true, false, true>(tile_ptr(i), tile_ptr(i + 1), nvalid(i + 1), i & 1, w, g, c, L, qreg, scale_log2,
+                                 st, S,
+                                 [&](int s) {
+                                   if (more && (s & 1) == 0 && (s >> 1) < kLdChunks)
+                                     lds_dma16_s<P>(cbase, voff[s >> 1], ndst + kThreads * (s >> 1) * 16);
+                                 },
+                                 [](int) {}, TokScale{}, tile_mask(i + 1));
+  }
+  __syncthreads();  // P of the last tile visible
+  pipe_step<false>(tile_ptr(ntiles - 1), nullptr, 0, (ntiles - 1) & 1, w, g, c, L, qreg, scale_log2, st, S,
+                   [](int) {}, [](int) {});
+  cpa::wait_vmcnt<0>();  // entry loads issued past the last tile have landed
 }
 
 // Closes the range: the softmax sum of every head into S.lsum (one barrier).

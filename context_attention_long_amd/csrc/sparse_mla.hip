@@ -1,0 +1,83 @@
+// Sparse (top-k index list) MLA attention over a latent cache.
+//
+// What it computes: "How GPUs Share a Long Context During LLM Inference",
+// 2.4 -- a query of a sparse-attention model brings its own list of selected
+// tokens; vLLM GLM-5.3 part 2, footnote 1 -- each query reads its 2,048
+// selected latent rows for all heads (QK over 576 dims, PV over 512). The
+// output is the partial O + LSE of the listed rows, so owner-local lists on
+// several ranks combine with the LSE merge (DeepSeek-V4 notes, 5.2).
+//
+// One workgroup per (query, split): the split's share of the query's list
+// runs through the shared MLA core (mla_core.h, run_bf16_gather), which
+// gathers the listed rows into LDS tiles with direct loads whose addresses
+// come from the list itself (staged in LDS ahead of use). The splits of a
+// query are merged by the LSE merge.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "mla_core.h"
+
+namespace {
+
+using namespace cpa::mla;
+
+template <cpa::Policy kP>
+__global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(cpa::SparseMlaArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
+  __shared__ __attribute__((aligned(16))) char ring[kIdxRingBytes];
+  __shared__ float alpha_s[2 * kH], lsum_s[kH];
+  const Lds S{smem, plds, alpha_s, lsum_s};
+
+  const int split = (int)(blockIdx.x % a.nsplit);
+  const int n = (int)(blockIdx.x / a.nsplit);
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+
+  int b = a.req ? a.req[n] : n;
+  int cnt = a.n_idx ? a.n_idx[n] : a.K;
+  cnt = cnt < 0 ? 0 : (cnt > a.K ? a.K : cnt);
+  if (b < 0 || b >= a.B || a.Lmax <= 0) cnt = 0, b = 0;  // no request or empty cache: nothing selected
+  const int e0 = (int)((int64_t)cnt * split / a.nsplit);
+  const int e1 = (int)((int64_t)cnt * (split + 1) / a.nsplit);
+
+  bf16x8 qreg[kQSteps];
+  load_q(a.q + (int64_t)n * a.q_n + (int64_t)(16 * w + c) * a.q_h, g, qreg);
+  State st;
+  init_state(st);
+  const LdsBases L = lds_bases(w, g, c);
+
+  run_bf16_gather<kP>(reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t,
+                      a.idx + (int64_t)n * a.i_n + e0, e1 - e0, a.Lmax, w, g, c, L, qreg, a.scale_log2, st, S, ring,
+                      blockIdx.x * 2654435761u >> 7);
+
+  const float l = finish(st, w, g, c, S);
+  if (g == 0)
+    a.lse[(int64_t)split * a.l_s + (int64_t)n * a.l_n + (int64_t)(16 * w + c) * a.l_h] =
+        l > 0.f ? (st.m_run + log2f(l)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int head = 16 * hb + c;
+    const float lh = lsum_s[head];
+    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    float* op = a.o + (int64_t)split * a.o_s + (int64_t)n * a.o_n + (int64_t)head * a.o_h + 128 * w + 4 * g;
+#pragma unroll
+    for (int m = 0; m < kMv; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = st.oacc[m][hb] * inv;
+  }
+}
+
+}  // namespace
+
+namespace cpa {
+
+int launch_sparse_mla(const SparseMlaArgs& a, void* stream) {
+  const dim3 grid((unsigned)((int64_t)a.N * a.nsplit));
+  hipStream_t st = (hipStream_t)stream;
+  if (a.reuse)
+    hipLaunchKernelGGL((sparse_mla_kernel<Policy::kReuse>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((sparse_mla_kernel<Policy::kStream>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace cpa

@@ -272,6 +272,36 @@ cpa_status cp_plan_round_robin(int32_t C, int32_t rank, int32_t n_req, const int
                                int32_t n_repl, int32_t repl_rank, int32_t* kv_begin, int32_t* kv_end,
                                int64_t* max_local_rows);
 
+/*
+ * Sparse (top-k index list) MLA attention (Long Context 2.4: a query of a
+ * sparse-attention model brings its own list of selected tokens; vLLM
+ * GLM-5.3 part 2, footnote 1: each query reads its 2,048 selected latent
+ * rows for all 64 heads, QK over 576 dims and PV over 512). Query n attends
+ * the cache rows idx[n, 0 .. n_idx[n]) of request req[n], emitting O and
+ * its LSE, so lists split by owner across ranks combine exactly with
+ * attn_merge_states (DeepSeek-V4 notes, 5.2).
+ *   q       [N, 64, 576] bf16
+ *   cache   [B, Lmax, 1, 576] bf16 (one latent per token)
+ *   req     [N] int32 DEVICE, or NULL: query n uses request n (then N <= B)
+ *   idx     DEVICE int32, row n at idx + n * idx_stride, k entries per row
+ *           (idx_stride >= k); an entry outside [0, Lmax) is no selection
+ *           (padding: skipped); an entry listed twice counts twice
+ *   n_idx   [N] int32 DEVICE, or NULL: only the first n_idx[n] entries of
+ *           row n count (clamped to [0, k))
+ *   out     [N, 64, 512] f32, lse [N, 64] f32; a query with no selection,
+ *           or whose request is outside [0, B), gets O = 0, LSE = -inf
+ *   workspace / ws_bytes: at least attn_sparse_mla_workspace_size(N, k)
+ *           bytes, 256-byte aligned (split states of long lists)
+ * Rows are addressed with 32-bit offsets: one request's cache may span at
+ * most 4 GiB. CPA_E_INVAL / CPA_E_UNSUPPORTED on shapes, dtypes, strides or
+ * sizes outside these; CPA_E_CAPACITY for a short workspace.
+ */
+size_t attn_sparse_mla_workspace_size(int64_t n_queries, int32_t k);
+cpa_status attn_sparse_mla(const cpa_tensor* q, const cpa_tensor* cache, const int32_t* req, const int32_t* idx,
+                           int64_t idx_stride, int32_t k, const int32_t* n_idx, float softmax_scale,
+                           const cpa_tensor* out, const cpa_tensor* lse, void* workspace, size_t ws_bytes,
+                           void* stream);
+
 /* Cache layouts of decode CP. */
 #define CPA_LAYOUT_CONTIGUOUS 0  /* rank c holds the c-th contiguous chunk (cp_decode_shards) */
 #define CPA_LAYOUT_ROUND_ROBIN 1 /* slot p on rank p % C, row p / C (cp_plan_round_robin) */

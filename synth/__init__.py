@@ -10,7 +10,8 @@ Seeding: a tensor of stream s for configuration k is drawn slab by slab along
 its first axis; slab i of ``chunk`` rows comes from
 ``numpy.random.default_rng([k, s, i])``. The result therefore does not
 depend on how many threads draw it. Streams: 0 request lengths, 1 queries,
-2 keys / latent cache, 3 values, 9 sampled rows.
+2 keys / latent cache, 3 values, 4 multi-query decode queries, 5 sparse
+queries, 6 top-k index lists, 9 sampled rows.
 
 Workload shapes follow the pages' workloads: a GLM-5.3-like 128k-token MLA
 context with 64 heads and a 576-dim latent (QK over 576, PV over 512), a
@@ -169,6 +170,27 @@ def agentic_lengths(config=5, n=16):
     un = g.integers(1024, 64 * 1024, size=n - half, endpoint=True).astype(np.int64)
     allv = np.concatenate([ln, un])
     return allv[g.permutation(n)].astype(np.int32)
+
+
+def topk_lists(config, stream, n, L, k, limit=None):
+    """Synthetic top-k selections: row i lists min(k, limit_i) distinct cache
+    rows drawn uniformly from [0, limit_i) (limit_i = L, or limit[i] for a
+    causal query that sees only rows below it), in random order, padded with
+    -1. Row i comes from default_rng([config, stream, i]). Returns (idx int32
+    [n, k], count int32 [n])."""
+    idx = np.full((n, k), -1, np.int32)
+    cnt = np.zeros(n, np.int32)
+    for i in range(n):
+        lim = int(L if limit is None else limit[i])
+        g = rng(config, stream, i)
+        m = min(k, lim)
+        if m == lim:
+            sel = g.permutation(lim)
+        else:
+            sel = g.choice(lim, m, replace=False)
+        idx[i, :m] = sel
+        cnt[i] = m
+    return idx, cnt
 
 
 CONFIGS = {
