@@ -25,6 +25,7 @@ the same kernels ran 10-15 % slower than in a sustained loop.
 """
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -243,7 +244,69 @@ def bench_decode(cpa, torch, synth, steps, warmup, warmup_ms):
     res["round_robin_bf16"] = bench_round_robin(cpa, torch, c, q, cache_bf16, steps, warmup, warmup_ms)
     res["multi_query_bf16"] = bench_multi_query(cpa, torch, synth, c, cache_bf16, 4, steps, warmup, warmup_ms)
     res["sparse_bf16"] = bench_sparse(cpa, torch, synth, c, cache_bf16, steps, warmup, warmup_ms)
+    res["topk"] = bench_topk(cpa, torch, synth, c, steps, warmup, warmup_ms)
     return res
+
+
+def bench_topk(cpa, torch, synth, c, steps, warmup, warmup_ms):
+    """Exact distributed top-2048 with the index split round robin over C=8
+    ranks, for the decode batch (64 query rows, 131072 index scores each):
+    a step is the C local top-k launches (16384 scores per row and rank) and
+    the merge of the C x 2048 candidates into the global top 2048 with the
+    owners' index lists. Algorithmic bytes: scores read once, candidate lists
+    written and read once, merged ids and owner lists written."""
+    N, L, C, k = c["B"], c["L"], c["C"], SPARSE_K
+    dev = torch.device("cuda:0")
+    s = synth.f32_normal(3, 8, (N, L))
+    loc = [torch.from_numpy(np.ascontiguousarray(s[:, r::C])).to(dev) for r in range(C)]
+    Lr = loc[0].shape[1]
+    sc = torch.empty((C, N, k), dtype=torch.float32, device=dev)
+    ids = torch.empty((C, N, k), dtype=torch.int32, device=dev)
+    rows = torch.empty((C, N, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((C, N), dtype=torch.int32, device=dev)
+    oid = torch.empty((N, k), dtype=torch.int32, device=dev)
+    orow = torch.empty((C, N, k), dtype=torch.int32, device=dev)
+    ocnt = torch.empty((C, N), dtype=torch.int32, device=dev)
+    lib = cpa.lib()
+    st = cpa._stream(None)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def step():
+        for r in range(C):
+            cpa._check(lib.attn_topk_local(ptr(loc[r]), Lr, N, Lr, None, k, r, C, ptr(sc[r]), ptr(ids[r]),
+                                           ptr(rows[r]), ptr(cnt[r]), st))
+        cpa._check(lib.attn_topk_merge(C, N, k, ptr(sc), ptr(ids), ptr(rows), ptr(cnt), k, ptr(oid), ptr(orow),
+                                       ptr(ocnt), st))
+
+    def local0():
+        cpa._check(lib.attn_topk_local(ptr(loc[0]), Lr, N, Lr, None, k, 0, C, ptr(sc[0]), ptr(ids[0]),
+                                       ptr(rows[0]), ptr(cnt[0]), st))
+
+    def merge():
+        cpa._check(lib.attn_topk_merge(C, N, k, ptr(sc), ptr(ids), ptr(rows), ptr(cnt), k, ptr(oid), ptr(orow),
+                                       ptr(ocnt), st))
+
+    _warm(torch, step, warmup, warmup_ms)
+
+    def timed(fn, n):
+        sev = _events(torch, 1)[0]
+        sev[0].record()
+        for _ in range(n):
+            fn()
+        sev[1].record()
+        torch.cuda.synchronize()
+        return sev[0].elapsed_time(sev[1]) / n
+
+    ms = timed(step, steps)
+    local_ms = timed(local0, steps)
+    merge_ms = timed(merge, steps)
+    nbytes = N * L * 4 + 2 * C * N * k * 12 + N * k * 4 + C * N * k * 4
+    # one rank's share: its local top-k over its 16384 scores per row, then the merge
+    rank_bytes = N * Lr * 4 + C * N * k * 12 + N * k * 4 + C * N * k * 4 + N * k * 12
+    rank_ms = local_ms + merge_ms
+    return dict(k=k, ranks=C, rows=N, step_us=ms * 1e3, step_gbs=nbytes / (ms * 1e-3) / 1e9,
+                local_us=local_ms * 1e3, merge_us=merge_ms * 1e3, per_rank_us=rank_ms * 1e3,
+                per_rank_gbs=rank_bytes / (rank_ms * 1e-3) / 1e9, algorithmic_bytes=nbytes)
 
 
 SPARSE_K = 2048
@@ -534,6 +597,7 @@ def main():
             },
             "round_robin_bf16": {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["round_robin_bf16"].items()},
             "frac_of_hbm_peak_step": {k: round(dec[k]["gbs"] / PEAK_HBM_GBS, 4) for k in ("bf16", "fp8", "round_robin_bf16")},
+            "topk_split_index": {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["topk"].items()},
             "sparse_bf16": {k: dict({kk: round(vv, 4) if isinstance(vv, float) else vv for kk, vv in v.items()},
                                     frac_of_hbm_peak=round(v["gbs"] / PEAK_HBM_GBS, 4))
                             for k, v in dec["sparse_bf16"].items()},

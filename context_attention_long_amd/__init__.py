@@ -57,7 +57,8 @@ assert SEGMENT_DTYPE.itemsize == ctypes.sizeof(CpaSegment) == 32
 SYMBOLS = ("cpa_last_error", "cpa_abi_version", "cp_plan_zigzag", "cp_plan_interleave", "cp_decode_shards",
            "attn_prefill_shard", "attn_decode_workspace_size", "attn_decode_shard", "attn_merge_states",
            "cp_round_robin_slot", "cp_plan_round_robin", "attn_cache_write_round_robin",
-           "attn_decode_shard_mq", "cp_plan_multi_query", "attn_sparse_mla_workspace_size", "attn_sparse_mla")
+           "attn_decode_shard_mq", "cp_plan_multi_query", "attn_sparse_mla_workspace_size", "attn_sparse_mla",
+           "attn_topk_local", "attn_topk_merge")
 
 _lib_handle = None
 
@@ -101,6 +102,13 @@ def lib():
         L.attn_sparse_mla.argtypes = [P(CpaTensor), P(CpaTensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, P(CpaTensor), P(CpaTensor),
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        vp = ctypes.c_void_p
+        L.attn_topk_local.restype = ctypes.c_int
+        L.attn_topk_local.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int32,
+                                      ctypes.c_int64, ctypes.c_int64, vp, vp, vp, vp, vp]
+        L.attn_topk_merge.restype = ctypes.c_int
+        L.attn_topk_merge.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_int32,
+                                      vp, vp, vp, vp]
         L.cp_round_robin_slot.restype = ctypes.c_int
         L.cp_round_robin_slot.argtypes = [ctypes.c_int64, ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int64)]
         L.cp_plan_round_robin.restype = ctypes.c_int
@@ -382,6 +390,54 @@ def attn_sparse_mla(q, cache, idx, softmax_scale, n_idx=None, req=None, out=None
                                  ctypes.byref(do), ctypes.byref(dl), ctypes.c_void_p(ws_ptr), ws_bytes,
                                  _stream(stream)))
     return out, lse
+
+
+def _dptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+
+
+def attn_topk_local(scores, k, id_base, id_stride, n_valid=None, stream=None):
+    """Local top-k of each row of scores [N, L] f32 (device, last dim
+    contiguous): entry j has global id id_base + j * id_stride. Returns
+    (score [N, k] f32, id [N, k] int32, row [N, k] int32, count [N] int32)."""
+    torch = _torch()
+    N, L = scores.shape
+    if scores.dtype != torch.float32 or (L > 1 and scores.stride(1) != 1):
+        raise TypeError("scores must be float32 [N, L] with a contiguous last dim")
+    if n_valid is not None and (n_valid.dtype != torch.int32 or not n_valid.is_contiguous() or n_valid.numel() != N):
+        raise TypeError("n_valid must be a contiguous int32 tensor [N]")
+    dev = scores.device
+    kk = max(int(k), 0)  # a negative k reaches the library, which rejects it
+    osc = torch.empty((N, kk), dtype=torch.float32, device=dev)
+    oid = torch.empty((N, kk), dtype=torch.int32, device=dev)
+    orow = torch.empty((N, kk), dtype=torch.int32, device=dev)
+    cnt = torch.empty((N,), dtype=torch.int32, device=dev)
+    _check(lib().attn_topk_local(_dptr(scores), int(scores.stride(0)) if N > 0 else int(L), int(N), int(L),
+                                 _dptr(n_valid), int(k), int(id_base), int(id_stride), _dptr(osc), _dptr(oid),
+                                 _dptr(orow), _dptr(cnt), _stream(stream)))
+    return osc, oid, orow, cnt
+
+
+def attn_topk_merge(cand_score, cand_id, cand_row, k, cand_count=None, stream=None):
+    """Exact global top k of P ranks' lists: cand_* [P, N, k_in] (f32 /
+    int32 / int32, contiguous), cand_count [P, N] int32 or None. Returns
+    (out_id [N, k], owner_row [P, N, k], owner_count [P, N]) int32."""
+    torch = _torch()
+    P, N, k_in = cand_score.shape
+    for t, dt in ((cand_score, torch.float32), (cand_id, torch.int32), (cand_row, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous() or tuple(t.shape) != (P, N, k_in):
+            raise TypeError("cand_score / cand_id / cand_row must be contiguous [P, N, k_in] f32 / int32 / int32")
+    if cand_count is not None and (cand_count.dtype != torch.int32 or not cand_count.is_contiguous()
+                                   or tuple(cand_count.shape) != (P, N)):
+        raise TypeError("cand_count must be a contiguous int32 tensor [P, N]")
+    dev = cand_score.device
+    kk = max(int(k), 0)
+    oid = torch.empty((N, kk), dtype=torch.int32, device=dev)
+    orow = torch.empty((P, N, kk), dtype=torch.int32, device=dev)
+    ocnt = torch.empty((P, N), dtype=torch.int32, device=dev)
+    _check(lib().attn_topk_merge(int(P), int(N), int(k_in), _dptr(cand_score), _dptr(cand_id), _dptr(cand_row),
+                                 _dptr(cand_count), int(k), _dptr(oid), _dptr(orow), _dptr(ocnt), _stream(stream)))
+    return oid, orow, ocnt
 
 
 def attn_merge_states(o_parts, lse_parts, out=None, lse_out=None, out_dtype=None, stream=None):

@@ -516,6 +516,56 @@ extern "C" cpa_status attn_sparse_mla(const cpa_tensor* q, const cpa_tensor* cac
   return CPA_OK;
 }
 
+// ------------------------------------------------------ distributed top-k
+
+extern "C" cpa_status attn_topk_local(const float* scores, int64_t score_stride, int32_t n_rows, int32_t L,
+                                      const int32_t* n_valid, int32_t k, int64_t id_base, int64_t id_stride,
+                                      float* out_score, int32_t* out_id, int32_t* out_row, int32_t* out_count,
+                                      void* stream) {
+  cpa::clear_error();
+  if (n_rows < 0 || L < 0 || k < 0) return fail(CPA_E_INVAL, "topk_local: negative n_rows, L or k");
+  if (score_stride < L) return fail(CPA_E_INVAL, "topk_local: score_stride %lld < L", (long long)score_stride);
+  if (n_rows == 0) return CPA_OK;
+  if (L > 0 && scores == nullptr) return fail(CPA_E_INVAL, "topk_local: scores is NULL");
+  if (out_count == nullptr || (k > 0 && (!out_score || !out_id || !out_row)))
+    return fail(CPA_E_INVAL, "topk_local: NULL output");
+  if (((uintptr_t)scores | (uintptr_t)out_score | (uintptr_t)out_id | (uintptr_t)out_row | (uintptr_t)out_count |
+       (uintptr_t)n_valid) % 4)
+    return fail(CPA_E_INVAL, "topk_local: arrays must be 4-byte aligned");
+  // global ids of rows 0 .. L-1 must be int32 values >= 0
+  const int64_t last = L > 0 ? id_base + (int64_t)(L - 1) * id_stride : id_base;
+  if (id_base < 0 || last < 0 || id_base > INT32_MAX || last > INT32_MAX)
+    return fail(CPA_E_INVAL, "topk_local: global ids outside [0, 2^31)");
+  if (L > 1 && id_stride == 0) return fail(CPA_E_INVAL, "topk_local: id_stride 0 gives equal ids");
+  cpa::TopkLocalArgs a{};
+  a.scores = scores, a.n_valid = n_valid, a.out_score = out_score, a.out_id = out_id, a.out_row = out_row;
+  a.out_count = out_count;
+  a.s_n = score_stride, a.id_base = id_base, a.id_stride = id_stride;
+  a.N = n_rows, a.L = L, a.k = k;
+  return hip_status(cpa::launch_topk_local(a, stream), "topk_local launch");
+}
+
+extern "C" cpa_status attn_topk_merge(int32_t P, int32_t n_rows, int32_t k_in, const float* cand_score,
+                                      const int32_t* cand_id, const int32_t* cand_row, const int32_t* cand_count,
+                                      int32_t k, int32_t* out_id, int32_t* owner_row, int32_t* owner_count,
+                                      void* stream) {
+  cpa::clear_error();
+  if (P < 1 || P > 64 || n_rows < 0 || k_in < 0 || k < 0)
+    return fail(CPA_E_INVAL, "topk_merge: bad P (1..64), n_rows, k_in or k");
+  if ((int64_t)P * k_in > INT32_MAX) return fail(CPA_E_INVAL, "topk_merge: P * k_in too large");
+  if (n_rows == 0) return CPA_OK;
+  if (k_in > 0 && (!cand_score || !cand_id || !cand_row)) return fail(CPA_E_INVAL, "topk_merge: NULL candidates");
+  if (owner_count == nullptr || (k > 0 && (!out_id || !owner_row))) return fail(CPA_E_INVAL, "topk_merge: NULL output");
+  if (((uintptr_t)cand_score | (uintptr_t)cand_id | (uintptr_t)cand_row | (uintptr_t)cand_count | (uintptr_t)out_id |
+       (uintptr_t)owner_row | (uintptr_t)owner_count) % 4)
+    return fail(CPA_E_INVAL, "topk_merge: arrays must be 4-byte aligned");
+  cpa::TopkMergeArgs a{};
+  a.cand_score = cand_score, a.cand_id = cand_id, a.cand_row = cand_row, a.cand_count = cand_count;
+  a.out_id = out_id, a.owner_row = owner_row, a.owner_count = owner_count;
+  a.P = P, a.N = n_rows, a.k_in = k_in, a.k = k;
+  return hip_status(cpa::launch_topk_merge(a, stream), "topk_merge launch");
+}
+
 // ------------------------------------------------------------------- prefill
 
 namespace {

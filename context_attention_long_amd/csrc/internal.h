@@ -91,6 +91,28 @@ struct SparseMlaArgs {
   float scale_log2;
 };
 
+struct TopkLocalArgs {
+  const float* scores;    // [N, L] (row stride s_n)
+  const int32_t* n_valid; // [N] or null (all L)
+  float* out_score;       // [N, k]
+  int32_t* out_id;        // [N, k] global ids
+  int32_t* out_row;       // [N, k] local rows
+  int32_t* out_count;     // [N]
+  int64_t s_n, id_base, id_stride;
+  int32_t N, L, k;
+};
+
+struct TopkMergeArgs {
+  const float* cand_score;  // [P, N, k_in]
+  const int32_t* cand_id;   // [P, N, k_in]
+  const int32_t* cand_row;  // [P, N, k_in]
+  const int32_t* cand_count;  // [P, N] or null (all k_in)
+  int32_t* out_id;          // [N, k]
+  int32_t* owner_row;       // [P, N, k]
+  int32_t* owner_count;     // [P, N]
+  int32_t P, N, k_in, k;
+};
+
 struct PrefillGqaArgs {
   const uint16_t* q;    // [n_local, Hq, 128] bf16
   const uint16_t* k;    // [T_kv, Hkv, 128]
@@ -131,5 +153,7 @@ int launch_prefill_gqa(const PrefillGqaArgs& a, const cpa_segment* seg, int n_se
 int launch_prefill_mla(const PrefillMlaArgs& a, const cpa_segment* seg, int n_seg, void* stream);
 int launch_cache_write_rr(const CacheWriteArgs& a, void* stream);
 int launch_sparse_mla(const SparseMlaArgs& a, void* stream);
+int launch_topk_local(const TopkLocalArgs& a, void* stream);
+int launch_topk_merge(const TopkMergeArgs& a, void* stream);
 
 }  // namespace cpa

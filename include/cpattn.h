@@ -302,6 +302,44 @@ cpa_status attn_sparse_mla(const cpa_tensor* q, const cpa_tensor* cache, const i
                            const cpa_tensor* out, const cpa_tensor* lse, void* workspace, size_t ws_bytes,
                            void* stream);
 
+/*
+ * Exact distributed top-k for sparse attention with a split index
+ * (DeepSeek-V4 notes, 5.2: each rank keeps a local top-k list of (score,
+ * global id), the at most P x k candidates merge into the exact global top
+ * k, the selected ids go to their owners; Long Context 4.1, Figure 11).
+ * Order: higher score first; equal scores (-0 = +0) by lower global id; NaN
+ * below every number. Using the same rule on every rank makes the union of
+ * the local lists contain the global top k, so the merge is exact. All
+ * arrays are DEVICE arrays, 4-byte aligned; both calls are asynchronous.
+ *
+ * attn_topk_local: for each of n_rows query rows, the best min(k, n) of the
+ * rank's local entries 0 .. n-1 (n = n_valid[row], clamped to [0, L], or L
+ * when n_valid is NULL), entry j having score scores[row * score_stride + j]
+ * and global id id_base + j * id_stride (round robin: rank, C; contiguous
+ * chunk: its first position, 1). Writes, in ascending local row order,
+ * out_score / out_id / out_row [n_rows, k] (padded with -inf / -1 / -1) and
+ * out_count [n_rows]. CPA_E_INVAL if a global id falls outside [0, 2^31), on
+ * negative sizes, NULL arrays or misalignment.
+ */
+cpa_status attn_topk_local(const float* scores, int64_t score_stride, int32_t n_rows, int32_t L,
+                           const int32_t* n_valid, int32_t k, int64_t id_base, int64_t id_stride, float* out_score,
+                           int32_t* out_id, int32_t* out_row, int32_t* out_count, void* stream);
+
+/*
+ * attn_topk_merge: for each query row, the exact global top k of the P
+ * ranks' lists (1 <= P <= 64). Candidates: cand_score / cand_id / cand_row [P, n_rows,
+ * k_in] (rank p's list of that row: its first cand_count[p * n_rows + row]
+ * entries, clamped to [0, k_in], or all k_in when cand_count is NULL).
+ * Global ids must be distinct within a row. Writes out_id [n_rows, k]: the
+ * selected global ids, grouped by rank (rank 0's first) and in each rank's
+ * list order, padded with -1; owner_row [P, n_rows, k]: for each rank the
+ * local rows (cand_row) of its selected entries, padded with -1 -- the
+ * index lists its attn_sparse_mla call takes -- and owner_count [P, n_rows].
+ */
+cpa_status attn_topk_merge(int32_t P, int32_t n_rows, int32_t k_in, const float* cand_score, const int32_t* cand_id,
+                           const int32_t* cand_row, const int32_t* cand_count, int32_t k, int32_t* out_id,
+                           int32_t* owner_row, int32_t* owner_count, void* stream);
+
 /* Cache layouts of decode CP. */
 #define CPA_LAYOUT_CONTIGUOUS 0  /* rank c holds the c-th contiguous chunk (cp_decode_shards) */
 #define CPA_LAYOUT_ROUND_ROBIN 1 /* slot p on rank p % C, row p / C (cp_plan_round_robin) */

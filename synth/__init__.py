@@ -11,7 +11,7 @@ its first axis; slab i of ``chunk`` rows comes from
 ``numpy.random.default_rng([k, s, i])``. The result therefore does not
 depend on how many threads draw it. Streams: 0 request lengths, 1 queries,
 2 keys / latent cache, 3 values, 4 multi-query decode queries, 5 sparse
-queries, 6 top-k index lists, 9 sampled rows.
+queries, 6 and 7 top-k index lists, 8 index scores, 9 sampled rows.
 
 Workload shapes follow the pages' workloads: a GLM-5.3-like 128k-token MLA
 context with 64 heads and a 576-dim latent (QK over 576, PV over 512), a
