@@ -15,6 +15,7 @@
 
 #include "internal.h"
 #include "mla_core.h"
+#include "mla_ws.h"
 
 namespace {
 
@@ -78,6 +79,63 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
   }
 }
 
+// bf16 cache: the wave-specialised core (mla_ws.h), 8 wavefronts.
+template <cpa::Policy kP>
+__global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::DecodeMlaArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
+  __shared__ float alpha_s[2 * kH], lsum_s[kH];
+  const Lds S{smem, plds, alpha_s, lsum_s};
+
+  const int u = (int)(blockIdx.x / (8 * a.Q)) * 8 + (int)(blockIdx.x % 8);
+  const int k = (int)(blockIdx.x / 8) % a.Q;
+  if (u >= a.B * a.nsplit) return;
+  const int split = u % a.nsplit;
+  const int b = u / a.nsplit;
+  const int row = b * a.Q + k;
+  const int tid = threadIdx.x;
+  const int w = (tid >> 6) & 3, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const bool qk_role = tid < 256;
+
+  int64_t beg = a.kv_begin[b], end = a.kv_end[row];
+  beg = beg < 0 ? 0 : (beg > a.Lmax ? a.Lmax : beg);
+  end = end < beg ? beg : (end > a.Lmax ? a.Lmax : end);
+  const int64_t len = end - beg;
+  const Tiles T(beg + len * split / a.nsplit, beg + len * (split + 1) / a.nsplit, (unsigned)u * 2654435761u >> 7);
+  const LdsBases L = lds_bases(w, g, c);
+
+  if (qk_role) {
+    bf16x8 qreg[kQSteps];
+    load_q(a.q + (int64_t)b * a.q_b + (int64_t)k * a.q_q + (int64_t)(16 * w + c) * a.q_h, g, qreg);
+    QkStat st{-INFINITY, 0.f};
+    ws_qk(T, w, g, c, L, qreg, a.scale_log2, st, S);
+    const float l = sum4_rows(st.l_run);
+    if (g == 0) S.lsum[16 * w + c] = l;
+    __syncthreads();
+    if (g == 0)
+      a.lse[(int64_t)split * a.l_s + (int64_t)row * a.l_b + (int64_t)(16 * w + c) * a.l_h] =
+          l > 0.f ? (st.m_run + log2f(l)) * kLn2 : -INFINITY;
+  } else {
+    f32x4 oacc[kMv][4];
+#pragma unroll
+    for (int m = 0; m < kMv; ++m)
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) oacc[m][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ws_pv<kP>(T, reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, tid - 256, w, g, c, L, oacc,
+              S);
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const int head = 16 * hb + c;
+      const float lh = lsum_s[head];
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      float* op = a.o + (int64_t)split * a.o_s + (int64_t)row * a.o_b + (int64_t)head * a.o_h + 128 * w + 4 * g;
+#pragma unroll
+      for (int m = 0; m < kMv; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = oacc[m][hb] * inv;
+    }
+  }
+}
+
 }  // namespace
 
 namespace cpa {
@@ -91,9 +149,9 @@ int launch_decode_mla(const DecodeMlaArgs& a, void* stream) {
   else if (a.fp8)
     hipLaunchKernelGGL((decode_mla_kernel<true, kR>), grid, dim3(kThreads), 0, st, a);
   else if (a.Q == 1)
-    hipLaunchKernelGGL((decode_mla_kernel<false, kS>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mla_ws_kernel<kS>), grid, dim3(kWsThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_mla_kernel<false, kR>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mla_ws_kernel<kR>), grid, dim3(kWsThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -284,7 +284,8 @@ __device__ __forceinline__ void soft_scores(Soft& sm, const f32x4 (&sacc)[2], in
     }
 }
 
-__device__ __forceinline__ void soft_ref(Soft& sm, State& st) {
+template <typename St>
+__device__ __forceinline__ void soft_ref(Soft& sm, St& st) {
   const float mx = max4_rows(sm.mx);
   const bool move = mx > st.m_run + 8.f;
   const float m_new = move ? mx : st.m_run;
@@ -296,8 +297,8 @@ __device__ __forceinline__ void soft_ref(Soft& sm, State& st) {
 
 // kMask: a head may have seen no selected token yet (reference max still
 // -inf, every score -inf); its probabilities are then 0, not -inf - -inf.
-template <bool kFp8, int J0, bool kMask = false>
-__device__ __forceinline__ void soft_exp(Soft& sm, const State& st, const TokScale& ts) {
+template <bool kFp8, int J0, bool kMask = false, typename St>
+__device__ __forceinline__ void soft_exp(Soft& sm, const St& st, const TokScale& ts) {
   const float mref = (kMask && st.m_run == -INFINITY) ? 0.f : st.m_run;
 #pragma unroll
   for (int j = J0; j < J0 + 4; ++j) {
@@ -307,7 +308,8 @@ __device__ __forceinline__ void soft_exp(Soft& sm, const State& st, const TokSca
   }
 }
 
-__device__ __forceinline__ void soft_store(Soft& sm, State& st, char* pbuf, float* abuf, int w, int g, int c) {
+template <typename St>
+__device__ __forceinline__ void soft_store(Soft& sm, St& st, char* pbuf, float* abuf, int w, int g, int c) {
   st.l_run += sm.psum;
   // P^T chunk of this lane: head 16w + c, k-elements 8g..8g+7 in score order
   *reinterpret_cast<bf16x8*>(pbuf + p_off(16 * w + c, g)) = pack8(sm.pf);

@@ -17,6 +17,7 @@
 
 #include "internal.h"
 #include "mla_core.h"
+#include "mla_ws.h"
 
 namespace {
 
@@ -41,14 +42,17 @@ struct Args {
   Seg seg[kMaxSeg];
 };
 
-__global__ __launch_bounds__(kThreads, 1) void prefill_mla_kernel(Args a) {
+// One workgroup per query row on the wave-specialised core (mla_ws.h): 4
+// QK + 4 PV wavefronts.
+__global__ __launch_bounds__(kWsThreads, 1) void prefill_mla_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
   __shared__ float alpha_s[2 * kH], lsum_s[kH];
   const Lds S{smem, plds, alpha_s, lsum_s};
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int w = (tid >> 6) & 3, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const bool qk_role = tid < 256;
 
   // ---- the query row of this workgroup (most expensive first) ----
   const int wi = blockIdx.x;
@@ -59,31 +63,40 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mla_kernel(Args a) {
   const int qi = Sg.q_len - 1 - (wi - Sg.tile_begin);
   const int64_t q_row = (int64_t)Sg.q_row0 + qi;
   const int pos = Sg.pos0 + qi * Sg.pos_stride;
-
-  bf16x8 qreg[kQSteps];
-  load_q(a.q + q_row * a.q_n + (int64_t)(16 * w + c) * a.q_h, g, qreg);
-  State st;
-  init_state(st);
+  const Tiles T(0, (int64_t)pos + 1, 0u);
   const LdsBases L = lds_bases(w, g, c);
-  run_bf16<cpa::Policy::kReuse>(a.lat + Sg.kv_row0 * a.k_t, a.k_t, 0, (int64_t)pos + 1, w, g, c, L, qreg,
-                                a.scale_log2, st, S);
 
-  // ---- normalise and store: LSE of the QK-role head, O of the PV-role dims ----
-  const float l = finish(st, w, g, c, S);
-  if (g == 0) a.lse[q_row * a.l_n + (int64_t)(16 * w + c) * a.l_h] = (st.m_run + log2f(l)) * kLn2;
+  if (qk_role) {
+    bf16x8 qreg[kQSteps];
+    load_q(a.q + q_row * a.q_n + (int64_t)(16 * w + c) * a.q_h, g, qreg);
+    QkStat st{-INFINITY, 0.f};
+    ws_qk(T, w, g, c, L, qreg, a.scale_log2, st, S);
+    const float l = sum4_rows(st.l_run);
+    if (g == 0) S.lsum[16 * w + c] = l;
+    __syncthreads();
+    if (g == 0) a.lse[q_row * a.l_n + (int64_t)(16 * w + c) * a.l_h] = (st.m_run + log2f(l)) * kLn2;
+  } else {
+    f32x4 oacc[kMv][4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    const int head = 16 * hb + c;
-    const float inv = 1.f / lsum_s[head];  // key 0 is always in range: the sum is >= 1
-    const int64_t o0 = q_row * a.o_n + (int64_t)head * a.o_h + 128 * w + 4 * g;
+    for (int m = 0; m < kMv; ++m)
 #pragma unroll
-    for (int m = 0; m < kMv; ++m) {
-      const f32x4 o = st.oacc[m][hb] * inv;
-      if (a.out_bf16)
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + o0 + 16 * m) =
-            make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
-      else
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o0 + 16 * m) = o;
+      for (int hb = 0; hb < 4; ++hb) oacc[m][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ws_pv<cpa::Policy::kReuse>(T, a.lat + Sg.kv_row0 * a.k_t, a.k_t, tid - 256, w, g, c, L, oacc, S);
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const int head = 16 * hb + c;
+      const float inv = 1.f / lsum_s[head];  // key 0 is always in range: the sum is >= 1
+      const int64_t o0 = q_row * a.o_n + (int64_t)head * a.o_h + 128 * w + 4 * g;
+#pragma unroll
+      for (int m = 0; m < kMv; ++m) {
+        const f32x4 o = oacc[m][hb] * inv;
+        if (a.out_bf16)
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + o0 + 16 * m) =
+              make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
+        else
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o0 + 16 * m) = o;
+      }
     }
   }
 }
@@ -123,7 +136,7 @@ int launch_prefill_mla(const PrefillMlaArgs& in, const cpa_segment* seg, int n_s
     }
     a.n_seg = ns;
     if (rows == 0) continue;
-    hipLaunchKernelGGL(prefill_mla_kernel, dim3((unsigned)rows), dim3(kThreads), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(prefill_mla_kernel, dim3((unsigned)rows), dim3(kWsThreads), 0, (hipStream_t)stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
