@@ -79,8 +79,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaA
   }
 }
 
-// bf16 cache: the wave-specialised core (mla_ws.h), 8 wavefronts.
-template <cpa::Policy kP>
+// The wave-specialised core (mla_ws.h), 8 wavefronts: bf16 tiles arrive by
+// direct loads, FP8 tiles are converted into LDS by the PV wavefronts.
+template <bool kFp8, cpa::Policy kP>
 __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::DecodeMlaArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
@@ -108,7 +109,26 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
     bf16x8 qreg[kQSteps];
     load_q(a.q + (int64_t)b * a.q_b + (int64_t)k * a.q_q + (int64_t)(16 * w + c) * a.q_h, g, qreg);
     QkStat st{-INFINITY, 0.f};
-    ws_qk(T, w, g, c, L, qreg, a.scale_log2, st, S);
+    if constexpr (kFp8) {
+      const float* sbase = a.kv_scale + (int64_t)b * a.s_b;
+      const uint32_t st32 = (uint32_t)a.s_t;  // the host bounds the scale stride
+      auto scales = [&](int i, TokScale& ts) {  // the 8 tokens whose scores this lane holds
+        const int64_t tok0 = T.t0 + (int64_t)T.phys(i) * kBN;
+        const int lim = (int)min((int64_t)(kBN - 1), T.t1 - 1 - tok0);
+        const float* sb = sbase + tok0 * a.s_t;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t r = (uint32_t)min(16 * (j >> 2) + 4 * g + (j & 3), lim);
+          if constexpr (kP == cpa::Policy::kStream) ts.v[j] = __builtin_nontemporal_load(sb + r * st32);
+          else ts.v[j] = sb[r * st32];
+        }
+      };
+      ws_qk<true>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return S.tiles + (i % 3) * kTileBytes; },
+                  scales);
+    } else {
+      ws_qk<false>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); },
+                   [](int, TokScale&) {});
+    }
     const float l = sum4_rows(st.l_run);
     if (g == 0) S.lsum[16 * w + c] = l;
     __syncthreads();
@@ -121,8 +141,12 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
     for (int m = 0; m < kMv; ++m)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) oacc[m][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    ws_pv<kP>(T, reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, tid - 256, w, g, c, L, oacc,
-              S);
+    if constexpr (kFp8)
+      ws_pv_fp8<kP>(T, reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, tid - 256, w, g, c, L,
+                    oacc, S);
+    else
+      ws_pv<kP>(T, reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, tid - 256, w, g, c, L,
+                oacc, S);
     __syncthreads();
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
@@ -145,13 +169,13 @@ int launch_decode_mla(const DecodeMlaArgs& a, void* stream) {
   constexpr auto kS = Policy::kStream, kR = Policy::kReuse;
   hipStream_t st = (hipStream_t)stream;
   if (a.fp8 && a.Q == 1)
-    hipLaunchKernelGGL((decode_mla_kernel<true, kS>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mla_ws_kernel<true, kS>), grid, dim3(kWsThreads), 0, st, a);
   else if (a.fp8)
-    hipLaunchKernelGGL((decode_mla_kernel<true, kR>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mla_ws_kernel<true, kR>), grid, dim3(kWsThreads), 0, st, a);
   else if (a.Q == 1)
-    hipLaunchKernelGGL((decode_mla_ws_kernel<kS>), grid, dim3(kWsThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mla_ws_kernel<false, kS>), grid, dim3(kWsThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_mla_ws_kernel<kR>), grid, dim3(kWsThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mla_ws_kernel<false, kR>), grid, dim3(kWsThreads), 0, st, a);
   return hipGetLastError();
 }
 

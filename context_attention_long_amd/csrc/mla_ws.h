@@ -22,6 +22,8 @@
 //   PV: O = alpha_i O + V_i^T P_i; loads of tile i+3 into tile i-1's stage
 #pragma once
 
+#include <type_traits>
+
 #include "mla_core.h"
 
 namespace cpa {
@@ -54,25 +56,44 @@ struct Tiles {
 __device__ __forceinline__ const char* ws_tile(const Lds& S, int i) { return S.tiles + (i & 3) * kTileBytes; }
 
 // QK role. Barriers: 1 (tile 0) + (ntiles - 1) (loop) + 1 (after the loop).
+// tile(i): LDS bf16 tile of step i. kFp8: scales(i, ts) loads the per-token
+// scales of tile i (two steps ahead of their use), folded into the scores
+// and P.
+template <bool kFp8, typename TileFn, typename ScaleFn>
 __device__ __forceinline__ void ws_qk(const Tiles& T, int w, int g, int c, const LdsBases& L,
-                                      const bf16x8 (&qreg)[kQSteps], float scale_log2, QkStat& st, const Lds& S) {
+                                      const bf16x8 (&qreg)[kQSteps], float scale_log2, QkStat& st, const Lds& S,
+                                      TileFn&& tile, ScaleFn&& scales) {
   if (T.ntiles <= 0) return;
-  const TokScale none{};
-  auto scores = [&](int i, int buf) {
+  TokScale tsc[2];
+  auto clampt = [&](int i) { return min(i, T.ntiles - 1); };
+  if constexpr (kFp8) {
+    scales(0, tsc[0]);
+    scales(clampt(1), tsc[1]);
+  }
+  auto step = [&](int i, auto parity) {  // scores and P of tile i; parity = i & 1
+    constexpr int P = decltype(parity)::value;
     f32x4 sacc[2];
-    qk_tile(ws_tile(S, i), L, qreg, sacc, [](int) {}, [](int) {});
+    qk_tile(tile(i), L, qreg, sacc, [](int) {}, [](int) {});
     Soft sm;
-    soft_scores<false>(sm, sacc, T.nvalid(i), g, scale_log2, none);
+    soft_scores<kFp8>(sm, sacc, T.nvalid(i), g, scale_log2, tsc[P]);
     soft_ref(sm, st);
-    soft_exp<false, 0>(sm, st, none);
-    soft_exp<false, 4>(sm, st, none);
-    soft_store(sm, st, S.p + kH * kPRowBytes * buf, S.alpha + kH * buf, w, g, c);
+    soft_exp<kFp8, 0>(sm, st, tsc[P]);
+    soft_exp<kFp8, 4>(sm, st, tsc[P]);
+    soft_store(sm, st, S.p + kH * kPRowBytes * P, S.alpha + kH * P, w, g, c);
+    if constexpr (kFp8) scales(clampt(i + 2), tsc[P]);  // tile i's scales are spent
   };
-  __syncthreads();  // tile 0 landed
-  scores(0, 0);
-  for (int i = 0; i + 1 < T.ntiles; ++i) {
+  __syncthreads();  // tile 0 ready
+  step(0, std::integral_constant<int, 0>{});
+  int i = 0;
+  for (; i + 2 < T.ntiles; i += 2) {
     __syncthreads();  // P_i and tile i+1 visible
-    scores(i + 1, (i + 1) & 1);
+    step(i + 1, std::integral_constant<int, 1>{});
+    __syncthreads();
+    step(i + 2, std::integral_constant<int, 0>{});
+  }
+  if (i + 1 < T.ntiles) {
+    __syncthreads();
+    step(i + 1, std::integral_constant<int, 1>{});
   }
   __syncthreads();  // P of the last tile visible
 }
@@ -167,6 +188,125 @@ __device__ __forceinline__ void ws_pv(const Tiles& T, const uint16_t* base, int6
         lds_dma16_s<P>(ntb, toff[m + 1], ndst + kThreads * (m + 1) * 16);
       }
     });
+  }
+  __syncthreads();  // P of the last tile visible
+  pv(n - 1, [](int) {});
+}
+
+// PV role over an FP8 E4M3 cache (entry = e4m3 * scale_t; the scale is
+// folded into P by the QK role). The cache bytes stream into registers two
+// tiles ahead (each thread holds 9 units of 8 bytes of a tile; nontemporal
+// for kStream); during the PV MFMAs of step i each unit of tile i+2 is
+// converted to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1) into its
+// swizzled LDS slot of stage (i+2) % 3, and the register is refilled with
+// tile i+4. The loads and conversions are unconditional (past the last tile
+// they re-read it and write a stage nobody reads again): loads under a
+// branch make the compiler's waits fall back to draining every load.
+template <Policy kPol>
+__device__ __forceinline__ void ws_pv_fp8(const Tiles& T, const uint8_t* base, int64_t c_t, int tp, int w, int g,
+                                          int c, const LdsBases& L, f32x4 (&oacc)[kMv][4], const Lds& S) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  if (T.ntiles <= 0) return;
+  auto stage = [&](int i) -> char* { return S.tiles + (i % 3) * kTileBytes; };
+  // unit j of this thread: 8 cache bytes of row u / 72, chunk u % 72 (u = tp + 256 j);
+  // recomputed where used (cheap next to the registers a table would hold)
+  auto urow = [&](int j) { return (tp + kThreads * j) / kRowChunks; };
+  auto uch = [&](int j) { return (tp + kThreads * j) % kRowChunks; };
+  u32x2 raw[2][kLdChunks];
+  const uint32_t ct32 = (uint32_t)c_t;  // the host bounds the token stride
+  auto load_unit = [&](int i, int j, u32x2& r) {
+    const int64_t tok0 = T.t0 + (int64_t)T.phys(i) * kBN;
+    const int lim = (int)min((int64_t)(kBN - 1), T.t1 - 1 - tok0);
+    const uint8_t* tb = base + tok0 * c_t;
+    const uint32_t off = (uint32_t)min(urow(j), lim) * ct32 + (uint32_t)(uch(j) * 8);
+    if constexpr (kPol == Policy::kStream)
+      r = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tb + off));
+    else
+      r = *reinterpret_cast<const u32x2*>(tb + off);
+  };
+  auto convert_unit = [&](const u32x2& r, int j, char* tile) {
+    const uint32_t o0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, false));
+    const uint32_t o1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, true));
+    const uint32_t o2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, false));
+    const uint32_t o3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, true));
+    const int row = urow(j);
+    *reinterpret_cast<uint4*>(tile + row * (kRowChunks * 16) + swz(row, uch(j)) * 16) = make_uint4(o0, o1, o2, o3);
+  };
+  const int n = T.ntiles;
+  auto clampt = [&](int i) { return min(i, n - 1); };
+  // ---- prologue: tiles 0 and 1 converted, tiles 2 and 3 in registers ----
+#pragma unroll
+  for (int j = 0; j < kLdChunks; ++j) load_unit(0, j, raw[0][j]);
+#pragma unroll
+  for (int j = 0; j < kLdChunks; ++j) load_unit(clampt(1), j, raw[1][j]);
+#pragma unroll
+  for (int j = 0; j < kLdChunks; ++j) {
+    convert_unit(raw[0][j], j, stage(0));
+    load_unit(clampt(2), j, raw[0][j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kLdChunks; ++j) {
+    convert_unit(raw[1][j], j, stage(1));
+    load_unit(clampt(3), j, raw[1][j]);
+  }
+  __syncthreads();
+
+  constexpr int kAheadV = 2;  // V operands read ahead (registers are tight next to the FP8 units)
+  auto pv = [&](int i, auto&& hook) {
+    const char* cur = stage(i);
+    const float* acur = S.alpha + kH * (i & 1);
+    const char* pcur = S.p + kH * kPRowBytes * (i & 1);
+    float al[4];
+    bf16x8 pb[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      al[hb] = acur[16 * hb + c];
+      pb[hb] = *reinterpret_cast<const bf16x8*>(pcur + p_off(16 * hb + c, g));
+    }
+    bf16x8 va[kMv];
+    auto load_v = [&](int m) {
+      va[m] = join_tr(lds_read_tr(cur + L.pv[0][m & 3] + 128 * (m >> 2)),
+                      lds_read_tr(cur + L.pv[1][m & 3] + 128 * (m >> 2)));
+    };
+#pragma unroll
+    for (int m = 0; m < kAheadV; ++m) load_v(m);
+    if (__any(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
+#pragma unroll
+      for (int m = 0; m < kMv; ++m)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) oacc[m][hb] *= al[hb];
+    }
+#pragma unroll
+    for (int m = 0; m < kMv; ++m) {
+      if (m + kAheadV < kMv) load_v(m + kAheadV);
+      hook(m);
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        oacc[m][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb[hb], oacc[m][hb], 0, 0, 0);
+    }
+  };
+  // step i: PV of tile i, conversion of tile i+2 from raw[i & 1], refill with tile i+4
+  auto step = [&](int i, auto parity) {
+    constexpr int P = decltype(parity)::value;
+    __syncthreads();  // P_i visible; every wave is done with tile i-1's stage
+    const int refill_t = clampt(i + 4);
+    char* dst = stage(i + 2);
+    pv(i, [&](int m) {  // units 0-1 at m-step 0, one per m-step after
+#pragma unroll
+      for (int j = (m == 0 ? 0 : m + 1); j <= m + 1; ++j) {
+        convert_unit(raw[P][j], j, dst);
+        load_unit(refill_t, j, raw[P][j]);
+      }
+    });
+  };
+  int i = 0;
+  for (; i + 2 < n; i += 2) {
+    step(i, std::integral_constant<int, 0>{});
+    step(i + 1, std::integral_constant<int, 1>{});
+  }
+  if (i + 1 < n) {
+    step(i, std::integral_constant<int, 0>{});
+    ++i;
   }
   __syncthreads();  // P of the last tile visible
   pv(n - 1, [](int) {});
