@@ -69,7 +69,7 @@ def _src_digest(files):
 
 KERNEL_SOURCES = {
     "prefill_gqa_kernel": ("prefill.hip", "lds_dma.h"),
-    "decode_mla_kernel<bf16>": ("decode_mla.hip", "mla_core.h", "lds_dma.h"),
+    "decode_mla_kernel<bf16>": ("decode_mla.hip", "mla_core.h", "mla_ws.h", "lds_dma.h"),
 }
 
 
@@ -589,7 +589,7 @@ def main():
             "bf16": {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["bf16"].items()},
             "fp8": {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["fp8"].items()},
             "roofline": {
-                "kernel": "decode_mla_kernel (bf16 cache)", "bound": "hbm",
+                "kernel": "decode_mla_ws_kernel (bf16 cache)", "bound": "hbm",
                 "achieved": round(dec["bf16"]["launch_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(dec["bf16"]["launch_gbs"] / PEAK_HBM_GBS, 4),
                 "traffic": traffic("decode_mla_kernel<bf16>")[0],

@@ -6,11 +6,12 @@
 // of the cache and reports partial output + LSE; 1.3 and the vLLM DCP post,
 // 5.3 -- one latent vector per token is read by all heads.
 //
-// One workgroup per (request, split): the split's contiguous token range
-// runs through the shared MLA core (mla_core.h), which reads every cache
-// byte from HBM once per workgroup (nontemporal: the shard is read once per
-// launch). The workgroup writes its split's normalised output and LSE; the
-// splits of a request are merged by the LSE merge.
+// One workgroup per (query row, split): the split's contiguous token range
+// runs through the wave-specialised MLA core (mla_ws.h), which reads every
+// cache byte from HBM once per workgroup (nontemporal when one query row
+// reads it: the shard is read once per launch). The workgroup writes its
+// split's normalised output and LSE; the splits of a row are merged by the
+// LSE merge.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -21,66 +22,10 @@ namespace {
 
 using namespace cpa::mla;
 
-// kP: kStream (one query row per request: every cache byte is read once) or
-// kReuse (several query rows read each tile through the shared L2).
-template <bool kFp8, cpa::Policy kP>
-__global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(cpa::DecodeMlaArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
-  __shared__ float alpha_s[2 * kH], lsum_s[kH];
-  const Lds S{smem, plds, alpha_s, lsum_s};
-
-  // unit u = (request, split); its Q query rows run as Q workgroups with
-  // block indices 8 apart, so they share an XCD (block index mod 8) and its
-  // L2, start together and walk the tiles in the same (rotated) order: one
-  // fetch of a tile from HBM serves all rows
-  const int u = (int)(blockIdx.x / (8 * a.Q)) * 8 + (int)(blockIdx.x % 8);
-  const int k = (int)(blockIdx.x / 8) % a.Q;
-  if (u >= a.B * a.nsplit) return;
-  const int split = u % a.nsplit;
-  const int b = u / a.nsplit;
-  const int row = b * a.Q + k;  // output row
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-
-  int64_t beg = a.kv_begin[b], end = a.kv_end[row];
-  beg = beg < 0 ? 0 : (beg > a.Lmax ? a.Lmax : beg);
-  end = end < beg ? beg : (end > a.Lmax ? a.Lmax : end);
-  const int64_t len = end - beg;
-  const int64_t t0 = beg + len * split / a.nsplit;
-  const int64_t t1 = beg + len * (split + 1) / a.nsplit;
-
-  bf16x8 qreg[kQSteps];
-  load_q(a.q + (int64_t)b * a.q_b + (int64_t)k * a.q_q + (int64_t)(16 * w + c) * a.q_h, g, qreg);
-  State st;
-  init_state(st);
-  const LdsBases L = lds_bases(w, g, c);
-
-  if constexpr (kFp8)
-    run_fp8<kP>(reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, a.kv_scale + (int64_t)b * a.s_b,
-            a.s_t, t0, t1, w, g, c, L, qreg, a.scale_log2, st, S, (unsigned)u * 2654435761u >> 7);
-  else
-    run_bf16<kP>(reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, t0, t1, w, g, c, L, qreg,
-                 a.scale_log2, st, S, (unsigned)u * 2654435761u >> 7);
-
-  // ---- split result: LSE of the QK-role head, normalised O of the PV-role dims ----
-  const float l = finish(st, w, g, c, S);
-  if (g == 0)
-    a.lse[(int64_t)split * a.l_s + (int64_t)row * a.l_b + (int64_t)(16 * w + c) * a.l_h] =
-        l > 0.f ? (st.m_run + log2f(l)) * kLn2 : -INFINITY;
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    const int head = 16 * hb + c;
-    const float lh = lsum_s[head];
-    const float inv = lh > 0.f ? 1.f / lh : 0.f;
-    float* op = a.o + (int64_t)split * a.o_s + (int64_t)row * a.o_b + (int64_t)head * a.o_h + 128 * w + 4 * g;
-#pragma unroll
-    for (int m = 0; m < kMv; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = st.oacc[m][hb] * inv;
-  }
-}
-
-// The wave-specialised core (mla_ws.h), 8 wavefronts: bf16 tiles arrive by
-// direct loads, FP8 tiles are converted into LDS by the PV wavefronts.
+// 8 wavefronts: bf16 tiles arrive by direct loads, FP8 tiles are converted
+// into LDS by the PV wavefronts. kP: kStream (one query row per request:
+// every cache byte is read once) or kReuse (several query rows read each
+// tile through the shared L2).
 template <bool kFp8, cpa::Policy kP>
 __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::DecodeMlaArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
@@ -123,11 +68,29 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
           else ts.v[j] = sb[r * st32];
         }
       };
+      // this role's share of the FP8 conversion, 4 units per thread: step i
+      // (before the barrier that publishes tile i+1) converts tile i+1 into
+      // stage (i+1) % 3 from set (i+1) & 1 and refills that set with tile
+      // i+3; the PV role converts its units of the same tile in the same
+      // interval.
+      Fp8Units<4, kP> U;
+      U.base = reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, U.c_t = a.c_t, U.t = tid;
+      if (T.ntiles > 0) U.template prologue<1>(T, S);
+      auto convert_ahead = [&](int i, auto parity) {
+        constexpr int P = decltype(parity)::value;
+        char* dst = S.tiles + ((i + 1) % 3) * kTileBytes;
+        const int refill_t = min(i + 3, T.ntiles - 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          U.convert(j, P ^ 1, dst);
+          U.load(T, refill_t, j, P ^ 1);
+        }
+      };
       ws_qk<true>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return S.tiles + (i % 3) * kTileBytes; },
-                  scales);
+                  scales, [](int) { return 0xffffffffu; }, convert_ahead);
     } else {
       ws_qk<false>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); },
-                   [](int, TokScale&) {});
+                   [](int, TokScale&) {}, [](int) { return 0xffffffffu; });
     }
     const float l = sum4_rows(st.l_run);
     if (g == 0) S.lsum[16 * w + c] = l;

@@ -1,6 +1,6 @@
-// Attention of one query (64 heads) over a contiguous range of an MLA latent
-// cache, on one 4-wavefront workgroup: the shared core of the split-KV
-// decode kernel and the MLA prefill kernel.
+// Building blocks of the MLA attention core: attention of one query's 64
+// heads over a range of an MLA latent cache in 32-token LDS tiles. The
+// pipeline that runs them (roles, stages, barriers) is in mla_ws.h.
 //
 // What it computes: "How GPUs Share a Long Context During LLM Inference",
 // 1.3 and 3.2-3.4 -- all heads of a query read one latent vector per token;
@@ -10,20 +10,15 @@
 // (O, running max, running sum) of the online softmax over the range.
 //
 // Design (gfx950):
-//  * 32-token tiles of the latent are staged in LDS by direct global -> LDS
-//    loads: bf16 keeps 4 stages (3 tiles in flight while one is consumed),
-//    FP8 keeps 4 raw stages plus 2 converted bf16 tiles; the next tile's
-//    loads are spread over the QK steps of the current one;
-//  * QK: wave w computes S^T = K Q^T for heads 16w..16w+15 with
+//  * QK (qk_tile): wave w computes S^T = K Q^T for heads 16w..16w+15 with
 //    v_mfma_f32_16x16x32_bf16 (A = 16 tokens x 32 dims from the LDS tile,
 //    B = Q^T held in registers for the whole range); each lane ends with 8
 //    scores of one head, the head's row max takes two row-swap permutes;
-//  * the wave turns its scores into bf16 probabilities P and writes them to
-//    LDS (one 16-byte store per lane) together with each head's rescale
-//    factor; one barrier later
-//  * PV: wave w accumulates O^T for value dims [128w, 128w+128) of all 64
-//    heads: A = V^T read from the same latent tile with ds_read_b64_tr_b16
-//    (each read feeds 4 MFMAs, one per head block), B = P^T from LDS. The
+//  * the softmax pieces (soft_*) turn the scores into bf16 probabilities P,
+//    stored to LDS (one 16-byte store per lane) with each head's rescale
+//    factor;
+//  * PV: A = V^T read from the same latent tile with ds_read_b64_tr_b16
+//    (each read feeds 4 MFMAs, one per head block), B = P^T from LDS; the
 //    32 tokens of a k-step are taken in the order the score registers hold
 //    them, so P needs no shuffle;
 //  * the softmax reference max only moves when a score exceeds it by more
@@ -52,7 +47,7 @@ constexpr int kH = 64;          // query heads sharing the latent
 constexpr int kDk = 576;        // QK dims (latent)
 constexpr int kDv = 512;        // PV dims (leading part of the latent)
 constexpr int kBN = 32;         // tokens per LDS tile
-constexpr int kThreads = 256;   // 4 wavefronts
+constexpr int kThreads = 256;   // threads of one role (4 wavefronts)
 constexpr int kRowChunks = kDk / 8;               // 72 chunks of 16 B per bf16 row
 constexpr int kTileChunks = kBN * kRowChunks;     // 2304
 constexpr int kTileBytes = kTileChunks * 16;      // 36864
@@ -157,24 +152,6 @@ __device__ __forceinline__ LdsBases lds_bases(int w, int g, int c) {
       L.pv[rr][m4] = row * (kRowChunks * 16) + 256 * w + swz(row, 2 * m4 + ((c & 3) >> 1)) * 16 + 8 * (c & 1);
   }
   return L;
-}
-
-struct State {
-  f32x4 oacc[kMv][4];  // PV role: O^T dims 128w + 16m + 4g + i, head 16 hb + c
-  float m_run;         // QK role: running reference max of head 16w + c (log2 domain)
-  float l_run;         // QK role: this lane's share of that head's running sum
-};
-
-__device__ __forceinline__ void init_state(State& st) {
-#pragma unroll
-  for (int m = 0; m < kMv; ++m)
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-      st.oacc[m][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      asm volatile("" : "+a"(st.oacc[m][hb]));
-    }
-  st.m_run = -INFINITY;
-  st.l_run = 0.f;
 }
 
 // Q^T operand of the QK role: lane (g, c) holds q[16w + c][32s + 8g .. +8]
@@ -316,442 +293,16 @@ __device__ __forceinline__ void soft_store(Soft& sm, St& st, char* pbuf, float* 
   if (g == 0) abuf[16 * w + c] = sm.alpha;
 }
 
-// Interleave `n` MFMAs of the current scheduling region with the VALU work
-// placed in it (1 MFMA, then up to `v` VALU instructions).
-template <int N, int V>
-__device__ __forceinline__ void interleave_mfma_valu() {
-#pragma unroll
-  for (int k = 0; k < N; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
-  }
-}
-
-// One pipeline step (see above). kNext: tile nxt exists (QK + softmax of it);
-// ts: the token scales of tile nxt (FP8).
-// pv_hook(m) runs in PV m-step m (the FP8 path converts its next tile there,
-// where the LDS is far less busy than during QK).
-// kMask / vmask: selection bits of tile nxt (see soft_scores).
-template <bool kNext, bool kFp8 = false, bool kMask = false, typename Hook, typename PvHook>
-__device__ __forceinline__ void pipe_step(const char* cur, const char* nxt, int nvalid_nxt, int buf, int w, int g,
-                                          int c, const LdsBases& L, const bf16x8 (&qreg)[kQSteps], float scale_log2,
-                                          State& st, const Lds& S, Hook&& hook, PvHook&& pv_hook,
-                                          const TokScale& ts = TokScale{}, uint32_t vmask = 0xffffffffu) {
-  constexpr int kAheadV = 4;
-  bf16x8 va[kMv];
-  auto load_v = [&](int m) {
-    va[m] = join_tr(lds_read_tr(cur + L.pv[0][m & 3] + 128 * (m >> 2)),
-                    lds_read_tr(cur + L.pv[1][m & 3] + 128 * (m >> 2)));
-  };
-  // P_i and alpha_i are read first: their LDS latency then hides behind the
-  // QK MFMAs instead of stalling the start of PV
-  const float* acur = S.alpha + kH * buf;
-  const char* pcur = S.p + kH * kPRowBytes * buf;
-  float al[4];
-  bf16x8 pb[4];
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    al[hb] = acur[16 * hb + c];
-    pb[hb] = *reinterpret_cast<const bf16x8*>(pcur + p_off(16 * hb + c, g));
-  }
-  f32x4 sacc[2];
-  if constexpr (kNext) {
-    qk_tile(nxt, L, qreg, sacc, hook, load_v);
-  } else {
-#pragma unroll
-    for (int m = 0; m < kAheadV; ++m) load_v(m);
-  }
-  // ---- alpha_i: rescale O (rare) ----
-  if (__any(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
-#pragma unroll
-    for (int m = 0; m < kMv; ++m)
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) {
-        asm volatile("" : "+a"(st.oacc[m][hb]));
-        st.oacc[m][hb] *= al[hb];
-        asm volatile("" : "+a"(st.oacc[m][hb]));
-      }
-  }
-  // ---- PV_i with softmax_{i+1} in the MFMA shadows ----
-  Soft sm;
-#pragma unroll
-  for (int m = 0; m < kMv; ++m) {
-    if (m + kAheadV < kMv) load_v(m + kAheadV);
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-      st.oacc[m][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb[hb], st.oacc[m][hb], 0, 0, 0);
-      asm volatile("" : "+a"(st.oacc[m][hb]));
-    }
-    if constexpr (kNext) {
-      if (m == 0) soft_scores<kFp8, kMask>(sm, sacc, nvalid_nxt, g, scale_log2, ts, vmask);
-      if (m == 1) soft_ref(sm, st);
-      if (m == 2) soft_exp<kFp8, 0, kMask>(sm, st, ts);
-      if (m == 3) soft_exp<kFp8, 4, kMask>(sm, st, ts);
-      if (m == 4) soft_store(sm, st, S.p + kH * kPRowBytes * (buf ^ 1), S.alpha + kH * (buf ^ 1), w, g, c);
-      if (m <= 4) interleave_mfma_valu<4, 6>();
-    }
-    pv_hook(m);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// Tokens [t0, t1) of a bf16 latent cache (`base` = token 0, `c_t` elements
-// per token) through the core. Step i consumes tile (i + rot) mod ntiles:
-// the softmax state does not depend on the order of the tiles, and a
-// workgroup-specific rotation keeps the many workgroups that stream equally
-// aligned ranges at the same rate from addressing the same HBM channels in
-// lockstep. Stage i % 4 holds step i's tile; tokens past t1 in the last tile
-// re-read token t1 - 1 and are masked. Needs S.p and S.alpha with room for
-// two buffers.
-template <Policy P>
-__device__ __forceinline__ void run_bf16(const uint16_t* base, int64_t c_t, int64_t t0, int64_t t1, int w, int g,
-                                         int c, const LdsBases& L, const bf16x8 (&qreg)[kQSteps], float scale_log2,
-                                         State& st, const Lds& S, uint32_t rot_seed = 0) {
-  const int tid = threadIdx.x;
-  const int ntok = (int)(t1 - t0);
-  const int ntiles = (ntok + kBN - 1) / kBN;
-  if (ntiles <= 0) return;
-  const int rot = (int)(rot_seed % (uint32_t)ntiles);
-  auto phys = [&](int i) { const int t = i + rot; return t >= ntiles ? t - ntiles : t; };
-  uint32_t toff[kLdChunks];  // byte offset of this thread's chunks inside a full tile
-#pragma unroll
-  for (int k = 0; k < kLdChunks; ++k) {
-    const int Pc = tid + kThreads * k;
-    const int row = Pc / kRowChunks, pc = Pc % kRowChunks;
-    toff[k] = (uint32_t)((row * c_t + swz(row, pc) * 8) * 2);
-  }
-  auto tile_ptr = [&](int i) -> const char* { return S.tiles + (i & 3) * kTileBytes; };
-  auto stage = [&](int i) { return S.tiles + (i & 3) * kTileBytes + 64 * w * 16; };
-  auto issue = [&](int i) {
-    const int64_t tok0 = t0 + (int64_t)phys(i) * kBN;
-    char* dst0 = stage(i);
-    if (tok0 + kBN <= t1) {
-      const uint16_t* tb = base + tok0 * c_t;
-#pragma unroll
-      for (int k = 0; k < kLdChunks; ++k) lds_dma16_sbase<P>(tb, toff[k], lds_addr(dst0 + kThreads * k * 16));
-    } else {
-#pragma unroll
-      for (int k = 0; k < kLdChunks; ++k) {
-        const int Pc = tid + kThreads * k;
-        const int row = Pc / kRowChunks, pc = Pc % kRowChunks;
-        const int64_t tok = min(tok0 + row, t1 - 1);
-        lds_dma16<P>(base + tok * c_t + swz(row, pc) * 8, lds_addr(dst0 + kThreads * k * 16));
-      }
-    }
-  };
-  auto nvalid = [&](int i) { return min(kBN, ntok - kBN * phys(i)); };
-  for (int i = 0; i < 3 && i < ntiles; ++i) issue(i);
-  // ---- prologue: S_0 and P_0 ----
-  wait_ahead<kLdChunks>(min(2, ntiles - 1));  // tile 0 landed
-  __syncthreads();
-  {
-    f32x4 sacc[2];
-    qk_tile(tile_ptr(0), L, qreg, sacc, [](int) {}, [](int) {});
-    Soft sm;
-    const TokScale none{};
-    soft_scores<false>(sm, sacc, nvalid(0), g, scale_log2, none);
-    soft_ref(sm, st);
-    soft_exp<false, 0>(sm, st, none);
-    soft_exp<false, 4>(sm, st, none);
-    soft_store(sm, st, S.p, S.alpha, w, g, c);
-  }
-  // ---- steady state ----
-  for (int i = 0; i + 1 < ntiles; ++i) {
-    wait_ahead<kLdChunks>(min(1, ntiles - 2 - i));  // tile i+1 landed
-    __syncthreads();  // P_i and tile i+1 visible; every wave is done with tile i-1 and P_{i-1}
-    // tile i+3 goes into the stage tile i-1 used: a full tile's loads are
-    // spread over the QK steps of tile i+1 (one every other step), the
-    // clamped last tile is issued at once
-    const int64_t nxt0 = t0 + (int64_t)phys(i + 3 < ntiles ? i + 3 : 0) * kBN;
-    const bool spread = (i + 3 < ntiles) && (nxt0 + kBN <= t1);
-    if (i + 3 < ntiles && !spread) issue(i + 3);
-    const uint64_t ntb = uniform_ptr(base + nxt0 * c_t);
-    const uint32_t ndst = __builtin_amdgcn_readfirstlane(lds_addr(stage(i + 3)));
-    pipe_step<true>(tile_ptr(i), tile_ptr(i + 1), nvalid(i + 1), i & 1, w, g, c, L, qreg, scale_log2, st, S,
-                    [&](int s) {
-                      if (spread && (s & 1) == 0 && (s >> 1) < kLdChunks)
-                        lds_dma16_s<P>(ntb, toff[s >> 1], ndst + kThreads * (s >> 1) * 16);
-                    },
-                    [](int) {});
-  }
-  __syncthreads();  // P of the last tile visible
-  pipe_step<false>(tile_ptr(ntiles - 1), nullptr, 0, (ntiles - 1) & 1, w, g, c, L, qreg, scale_log2, st, S,
-                   [](int) {}, [](int) {});
-}
-
-// Tokens [t0, t1) of an FP8 E4M3 latent cache with one fp32 scale per token
-// (entry = e4m3 * scale_t), through the same pipeline as bf16. The cache
-// bytes stream into registers two tiles ahead of use (nontemporal vector
-// loads: each thread holds 9 units of 8 bytes of a tile); during the PV
-// MFMAs of step i each unit of tile i+2 is converted to bf16 exactly
-// (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and written to its swizzled LDS
-// position, and its register is refilled with tile i+4. Three bf16 stages:
-// tile i (PV), tile i+1 (QK), tile i+2 (being written). The scales are
-// loaded into registers one step ahead of the softmax that folds them in.
-// Tile order rotated as in run_bf16. kPol = kStream marks the loads
-// nontemporal (a range read once), kReuse leaves them cached (a range other
-// workgroups read too).
-template <Policy kPol = Policy::kStream>
-__device__ __forceinline__ void run_fp8(const uint8_t* base, int64_t c_t, const float* sbase, int64_t s_t, int64_t t0,
-                                        int64_t t1, int w, int g, int c, const LdsBases& L,
-                                        const bf16x8 (&qreg)[kQSteps], float scale_log2, State& st, const Lds& S,
-                                        uint32_t rot_seed = 0) {
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  const int tid = threadIdx.x;
-  const int ntok = (int)(t1 - t0);
-  const int ntiles = (ntok + kBN - 1) / kBN;
-  if (ntiles <= 0) return;
-  const int rot = (int)(rot_seed % (uint32_t)ntiles);
-  auto phys = [&](int i) { const int t = i + rot; return t >= ntiles ? t - ntiles : t; };
-  auto nvalid = [&](int i) { return min(kBN, ntok - kBN * phys(i)); };
-  auto stage = [&](int i) -> char* { return S.tiles + (i % 3) * kTileBytes; };
-  // unit j of this thread: 8 cache bytes of row u / 72, chunk u % 72 (u = tid + 256 j)
-  uint32_t goff[kLdChunks], loff[kLdChunks];
-  int urow[kLdChunks];
-#pragma unroll
-  for (int j = 0; j < kLdChunks; ++j) {
-    const int u = tid + kThreads * j;
-    const int row = u / kRowChunks, ch = u % kRowChunks;
-    urow[j] = row;
-    goff[j] = (uint32_t)(ch * 8);
-    loff[j] = (uint32_t)(row * (kRowChunks * 16) + swz(row, ch) * 16);
-  }
-  u32x2 raw[2][kLdChunks];
-  TokScale tsc[2];
-  // Addresses: a wavefront-uniform tile base plus a 32-bit lane offset; rows
-  // past the range's last token re-read it (lim = last valid row). The host
-  // bounds the token stride so that 32 rows fit 32-bit offsets.
-  const uint32_t ct32 = (uint32_t)c_t, st32 = (uint32_t)s_t;
-  auto load_unit = [&](int i, int j, u32x2& r) {
-    const int64_t tok0 = t0 + (int64_t)phys(i) * kBN;
-    const int lim = (int)min((int64_t)(kBN - 1), t1 - 1 - tok0);
-    const uint8_t* tb = base + tok0 * c_t;
-    const uint32_t off = (uint32_t)min(urow[j], lim) * ct32 + goff[j];
-    if constexpr (kPol == Policy::kStream)
-      r = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tb + off));
-    else
-      r = *reinterpret_cast<const u32x2*>(tb + off);
-  };
-  auto load_scales = [&](int i, TokScale& ts) {
-    const int64_t tok0 = t0 + (int64_t)phys(i) * kBN;
-    const int lim = (int)min((int64_t)(kBN - 1), t1 - 1 - tok0);
-    const float* sb = sbase + tok0 * s_t;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if constexpr (kPol == Policy::kStream)
-        ts.v[j] = __builtin_nontemporal_load(sb + (uint32_t)min(16 * (j >> 2) + 4 * g + (j & 3), lim) * st32);
-      else
-        ts.v[j] = sb[(uint32_t)min(16 * (j >> 2) + 4 * g + (j & 3), lim) * st32];
-  };
-  auto convert_unit = [&](const u32x2& r, int j, char* tile) {
-    const uint32_t o0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, false));
-    const uint32_t o1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, true));
-    const uint32_t o2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, false));
-    const uint32_t o3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, true));
-    *reinterpret_cast<uint4*>(tile + loff[j]) = make_uint4(o0, o1, o2, o3);
-  };
-
-  // ---- prologue: tiles 0, 1 converted; tiles 2, 3 in flight; S_0 and P_0 ----
-  auto clampt = [&](int i) { return min(i, ntiles - 1); };
-#pragma unroll
-  for (int j = 0; j < kLdChunks; ++j) load_unit(0, j, raw[0][j]);
-  load_scales(0, tsc[0]);
-#pragma unroll
-  for (int j = 0; j < kLdChunks; ++j) load_unit(clampt(1), j, raw[1][j]);
-  load_scales(clampt(1), tsc[1]);
-#pragma unroll
-  for (int j = 0; j < kLdChunks; ++j) {
-    convert_unit(raw[0][j], j, stage(0));
-    load_unit(clampt(2), j, raw[0][j]);
-  }
-#pragma unroll
-  for (int j = 0; j < kLdChunks; ++j) {
-    convert_unit(raw[1][j], j, stage(1));
-    load_unit(clampt(3), j, raw[1][j]);
-  }
-  __syncthreads();
-  {
-    f32x4 sacc[2];
-    qk_tile(stage(0), L, qreg, sacc, [](int) {}, [](int) {});
-    Soft sm;
-    soft_scores<true>(sm, sacc, nvalid(0), g, scale_log2, tsc[0]);
-    soft_ref(sm, st);
-    soft_exp<true, 0>(sm, st, tsc[0]);
-    soft_exp<true, 4>(sm, st, tsc[0]);
-    soft_store(sm, st, S.p, S.alpha, w, g, c);
-  }
-  // ---- steady state, two steps per trip so the register sets are static ----
-  // The loads and conversions of a step are unconditional (past the last
-  // tile they re-read the last tile and write a stage nobody reads again):
-  // loads under a branch make the compiler's wait placement fall back to
-  // waiting for every outstanding load, which would drain the stream.
-  auto step = [&](int i, auto parity) {
-    constexpr int P = decltype(parity)::value;  // i & 1
-    __syncthreads();  // P_i and bf16 tile i+1 visible; every wave is done with tile i-1 and P_{i-1}
-    const int conv_t = min(i + 2, ntiles - 1), refill_t = min(i + 4, ntiles - 1);
-    char* dst = stage(i + 2);
-    pipe_step<true, true>(stage(i), stage(i + 1), nvalid(i + 1), P, w, g, c, L, qreg, scale_log2, st, S,
-                          [&](int s) {
-                            if (s == 1) load_scales(conv_t, tsc[P]);  // tile i's scales are spent
-                          },
-                          [&](int m) {  // units 0-1 at m-step 0, one per m-step after
-#pragma unroll
-                            for (int j = (m == 0 ? 0 : m + 1); j <= m + 1; ++j) {
-                              convert_unit(raw[P][j], j, dst);
-                              load_unit(refill_t, j, raw[P][j]);
-                            }
-                          },
-                          tsc[P ^ 1]);
-  };
-  int i = 0;
-  for (; i + 2 < ntiles; i += 2) {
-    step(i, std::integral_constant<int, 0>{});
-    step(i + 1, std::integral_constant<int, 1>{});
-  }
-  if (i + 1 < ntiles) {
-    step(i, std::integral_constant<int, 0>{});
-    ++i;
-  }
-  __syncthreads();  // P of the last tile visible
-  pipe_step<false>(stage(ntiles - 1), nullptr, 0, (ntiles - 1) & 1, w, g, c, L, qreg, scale_log2, st, S, [](int) {},
-                   [](int) {});
-}
-
-// ---- index-list (sparse) attention ----
-// The tokens are the cache rows named by entries [0, ntok) of an index list
-// (Long Context 2.4: a sparse-attention query brings its own list). Entry
+// ---- index-list (sparse) attention: the LDS ring of list entries ----
+// (Long Context 2.4: a sparse-attention query brings its own list.) Entry
 // values outside [0, nrows) are no selection: their scores are masked and
-// their loads read row 0. Each wavefront copies the entries of a tile into
-// its own LDS ring slot with one 4-byte-per-lane direct load (lane l: entry
-// l mod 32), five tiles ahead of use, so the index values never pass through
-// registers the compiler would have to wait for. Per step i, in this order:
-// the entries of tile i+5, then the nine row loads of tile i+3 (addresses
-// from the ring, spread over the QK steps of tile i+1). Since vector-memory
-// loads complete in issue order, the wait at the top of step i for tile i+1
-// (at most 1 + 9 loads issued after it) also covers the entries of tiles up
-// to i+3; the ring slot of tile i is rewritten (step i) only after its last
-// readers (the address reads of step i-3, the selection mask of step i-1).
+// their loads read row 0. A loading wavefront copies the entries of a tile
+// into its own ring slot with one 4-byte-per-lane direct load (lane l: entry
+// l mod 32), five tiles ahead of use, so the index values never pass
+// through registers the compiler would have to wait for (see ws_pv_gather).
 constexpr int kIdxSlots = 5;
 constexpr int kIdxSlotBytes = 256;                          // 64 lanes x 4 B
 constexpr int kIdxRingBytes = 4 * kIdxSlots * kIdxSlotBytes;  // per workgroup (4 waves)
-
-template <Policy P>
-__device__ __forceinline__ void run_bf16_gather(const uint16_t* base, int64_t c_t, const int32_t* ilist, int ntok,
-                                                int nrows, int w, int g, int c, const LdsBases& L,
-                                                const bf16x8 (&qreg)[kQSteps], float scale_log2, State& st,
-                                                const Lds& S, char* ring, uint32_t rot_seed = 0) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int ntiles = (ntok + kBN - 1) / kBN;
-  if (ntiles <= 0) return;
-  const int rot = (int)(rot_seed % (uint32_t)ntiles);
-  auto phys = [&](int i) { const int t = i + rot; return t >= ntiles ? t - ntiles : t; };
-  auto nvalid = [&](int i) { return min(kBN, ntok - kBN * phys(i)); };
-  const uint32_t rowbytes = (uint32_t)c_t * 2u;  // the host bounds nrows * rowbytes below 2^32
-  // this thread's chunks of a tile: tile row (high half) and swizzled source byte offset
-  uint32_t rinfo[kLdChunks];
-#pragma unroll
-  for (int k = 0; k < kLdChunks; ++k) {
-    const int Pc = tid + kThreads * k;
-    const int row = Pc / kRowChunks, pc = Pc % kRowChunks;
-    rinfo[k] = ((uint32_t)row << 16) | (uint32_t)(swz(row, pc) * 16);
-  }
-  const char* wring = ring + w * (kIdxSlots * kIdxSlotBytes);
-  const uint32_t wring_lds = __builtin_amdgcn_readfirstlane(lds_addr(wring));
-  const uint64_t ibase = uniform_ptr(ilist), cbase = uniform_ptr(base);
-  auto slot = [&](int T) { return (T % kIdxSlots) * kIdxSlotBytes; };
-  auto issue_idx = [&](int T) {
-    const int Tc = T < ntiles ? T : ntiles - 1;  // past the end: re-read the last tile's entries
-    const int e = min(kBN * phys(Tc) + (lane & 31), ntok - 1);
-    lds_dma4_s<Policy::kReuse>(ibase, (uint32_t)e * 4u, wring_lds + (uint32_t)slot(T));
-  };
-  auto row_of = [&](int T, int row) -> uint32_t {
-    const int v = *reinterpret_cast<const int*>(wring + slot(T) + 4 * row);
-    return (uint32_t)v < (uint32_t)nrows ? (uint32_t)v : 0u;
-  };
-  auto offsets = [&](int T, uint32_t (&voff)[kLdChunks]) {
-#pragma unroll
-    for (int k = 0; k < kLdChunks; ++k) voff[k] = row_of(T, (int)(rinfo[k] >> 16)) * rowbytes + (rinfo[k] & 0xffffu);
-  };
-  auto tile_mask = [&](int T) -> uint32_t {
-    const int v = *reinterpret_cast<const int*>(wring + slot(T) + 4 * (lane & 31));
-    return (uint32_t)__ballot((uint32_t)v < (uint32_t)nrows);
-  };
-  auto tile_ptr = [&](int i) -> const char* { return S.tiles + (i & 3) * kTileBytes; };
-  auto dst = [&](int i) {
-    return __builtin_amdgcn_readfirstlane(lds_addr(S.tiles + (i & 3) * kTileBytes + 64 * w * 16));
-  };
-  auto issue_tile = [&](int T) {
-    uint32_t voff[kLdChunks];
-    offsets(T, voff);
-    const uint32_t d = dst(T);
-#pragma unroll
-    for (int k = 0; k < kLdChunks; ++k) lds_dma16_s<P>(cbase, voff[k], d + kThreads * k * 16);
-  };
-  // ---- prologue: entries of tiles 0..4, rows of tiles 0..2 ----
-  issue_idx(0);
-  issue_idx(1);
-  issue_idx(2);
-  cpa::wait_vmcnt<2>();  // entries of tile 0
-  issue_tile(0);
-  issue_idx(3);
-  if (ntiles > 1) {
-    cpa::wait_vmcnt<11>();  // entries of tile 1 (then: 2, rows 0, 3)
-    issue_tile(1);
-  }
-  issue_idx(4);
-  if (ntiles > 2) {
-    cpa::wait_vmcnt<20>();  // entries of tile 2 (then: rows 0, 3, rows 1, 4)
-    issue_tile(2);
-  }
-  // rows of tile 0 landed (after them: entries 3, rows 1, entries 4, rows 2)
-  if (ntiles > 2) cpa::wait_vmcnt<20>();
-  else if (ntiles == 2) cpa::wait_vmcnt<11>();
-  else cpa::wait_vmcnt<2>();
-  __syncthreads();
-  {
-    f32x4 sacc[2];
-    qk_tile(tile_ptr(0), L, qreg, sacc, [](int) {}, [](int) {});
-    Soft sm;
-    const TokScale none{};
-    soft_scores<false, true>(sm, sacc, nvalid(0), g, scale_log2, none, tile_mask(0));
-    soft_ref(sm, st);
-    soft_exp<false, 0, true>(sm, st, none);
-    soft_exp<false, 4, true>(sm, st, none);
-    soft_store(sm, st, S.p, S.alpha, w, g, c);
-  }
-  // ---- steady state ----
-  for (int i = 0; i + 1 < ntiles; ++i) {
-    // rows of tile i+1 landed: after them only the entries of tile i+4 and the rows of tile i+2
-    if (i + 2 < ntiles) cpa::wait_vmcnt<10>();
-    else cpa::wait_vmcnt<1>();
-    __syncthreads();  // P_i and tile i+1 visible; every wave is done with tile i-1 and P_{i-1}
-    issue_idx(i + 5);
-    const bool more = i + 3 < ntiles;
-    uint32_t voff[kLdChunks];
-    offsets(i + 3, voff);
-    const uint32_t ndst = dst(i + 3);
-    pipe_step<true, false, true>(tile_ptr(i), tile_ptr(i + 1), nvalid(i + 1), i & 1, w, g, c, L, qreg, scale_log2,
-                                 st, S,
-                                 [&](int s) {
-                                   if (more && (s & 1) == 0 && (s >> 1) < kLdChunks)
-                                     lds_dma16_s<P>(cbase, voff[s >> 1], ndst + kThreads * (s >> 1) * 16);
-                                 },
-                                 [](int) {}, TokScale{}, tile_mask(i + 1));
-  }
-  __syncthreads();  // P of the last tile visible
-  pipe_step<false>(tile_ptr(ntiles - 1), nullptr, 0, (ntiles - 1) & 1, w, g, c, L, qreg, scale_log2, st, S,
-                   [](int) {}, [](int) {});
-  cpa::wait_vmcnt<0>();  // entry loads issued past the last tile have landed
-}
-
-// Closes the range: the softmax sum of every head into S.lsum (one barrier).
-// Returns this lane's QK-role head total (head 16w + c).
-__device__ __forceinline__ float finish(const State& st, int w, int g, int c, const Lds& S) {
-  const float l = sum4_rows(st.l_run);
-  if (g == 0) S.lsum[16 * w + c] = l;
-  __syncthreads();
-  return l;
-}
 
 }  // namespace mla
 }  // namespace cpa

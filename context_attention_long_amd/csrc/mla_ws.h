@@ -36,8 +36,10 @@ struct QkStat {
   float l_run;  // this lane's share of the head's running sum
 };
 
-// The tile sequence of a range: step i consumes tile (i + rot) mod ntiles
-// (see run_bf16 for the rotation).
+// The tile sequence of a range: step i consumes tile (i + rot) mod ntiles.
+// The rotation is a per-workgroup hash, so workgroups that start together do
+// not all read the same tile offsets of their ranges at once (the order of
+// tiles does not change the result beyond rounding: online softmax).
 struct Tiles {
   int64_t t0, t1;
   int ntok, ntiles, rot;
@@ -55,14 +57,80 @@ struct Tiles {
 
 __device__ __forceinline__ const char* ws_tile(const Lds& S, int i) { return S.tiles + (i & 3) * kTileBytes; }
 
+// FP8 tiles: a 32-token tile is 2304 units of 8 cache bytes (unit u: row
+// u / 72, chunk u % 72). The 512 threads share them: QK threads (t < 256)
+// take units 512 j + t (j < 4), PV threads also 512 j + t and one more,
+// 2048 + t - 256, so the raw registers of two tiles in flight stay small in
+// both roles. A unit is streamed into registers two tiles ahead and, two
+// steps later, converted exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8, scale
+// 1) into its swizzled LDS slot. Loads are unconditional (past the last tile
+// they re-read it) so the compiler never falls back to draining every load.
+template <int NU, Policy kPol>
+struct Fp8Units {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 raw[2][NU];
+  const uint8_t* base;
+  int64_t c_t;
+  int t;  // thread index in the workgroup
+  __device__ __forceinline__ int unit(int j) const { return j < 4 ? 512 * j + t : 2048 + t - 256; }
+  __device__ __forceinline__ void load(const Tiles& T, int i, int j, int set) {
+    const int64_t tok0 = T.t0 + (int64_t)T.phys(i) * kBN;
+    const int lim = (int)min((int64_t)(kBN - 1), T.t1 - 1 - tok0);
+    const int u = unit(j);
+    const uint8_t* tb = base + tok0 * c_t;
+    // the host bounds the token stride so that 32 rows fit 32-bit offsets
+    const uint32_t off = (uint32_t)min(u / kRowChunks, lim) * (uint32_t)c_t + (uint32_t)(u % kRowChunks) * 8u;
+    if constexpr (kPol == Policy::kStream)
+      raw[set][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tb + off));
+    else
+      raw[set][j] = *reinterpret_cast<const u32x2*>(tb + off);
+  }
+  __device__ __forceinline__ void convert(int j, int set, char* tile) const {
+    const u32x2 r = raw[set][j];
+    const uint32_t o0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, false));
+    const uint32_t o1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, true));
+    const uint32_t o2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, false));
+    const uint32_t o3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, true));
+    const int u = unit(j), row = u / kRowChunks;
+    *reinterpret_cast<uint4*>(tile + row * (kRowChunks * 16) + swz(row, u % kRowChunks) * 16) =
+        make_uint4(o0, o1, o2, o3);
+  }
+  // prologue, kConv = 2 (PV role): tiles 0 and 1 converted into stages 0 and
+  // 1, tile 2 in set 0, tile 3 in set 1. kConv = 1 (QK role, which converts
+  // one tile less ahead): tile 0 converted, tile 1 in set 1, tile 2 in set 0.
+  template <int kConv>
+  __device__ __forceinline__ void prologue(const Tiles& T, const Lds& S) {
+    const int n = T.ntiles;
+#pragma unroll
+    for (int j = 0; j < NU; ++j) load(T, 0, j, 0);
+#pragma unroll
+    for (int j = 0; j < NU; ++j) load(T, min(1, n - 1), j, 1);
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+      convert(j, 0, S.tiles);
+      load(T, min(2, n - 1), j, 0);
+    }
+    if constexpr (kConv == 2) {
+#pragma unroll
+      for (int j = 0; j < NU; ++j) {
+        convert(j, 1, S.tiles + kTileBytes);
+        load(T, min(3, n - 1), j, 1);
+      }
+    }
+  }
+};
+
 // QK role. Barriers: 1 (tile 0) + (ntiles - 1) (loop) + 1 (after the loop).
 // tile(i): LDS bf16 tile of step i. kFp8: scales(i, ts) loads the per-token
 // scales of tile i (two steps ahead of their use), folded into the scores
-// and P.
-template <bool kFp8, typename TileFn, typename ScaleFn>
+// and P. kMask: mask(i) gives the selection bits of tile i (index lists).
+// extra(i, parity) runs after the softmax of tile i (the FP8 path converts
+// its share of tile i+2 there).
+template <bool kFp8, bool kMask = false, typename TileFn, typename ScaleFn, typename MaskFn,
+          typename ExtraFn = void (*)(int, std::integral_constant<int, 0>)>
 __device__ __forceinline__ void ws_qk(const Tiles& T, int w, int g, int c, const LdsBases& L,
                                       const bf16x8 (&qreg)[kQSteps], float scale_log2, QkStat& st, const Lds& S,
-                                      TileFn&& tile, ScaleFn&& scales) {
+                                      TileFn&& tile, ScaleFn&& scales, MaskFn&& mask, ExtraFn&& extra = nullptr) {
   if (T.ntiles <= 0) return;
   TokScale tsc[2];
   auto clampt = [&](int i) { return min(i, T.ntiles - 1); };
@@ -75,12 +143,15 @@ __device__ __forceinline__ void ws_qk(const Tiles& T, int w, int g, int c, const
     f32x4 sacc[2];
     qk_tile(tile(i), L, qreg, sacc, [](int) {}, [](int) {});
     Soft sm;
-    soft_scores<kFp8>(sm, sacc, T.nvalid(i), g, scale_log2, tsc[P]);
+    soft_scores<kFp8, kMask>(sm, sacc, T.nvalid(i), g, scale_log2, tsc[P], kMask ? mask(i) : 0xffffffffu);
     soft_ref(sm, st);
-    soft_exp<kFp8, 0>(sm, st, tsc[P]);
-    soft_exp<kFp8, 4>(sm, st, tsc[P]);
+    soft_exp<kFp8, 0, kMask>(sm, st, tsc[P]);
+    soft_exp<kFp8, 4, kMask>(sm, st, tsc[P]);
     soft_store(sm, st, S.p + kH * kPRowBytes * P, S.alpha + kH * P, w, g, c);
-    if constexpr (kFp8) scales(clampt(i + 2), tsc[P]);  // tile i's scales are spent
+    if constexpr (kFp8) {
+      scales(clampt(i + 2), tsc[P]);  // tile i's scales are spent
+      extra(i, parity);
+    }
   };
   __syncthreads();  // tile 0 ready
   step(0, std::integral_constant<int, 0>{});
@@ -194,61 +265,20 @@ __device__ __forceinline__ void ws_pv(const Tiles& T, const uint16_t* base, int6
 }
 
 // PV role over an FP8 E4M3 cache (entry = e4m3 * scale_t; the scale is
-// folded into P by the QK role). The cache bytes stream into registers two
-// tiles ahead (each thread holds 9 units of 8 bytes of a tile; nontemporal
-// for kStream); during the PV MFMAs of step i each unit of tile i+2 is
-// converted to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1) into its
-// swizzled LDS slot of stage (i+2) % 3, and the register is refilled with
-// tile i+4. The loads and conversions are unconditional (past the last tile
-// they re-read it and write a stage nobody reads again): loads under a
-// branch make the compiler's waits fall back to draining every load.
+// folded into P by the QK role). During the PV MFMAs of step i each of this
+// thread's units of tile i+2 is converted into stage (i+2) % 3 and its
+// register refilled with tile i+4 (Fp8Units; the QK role does its share in
+// the same step).
 template <Policy kPol>
 __device__ __forceinline__ void ws_pv_fp8(const Tiles& T, const uint8_t* base, int64_t c_t, int tp, int w, int g,
                                           int c, const LdsBases& L, f32x4 (&oacc)[kMv][4], const Lds& S) {
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
   if (T.ntiles <= 0) return;
   auto stage = [&](int i) -> char* { return S.tiles + (i % 3) * kTileBytes; };
-  // unit j of this thread: 8 cache bytes of row u / 72, chunk u % 72 (u = tp + 256 j);
-  // recomputed where used (cheap next to the registers a table would hold)
-  auto urow = [&](int j) { return (tp + kThreads * j) / kRowChunks; };
-  auto uch = [&](int j) { return (tp + kThreads * j) % kRowChunks; };
-  u32x2 raw[2][kLdChunks];
-  const uint32_t ct32 = (uint32_t)c_t;  // the host bounds the token stride
-  auto load_unit = [&](int i, int j, u32x2& r) {
-    const int64_t tok0 = T.t0 + (int64_t)T.phys(i) * kBN;
-    const int lim = (int)min((int64_t)(kBN - 1), T.t1 - 1 - tok0);
-    const uint8_t* tb = base + tok0 * c_t;
-    const uint32_t off = (uint32_t)min(urow(j), lim) * ct32 + (uint32_t)(uch(j) * 8);
-    if constexpr (kPol == Policy::kStream)
-      r = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tb + off));
-    else
-      r = *reinterpret_cast<const u32x2*>(tb + off);
-  };
-  auto convert_unit = [&](const u32x2& r, int j, char* tile) {
-    const uint32_t o0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, false));
-    const uint32_t o1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, true));
-    const uint32_t o2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, false));
-    const uint32_t o3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, true));
-    const int row = urow(j);
-    *reinterpret_cast<uint4*>(tile + row * (kRowChunks * 16) + swz(row, uch(j)) * 16) = make_uint4(o0, o1, o2, o3);
-  };
+  Fp8Units<5, kPol> U;
+  U.base = base, U.c_t = c_t, U.t = 256 + tp;
   const int n = T.ntiles;
   auto clampt = [&](int i) { return min(i, n - 1); };
-  // ---- prologue: tiles 0 and 1 converted, tiles 2 and 3 in registers ----
-#pragma unroll
-  for (int j = 0; j < kLdChunks; ++j) load_unit(0, j, raw[0][j]);
-#pragma unroll
-  for (int j = 0; j < kLdChunks; ++j) load_unit(clampt(1), j, raw[1][j]);
-#pragma unroll
-  for (int j = 0; j < kLdChunks; ++j) {
-    convert_unit(raw[0][j], j, stage(0));
-    load_unit(clampt(2), j, raw[0][j]);
-  }
-#pragma unroll
-  for (int j = 0; j < kLdChunks; ++j) {
-    convert_unit(raw[1][j], j, stage(1));
-    load_unit(clampt(3), j, raw[1][j]);
-  }
+  U.template prologue<2>(T, S);
   __syncthreads();
 
   constexpr int kAheadV = 2;  // V operands read ahead (registers are tight next to the FP8 units)
@@ -291,11 +321,10 @@ __device__ __forceinline__ void ws_pv_fp8(const Tiles& T, const uint8_t* base, i
     __syncthreads();  // P_i visible; every wave is done with tile i-1's stage
     const int refill_t = clampt(i + 4);
     char* dst = stage(i + 2);
-    pv(i, [&](int m) {  // units 0-1 at m-step 0, one per m-step after
-#pragma unroll
-      for (int j = (m == 0 ? 0 : m + 1); j <= m + 1; ++j) {
-        convert_unit(raw[P][j], j, dst);
-        load_unit(refill_t, j, raw[P][j]);
+    pv(i, [&](int m) {  // one unit per m-step from m-step 1
+      if (m >= 1 && m <= 5) {
+        U.convert(m - 1, P, dst);
+        U.load(T, refill_t, m - 1, P);
       }
     });
   };
@@ -310,6 +339,136 @@ __device__ __forceinline__ void ws_pv_fp8(const Tiles& T, const uint8_t* base, i
   }
   __syncthreads();  // P of the last tile visible
   pv(n - 1, [](int) {});
+}
+
+// PV role of index-list (sparse) attention: the rows of a tile are the cache
+// rows named by list entries (index ring: mla_core.h, kIdxSlots). Each PV
+// wavefront copies the 32 entries of a tile into its own LDS
+// ring slot (one 4-byte direct load per lane), five tiles ahead; per step
+// i: the entries of tile i+5, then the nine row loads of tile i+3 with
+// addresses from the ring (spread over the m-steps). Vector-memory loads
+// complete in issue order, so the wait for tile i+1 (at most 1 + 9 later
+// loads) also covers the entries of tiles up to i+3. The QK wavefronts read
+// the selection bits of a tile from the ring of the PV wavefront with the
+// same index after the barrier that publishes the tile.
+template <Policy P>
+__device__ __forceinline__ void ws_pv_gather(const Tiles& T, const uint16_t* base, int64_t c_t, const int32_t* ilist,
+                                             int nrows, int tp, int w, int g, int c, const LdsBases& L,
+                                             f32x4 (&oacc)[kMv][4], const Lds& S, char* ring) {
+  if (T.ntiles <= 0) return;
+  const int lane = tp & 63;
+  const int n = T.ntiles;
+  const uint32_t rowbytes = (uint32_t)c_t * 2u;  // the host bounds nrows * rowbytes below 2^32
+  uint32_t rinfo[kLdChunks];  // tile row (high half) and swizzled source byte offset of this thread's chunks
+#pragma unroll
+  for (int k = 0; k < kLdChunks; ++k) {
+    const int Pc = tp + kThreads * k;
+    const int row = Pc / kRowChunks, pc = Pc % kRowChunks;
+    rinfo[k] = ((uint32_t)row << 16) | (uint32_t)(swz(row, pc) * 16);
+  }
+  const char* wring = ring + w * (kIdxSlots * kIdxSlotBytes);
+  const uint32_t wring_lds = __builtin_amdgcn_readfirstlane(lds_addr(wring));
+  const uint64_t ibase = uniform_ptr(ilist), cbase = uniform_ptr(base);
+  auto slot = [&](int t) { return (t % kIdxSlots) * kIdxSlotBytes; };
+  auto issue_idx = [&](int t) {
+    const int tc = t < n ? t : n - 1;  // past the end: re-read the last tile's entries
+    const int e = min(kBN * T.phys(tc) + (lane & 31), T.ntok - 1);
+    lds_dma4_s<Policy::kReuse>(ibase, (uint32_t)e * 4u, wring_lds + (uint32_t)slot(t));
+  };
+  auto row_of = [&](int t, int row) -> uint32_t {
+    const int v = *reinterpret_cast<const int*>(wring + slot(t) + 4 * row);
+    return (uint32_t)v < (uint32_t)nrows ? (uint32_t)v : 0u;
+  };
+  auto offsets = [&](int t, uint32_t (&voff)[kLdChunks]) {
+#pragma unroll
+    for (int k = 0; k < kLdChunks; ++k) voff[k] = row_of(t, (int)(rinfo[k] >> 16)) * rowbytes + (rinfo[k] & 0xffffu);
+  };
+  auto dst = [&](int t) {
+    return __builtin_amdgcn_readfirstlane(lds_addr(S.tiles + (t & 3) * kTileBytes + 64 * w * 16));
+  };
+  auto issue_tile = [&](int t) {
+    uint32_t voff[kLdChunks];
+    offsets(t, voff);
+    const uint32_t d = dst(t);
+#pragma unroll
+    for (int k = 0; k < kLdChunks; ++k) lds_dma16_s<P>(cbase, voff[k], d + kThreads * k * 16);
+  };
+  // ---- prologue: entries of tiles 0..4, rows of tiles 0..2 ----
+  issue_idx(0);
+  issue_idx(1);
+  issue_idx(2);
+  wait_vmcnt<2>();  // entries of tile 0
+  issue_tile(0);
+  issue_idx(3);
+  if (n > 1) {
+    wait_vmcnt<11>();  // entries of tile 1 (then: 2, rows 0, 3)
+    issue_tile(1);
+  }
+  issue_idx(4);
+  if (n > 2) {
+    wait_vmcnt<20>();  // entries of tile 2 (then: rows 0, 3, rows 1, 4)
+    issue_tile(2);
+  }
+  // rows of tile 0 landed (after them: entries 3, rows 1, entries 4, rows 2)
+  if (n > 2) wait_vmcnt<20>();
+  else if (n == 2) wait_vmcnt<11>();
+  else wait_vmcnt<2>();
+  __syncthreads();
+
+  constexpr int kAheadV = 4;
+  auto pv = [&](int i, auto&& hook) {
+    const char* cur = ws_tile(S, i);
+    const float* acur = S.alpha + kH * (i & 1);
+    const char* pcur = S.p + kH * kPRowBytes * (i & 1);
+    float al[4];
+    bf16x8 pb[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      al[hb] = acur[16 * hb + c];
+      pb[hb] = *reinterpret_cast<const bf16x8*>(pcur + p_off(16 * hb + c, g));
+    }
+    bf16x8 va[kMv];
+    auto load_v = [&](int m) {
+      va[m] = join_tr(lds_read_tr(cur + L.pv[0][m & 3] + 128 * (m >> 2)),
+                      lds_read_tr(cur + L.pv[1][m & 3] + 128 * (m >> 2)));
+    };
+#pragma unroll
+    for (int m = 0; m < kAheadV; ++m) load_v(m);
+    if (__any(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
+#pragma unroll
+      for (int m = 0; m < kMv; ++m)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) oacc[m][hb] *= al[hb];
+    }
+#pragma unroll
+    for (int m = 0; m < kMv; ++m) {
+      if (m + kAheadV < kMv) load_v(m + kAheadV);
+      hook(m);
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        oacc[m][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb[hb], oacc[m][hb], 0, 0, 0);
+    }
+  };
+  for (int i = 0; i + 1 < n; ++i) {
+    // rows of tile i+1 landed: after them only the entries of tile i+4 and the rows of tile i+2
+    if (i + 2 < n) wait_vmcnt<10>();
+    else wait_vmcnt<1>();
+    __syncthreads();  // P_i and tile i+1 visible; every wave is done with tile i-1 and P_{i-1}
+    issue_idx(i + 5);
+    const bool more = i + 3 < n;
+    uint32_t voff[kLdChunks];
+    offsets(i + 3, voff);
+    const uint32_t ndst = dst(i + 3);
+    pv(i, [&](int m) {
+      if (more) {
+        if (m == 0) lds_dma16_s<P>(cbase, voff[0], ndst);
+        lds_dma16_s<P>(cbase, voff[m + 1], ndst + kThreads * (m + 1) * 16);
+      }
+    });
+  }
+  __syncthreads();  // P of the last tile visible
+  pv(n - 1, [](int) {});
+  wait_vmcnt<0>();  // entry loads issued past the last tile have landed
 }
 
 }  // namespace mla

@@ -8,7 +8,7 @@
 // several ranks combine with the LSE merge (DeepSeek-V4 notes, 5.2).
 //
 // One workgroup per (query, split): the split's share of the query's list
-// runs through the shared MLA core (mla_core.h, run_bf16_gather), which
+// runs through the wave-specialised MLA core (mla_ws.h, ws_pv_gather), which
 // gathers the listed rows into LDS tiles with direct loads whose addresses
 // come from the list itself (staged in LDS ahead of use). The splits of a
 // query are merged by the LSE merge.
@@ -16,13 +16,14 @@
 
 #include "internal.h"
 #include "mla_core.h"
+#include "mla_ws.h"
 
 namespace {
 
 using namespace cpa::mla;
 
 template <cpa::Policy kP>
-__global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(cpa::SparseMlaArgs a) {
+__global__ __launch_bounds__(kWsThreads, 1) void sparse_mla_kernel(cpa::SparseMlaArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
   __shared__ __attribute__((aligned(16))) char ring[kIdxRingBytes];
@@ -32,7 +33,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(cpa::SparseMlaA
   const int split = (int)(blockIdx.x % a.nsplit);
   const int n = (int)(blockIdx.x / a.nsplit);
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int w = (tid >> 6) & 3, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const bool qk_role = tid < 256;
 
   int b = a.req ? a.req[n] : n;
   int cnt = a.n_idx ? a.n_idx[n] : a.K;
@@ -40,29 +42,46 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(cpa::SparseMlaA
   if (b < 0 || b >= a.B || a.Lmax <= 0) cnt = 0, b = 0;  // no request or empty cache: nothing selected
   const int e0 = (int)((int64_t)cnt * split / a.nsplit);
   const int e1 = (int)((int64_t)cnt * (split + 1) / a.nsplit);
-
-  bf16x8 qreg[kQSteps];
-  load_q(a.q + (int64_t)n * a.q_n + (int64_t)(16 * w + c) * a.q_h, g, qreg);
-  State st;
-  init_state(st);
+  // the tile "positions" are list entries [e0, e1)
+  const Tiles T(0, e1 - e0, blockIdx.x * 2654435761u >> 7);
   const LdsBases L = lds_bases(w, g, c);
 
-  run_bf16_gather<kP>(reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t,
-                      a.idx + (int64_t)n * a.i_n + e0, e1 - e0, a.Lmax, w, g, c, L, qreg, a.scale_log2, st, S, ring,
-                      blockIdx.x * 2654435761u >> 7);
-
-  const float l = finish(st, w, g, c, S);
-  if (g == 0)
-    a.lse[(int64_t)split * a.l_s + (int64_t)n * a.l_n + (int64_t)(16 * w + c) * a.l_h] =
-        l > 0.f ? (st.m_run + log2f(l)) * kLn2 : -INFINITY;
+  if (qk_role) {
+    bf16x8 qreg[kQSteps];
+    load_q(a.q + (int64_t)n * a.q_n + (int64_t)(16 * w + c) * a.q_h, g, qreg);
+    QkStat st{-INFINITY, 0.f};
+    // selection bits of tile i from the entry ring of PV wavefront w
+    const char* wring = ring + w * (kIdxSlots * kIdxSlotBytes);
+    auto mask = [&](int i) -> uint32_t {
+      const int v = *reinterpret_cast<const int*>(wring + (i % kIdxSlots) * kIdxSlotBytes + 4 * (lane & 31));
+      return (uint32_t)__ballot((uint32_t)v < (uint32_t)a.Lmax);
+    };
+    ws_qk<false, true>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); },
+                       [](int, TokScale&) {}, mask);
+    const float l = sum4_rows(st.l_run);
+    if (g == 0) S.lsum[16 * w + c] = l;
+    __syncthreads();
+    if (g == 0)
+      a.lse[(int64_t)split * a.l_s + (int64_t)n * a.l_n + (int64_t)(16 * w + c) * a.l_h] =
+          l > 0.f ? (st.m_run + log2f(l)) * kLn2 : -INFINITY;
+  } else {
+    f32x4 oacc[kMv][4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    const int head = 16 * hb + c;
-    const float lh = lsum_s[head];
-    const float inv = lh > 0.f ? 1.f / lh : 0.f;
-    float* op = a.o + (int64_t)split * a.o_s + (int64_t)n * a.o_n + (int64_t)head * a.o_h + 128 * w + 4 * g;
+    for (int m = 0; m < kMv; ++m)
 #pragma unroll
-    for (int m = 0; m < kMv; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = st.oacc[m][hb] * inv;
+      for (int hb = 0; hb < 4; ++hb) oacc[m][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ws_pv_gather<kP>(T, reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t,
+                     a.idx + (int64_t)n * a.i_n + e0, a.Lmax, tid - 256, w, g, c, L, oacc, S, ring);
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const int head = 16 * hb + c;
+      const float lh = lsum_s[head];
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      float* op = a.o + (int64_t)split * a.o_s + (int64_t)n * a.o_n + (int64_t)head * a.o_h + 128 * w + 4 * g;
+#pragma unroll
+      for (int m = 0; m < kMv; ++m) *reinterpret_cast<f32x4*>(op + 16 * m) = oacc[m][hb] * inv;
+    }
   }
 }
 
@@ -74,9 +93,9 @@ int launch_sparse_mla(const SparseMlaArgs& a, void* stream) {
   const dim3 grid((unsigned)((int64_t)a.N * a.nsplit));
   hipStream_t st = (hipStream_t)stream;
   if (a.reuse)
-    hipLaunchKernelGGL((sparse_mla_kernel<Policy::kReuse>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<Policy::kReuse>), grid, dim3(kWsThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((sparse_mla_kernel<Policy::kStream>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<Policy::kStream>), grid, dim3(kWsThreads), 0, st, a);
   return hipGetLastError();
 }
 
