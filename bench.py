@@ -48,13 +48,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # they were measured at; after any change the field is null until re-measured.
 TRAFFIC = {
     # profiles/prefill_gqa_zigzag_16k_c4_rank1.md
-    "prefill_gqa_kernel": dict(digest="c8a2cf5c27a1c692", fetch_kib=65466.0, write_kib=33792.6,
+    "prefill_gqa_kernel": dict(digest="81b1083652492a8d", fetch_kib=67469.8, write_kib=33792.4,
                                fetch_scale=1.99994, write_scale=1.0,
-                               fetch_bytes=134070346, write_bytes=34603622),
+                               fetch_bytes=138173945, write_bytes=34603408),
     # profiles/decode_mla_b64_h64_ctx131072_c8.md
-    "decode_mla_kernel<bf16>": dict(digest="4871fe18e7f334be", fetch_kib=599188.0, write_kib=32832.2,
+    "decode_mla_kernel<bf16>": dict(digest="26a930ede73193c6", fetch_kib=599174.0, write_kib=32833.1,
                                     fetch_scale=1.99994, write_scale=1.0,
-                                    fetch_bytes=1227100210, write_bytes=33620173),
+                                    fetch_bytes=1227071552, write_bytes=33621093),
 }
 
 

@@ -253,15 +253,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_gqa_kernel(Args a) {
     const char* Vt = &lds[ST][1][0];
 
     // ---- S^T = K Q^T ----
-    f32x16 sacc[2];
+    // (the two key blocks alternate, and each K operand is read two k-steps
+    // ahead, so an LDS read has four MFMAs to land)
+    constexpr int kAhead = 2;
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    bf16x8 ka[kD / 16][2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      sacc[mt] = f32x16{};
+    for (int s = 0; s < kAhead; ++s)
 #pragma unroll
-      for (int s = 0; s < kD / 16; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kt + qk_off[mt][s]);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[mt], 0, 0, 0);
+      for (int mt = 0; mt < 2; ++mt) ka[s][mt] = *reinterpret_cast<const bf16x8*>(Kt + qk_off[mt][s]);
+#pragma unroll
+    for (int s = 0; s < kD / 16; ++s) {
+      if (s + kAhead < kD / 16) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          ka[s + kAhead][mt] = *reinterpret_cast<const bf16x8*>(Kt + qk_off[mt][s + kAhead]);
       }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][mt], qreg[s], sacc[mt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // ---- mask (only tiles that reach past the wave's first row), max ----
     // The running max is kept in the scaled log2 domain; the max is taken over
