@@ -52,7 +52,7 @@ TRAFFIC = {
                                fetch_scale=1.99994, write_scale=1.0,
                                fetch_bytes=138173945, write_bytes=34603408),
     # profiles/decode_mla_b64_h64_ctx131072_c8.md
-    "decode_mla_kernel<bf16>": dict(digest="26a930ede73193c6", fetch_kib=599174.0, write_kib=32833.1,
+    "decode_mla_kernel<bf16>": dict(digest="a0a96daa708910cb", fetch_kib=599174.0, write_kib=32833.1,
                                     fetch_scale=1.99994, write_scale=1.0,
                                     fetch_bytes=1227071552, write_bytes=33621093),
 }

@@ -177,21 +177,8 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
   else cpa::wait_vmcnt<0>();
 }
 
-// Tokens [t0, t1) of a bf16 latent cache (`base` = token 0, `c_t` elements
-// per token) through the core. Stage i % 4 holds tile i; tokens past t1 in
-// the last tile re-read token t1 - 1 and are masked.
-// ---- bf16 pipeline: one barrier per tile ----
-// Step i, after the barrier that publishes P_i (and tile i+1):
-//   S_{i+1} = K_{i+1} Q^T                      (QK role, MFMA)
-//   O += V_i^T P_i, rescaled by alpha_i first   (PV role, MFMA)
-//   softmax(S_{i+1}) -> P_{i+1}, alpha_{i+1}    (VALU, placed between the PV
-//                                                MFMAs so it runs in their shadow)
-// P and alpha are double buffered (P_{i+1} goes to the buffer P_{i-1} used,
-// which every wave finished reading before the barrier), so one barrier per
-// tile orders everything: the tile stages, the P exchange and the reuse.
-
-// QK of one tile into sacc; hook(s) runs at k-step s; vpre(m) at the last
-// kAheadV steps issues the first V operand reads of the tile PV works on.
+// QK of one tile into sacc (K operands read kAhead k-steps ahead); hook(s)
+// runs at k-step s; vpre(m) runs at the last kAheadV k-steps.
 template <typename Hook, typename VPre>
 __device__ __forceinline__ void qk_tile(const char* tile, const LdsBases& L, const bf16x8 (&qreg)[kQSteps],
                                         f32x4 (&sacc)[2], Hook&& hook, VPre&& vpre) {
