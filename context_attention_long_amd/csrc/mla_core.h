@@ -113,11 +113,15 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
 
 // Maximum / sum over the four lanes l, l^16, l^32, l^48 (one head's four
 // score groups), with the gfx950 row-swap permutes instead of LDS round trips.
+// (compare-select rather than fmaxf: the swapped values are not known to be
+// canonical floats, and fmaxf would canonicalise both operands first)
 __device__ __forceinline__ float max4_rows(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const float a0 = __uint_as_float(a[0]), a1 = __uint_as_float(a[1]);
+  const float y = a0 > a1 ? a0 : a1;
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  const float b0 = __uint_as_float(b[0]), b1 = __uint_as_float(b[1]);
+  return b0 > b1 ? b0 : b1;
 }
 
 __device__ __forceinline__ float sum4_rows(float x) {
@@ -226,31 +230,37 @@ struct TokScale {
   float v[8];
 };
 
-// kMask: bit t of vmask says whether token t of the tile is a selection
-// (index-list attention); without it the first nvalid tokens are.
+// Scores stay unscaled (raw dot products; times the token scale for FP8)
+// until the exponential, where one FMA applies the softmax scale and
+// subtracts the reference: the max is taken over raw scores (the scale is
+// positive) and scaled once. The mask (ragged last tile, or selection bits)
+// is applied only where it can matter. kMask: bit t of vmask says whether
+// token t of the tile is a selection (index-list attention); without it the
+// first nvalid tokens are.
 template <bool kFp8, bool kMask = false>
 __device__ __forceinline__ void soft_scores(Soft& sm, const f32x4 (&sacc)[2], int nvalid, int g, float scale_log2,
                                             const TokScale& ts, uint32_t vmask = 0xffffffffu) {
-  sm.mx = -INFINITY;
+  (void)scale_log2;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * mt + 4 * g + i;
-      float v = sacc[mt][i] * scale_log2;
-      if constexpr (kFp8) v *= ts.v[4 * mt + i];
-      if constexpr (kMask)
-        v = (t < nvalid && ((vmask >> t) & 1u)) ? v : -INFINITY;
-      else
-        v = (t < nvalid) ? v : -INFINITY;
-      sm.x[4 * mt + i] = v;
-      sm.mx = fmaxf(sm.mx, v);
+    for (int i = 0; i < 4; ++i) sm.x[4 * mt + i] = kFp8 ? sacc[mt][i] * ts.v[4 * mt + i] : sacc[mt][i];
+  if (kMask || nvalid < kBN) {  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = 16 * (j >> 2) + 4 * g + (j & 3);
+      const bool keep = kMask ? (t < nvalid && ((vmask >> t) & 1u)) : t < nvalid;
+      sm.x[j] = keep ? sm.x[j] : -INFINITY;
     }
+  }
+  sm.mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sm.mx = fmaxf(sm.mx, sm.x[j]);
 }
 
 template <typename St>
-__device__ __forceinline__ void soft_ref(Soft& sm, St& st) {
-  const float mx = max4_rows(sm.mx);
+__device__ __forceinline__ void soft_ref(Soft& sm, St& st, float scale_log2) {
+  const float mx = max4_rows(sm.mx) * scale_log2;
   const bool move = mx > st.m_run + 8.f;
   const float m_new = move ? mx : st.m_run;
   sm.alpha = move ? __builtin_amdgcn_exp2f(st.m_run - m_new) : 1.f;  // 0 on the first tile
@@ -262,11 +272,11 @@ __device__ __forceinline__ void soft_ref(Soft& sm, St& st) {
 // kMask: a head may have seen no selected token yet (reference max still
 // -inf, every score -inf); its probabilities are then 0, not -inf - -inf.
 template <bool kFp8, int J0, bool kMask = false, typename St>
-__device__ __forceinline__ void soft_exp(Soft& sm, const St& st, const TokScale& ts) {
+__device__ __forceinline__ void soft_exp(Soft& sm, const St& st, const TokScale& ts, float scale_log2) {
   const float mref = (kMask && st.m_run == -INFINITY) ? 0.f : st.m_run;
 #pragma unroll
   for (int j = J0; j < J0 + 4; ++j) {
-    const float p = __builtin_amdgcn_exp2f(sm.x[j] - mref);
+    const float p = __builtin_amdgcn_exp2f(fmaf(sm.x[j], scale_log2, -mref));
     sm.psum += p;
     sm.pf[j] = kFp8 ? p * ts.v[j] : p;
   }
@@ -277,7 +287,7 @@ __device__ __forceinline__ void soft_store(Soft& sm, St& st, char* pbuf, float* 
   st.l_run += sm.psum;
   // P^T chunk of this lane: head 16w + c, k-elements 8g..8g+7 in score order
   *reinterpret_cast<bf16x8*>(pbuf + p_off(16 * w + c, g)) = pack8(sm.pf);
-  if (g == 0) abuf[16 * w + c] = sm.alpha;
+  abuf[16 * w + c] = sm.alpha;  // the head's four lane groups hold the same value
 }
 
 // ---- index-list (sparse) attention: the LDS ring of list entries ----

@@ -144,9 +144,9 @@ __device__ __forceinline__ void ws_qk(const Tiles& T, int w, int g, int c, const
     qk_tile(tile(i), L, qreg, sacc, [](int) {}, [](int) {});
     Soft sm;
     soft_scores<kFp8, kMask>(sm, sacc, T.nvalid(i), g, scale_log2, tsc[P], kMask ? mask(i) : 0xffffffffu);
-    soft_ref(sm, st);
-    soft_exp<kFp8, 0, kMask>(sm, st, tsc[P]);
-    soft_exp<kFp8, 4, kMask>(sm, st, tsc[P]);
+    soft_ref(sm, st, scale_log2);
+    soft_exp<kFp8, 0, kMask>(sm, st, tsc[P], scale_log2);
+    soft_exp<kFp8, 4, kMask>(sm, st, tsc[P], scale_log2);
     soft_store(sm, st, S.p + kH * kPRowBytes * P, S.alpha + kH * P, w, g, c);
     if constexpr (kFp8) {
       scales(clampt(i + 2), tsc[P]);  // tile i's scales are spent
