@@ -50,13 +50,13 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # they were measured at; after any change the field is null until re-measured.
 TRAFFIC = {
     # profiles/prefill_gqa_zigzag_16k_c4_rank1.md
-    "prefill_gqa_kernel": dict(digest="81b1083652492a8d", fetch_kib=67469.8, write_kib=33792.4,
+    "prefill_gqa_kernel": dict(digest="81b1083652492a8d", fetch_kib=67673.6, write_kib=33792.7,
                                fetch_scale=1.99994, write_scale=1.0,
-                               fetch_bytes=138173945, write_bytes=34603408),
+                               fetch_bytes=138591435, write_bytes=34603733),
     # profiles/decode_mla_b64_h64_ctx131072_c8.md
-    "decode_mla_kernel<bf16>": dict(digest="a0a96daa708910cb", fetch_kib=599174.0, write_kib=32833.1,
+    "decode_mla_kernel<bf16>": dict(digest="98430b6f097e8e63", fetch_kib=599183.0, write_kib=32833.1,
                                     fetch_scale=1.99994, write_scale=1.0,
-                                    fetch_bytes=1227071552, write_bytes=33621093),
+                                    fetch_bytes=1227089957, write_bytes=33621060),
 }
 
 
