@@ -54,7 +54,7 @@ TRAFFIC = {
                                fetch_scale=1.99994, write_scale=1.0,
                                fetch_bytes=138591435, write_bytes=34603733),
     # profiles/decode_mla_b64_h64_ctx131072_c8.md
-    "decode_mla_kernel<bf16>": dict(digest="98430b6f097e8e63", fetch_kib=599183.0, write_kib=32833.1,
+    "decode_mla_kernel<bf16>": dict(digest="7c6e7b0beed0a69e", fetch_kib=599183.0, write_kib=32833.1,
                                     fetch_scale=1.99994, write_scale=1.0,
                                     fetch_bytes=1227089957, write_bytes=33621060),
 }

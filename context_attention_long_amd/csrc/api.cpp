@@ -103,7 +103,7 @@ struct DecodePlan {
 
 int mla_nsplit(int64_t B, int64_t max_len) {
   if (B <= 0) return 1;
-  const int64_t slots = num_cus();                 // one 4-wave workgroup per CU
+  const int64_t slots = num_cus();                 // one 8-wavefront workgroup per CU
   int64_t ns = (slots + B - 1) / B;                // fill the machine once
   const int64_t by_len = (max_len + 255) / 256;    // at least 256 tokens per split
   if (ns > by_len) ns = by_len;

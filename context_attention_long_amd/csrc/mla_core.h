@@ -299,7 +299,7 @@ __device__ __forceinline__ void soft_store(Soft& sm, St& st, char* pbuf, float* 
 // through registers the compiler would have to wait for (see ws_pv_gather).
 constexpr int kIdxSlots = 5;
 constexpr int kIdxSlotBytes = 256;                          // 64 lanes x 4 B
-constexpr int kIdxRingBytes = 4 * kIdxSlots * kIdxSlotBytes;  // per workgroup (4 waves)
+constexpr int kIdxRingBytes = 4 * kIdxSlots * kIdxSlotBytes;  // per workgroup (the 4 PV wavefronts)
 
 }  // namespace mla
 }  // namespace cpa
