@@ -13,13 +13,20 @@
 // One workgroup per query row. The order is a 64-bit key per candidate:
 // an order-preserving map of the score in the high word, the complement of
 // the id in the low word, so larger key = better and keys are distinct.
-// A most-significant-digit radix select (8 bits per pass, one LDS
-// histogram per wavefront) finds the k-th key, stopping as soon as a digit
-// bin holds exactly the entries still needed; then a stable compaction
-// writes the selection in candidate order. Up to 16384 candidates per row
-// keep their score keys in LDS (64 KB, candidate j at word j) for all
-// passes; longer rows are re-read from memory (L2) on every pass.
+// A most-significant-digit radix select (8 bits per pass, an LDS
+// histogram in 16 copies) finds the k-th key, starting below the leading
+// bits every candidate shares and stopping as soon as a digit bin holds
+// exactly the entries still needed. The selection is then every key at or
+// above one 64-bit threshold; a stable compaction takes it in candidate
+// order. Up to 16384 candidates per row keep their score keys in LDS (64 KB,
+// candidate j at word j, key 0 in the empty words up to a multiple of 4096)
+// for all passes; the compaction then lists the selected candidates in the
+// same words, and their scores, ids and rows are read in one batch. Longer
+// rows are re-read from memory (L2) on every pass and written out chunk by
+// chunk.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -29,6 +36,7 @@ constexpr int kThreads = 1024;            // 16 wavefronts: the passes are laten
 constexpr int kWaves = kThreads / 64;
 constexpr int kE = 16;                     // chunks of 1024 candidates per compaction round
 constexpr int kLdsCands = kE * kThreads;   // 16384 candidates with keys in LDS
+constexpr int kVisit = 4 * kThreads;       // slots per step of a sweep: 4 per thread, read together
 
 // Score key: larger = better; 0 is reserved for "no candidate" (an unused
 // register slot or a list entry past its count), NaN maps to 1.
@@ -38,15 +46,45 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-struct SelectLds {
-  uint32_t hist[256];
+// The digit histogram is kept in 16 copies, lane l adding into copy l mod
+// 16: a float score's leading digits (sign and exponent bits) put most
+// entries into a few bins, and LDS atomics of one wavefront on one address
+// serialise. A copy's row is 260 words, so copy c's bin d sits in bank
+// (4 c + d) mod 64: the copies of one bin never share a bank.
+constexpr int kCopies = 16;
+constexpr int kCopyWords = 260;
+
+struct alignas(16) SelectLds {
+  uint32_t hist[kCopies][kCopyWords];
   uint64_t mask[kE][kWaves];  // selection ballot per (chunk, wave)
   uint32_t off[kE][kWaves];   // output offset of each (chunk, wave)
-  uint32_t lcnt[64];          // selected per source list (merge)
+  uint32_t lcnt[64];          // selected per source list (merge of long lists)
+  uint32_t lbase[65];         // first output position of each source list (merge)
   int32_t cnt_in[64];         // entries of each source list (merge)
   uint32_t wsum[kWaves];
   uint32_t bcast[4];
 };
+
+// Inclusive scans over the 64 lanes of a wavefront with DPP moves (no LDS
+// round trips): shifts by 1, 2, 4, 8 within rows of 16 lanes, then the last
+// lane of row 0 (2) carried into row 1 (3), then lane 31 into rows 2 and 3.
+// Lanes without a source take `id`, the operation's identity.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, uint32_t id, Op&& op) {
+  int x = (int)v;
+  const int e = (int)id;
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(e, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(e, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(e, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(e, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(e, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = (int)op((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(e, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)x;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  return wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
 
 // The digit search of one radix pass over the per-wave histograms: the digit
 // d holding the need-th largest key, the count of entries in bins above d and
@@ -57,18 +95,16 @@ __device__ __forceinline__ void pick_digit(SelectLds& sl, uint32_t need, uint32_
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   __syncthreads();
   if (w == 0) {
-    uint32_t b[4], s = 0;  // lane l: bins 255-4l .. 252-4l (descending digit order)
+    uint32_t b[4] = {0u, 0u, 0u, 0u}, s = 0;  // lane l: bins 255-4l .. 252-4l (descending digit order)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int bi = 255 - 4 * lane - i;
-      b[i] = sl.hist[bi] - (bi == 0 ? phantom : 0u);
-      s += b[i];
+    for (int cp = 0; cp < kCopies; ++cp) {
+      const uint4 h = *reinterpret_cast<const uint4*>(&sl.hist[cp][252 - 4 * lane]);
+      b[0] += h.w, b[1] += h.z, b[2] += h.y, b[3] += h.x;
     }
-    uint32_t incl = s;
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
+    if (lane == 63) b[3] -= phantom;  // bin 0
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += b[i];
+    const uint32_t incl = wave_incl_sum(s);
     uint32_t ab = incl - s;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -86,62 +122,72 @@ __device__ __forceinline__ void pick_digit(SelectLds& sl, uint32_t need, uint32_
 }
 
 // Histogram add of one digit per lane (lanes with in = false skip): one LDS
-// atomic into the workgroup's histogram. (Counting a thread's first two
-// distinct digits in registers first was measured slower.)
-__device__ __forceinline__ void hist_add(uint32_t* hist, bool in, uint32_t digit) {
-  if (in) atomicAdd(&hist[digit], 1u);
+// atomic into the lane's copy. (Counting a thread's first two distinct
+// digits in registers first, and adding the lanes of a shared digit with one
+// atomic, were measured slower.)
+__device__ __forceinline__ void hist_add(SelectLds& sl, bool in, uint32_t digit) {
+  if (in) atomicAdd(&sl.hist[threadIdx.x & (kCopies - 1)][digit], 1u);
 }
 
 __device__ __forceinline__ void clear_hist(SelectLds& sl) {
-  if (threadIdx.x < 256) sl.hist[threadIdx.x] = 0;
+  // 1024 threads x 4 words: copy t / 64, bins 4 (t mod 64) .. + 3
+  static_assert(kCopies * 256 == 4 * kThreads, "one 16-byte store per thread clears the copies");
+  *reinterpret_cast<uint4*>(&sl.hist[threadIdx.x >> 6][4 * (threadIdx.x & 63)]) = uint4{0u, 0u, 0u, 0u};
 }
 
-// Threshold of a selection: candidate with key K = (score key << 32) | ~id is
-// selected iff it exists and (K >> shift) >= prefix; shift = 64: all that
-// exist; shift < 0: none.
+// Selection of a radix select: a candidate with score key sk and low key
+// word lo is selected iff sk != 0 and (sk, lo) >= (hi, lo_t) in
+// lexicographic order. {0, 0} selects every candidate; hi = ~0u selects none
+// (no score key reaches it: +inf maps to 0xff800000).
 struct Thresh {
-  uint64_t prefix;
-  int shift;
+  uint32_t hi, lo;
 };
 
-__device__ __forceinline__ bool above_hi(uint32_t sk, const Thresh& t) {
-  return (sk >> (t.shift - 32)) >= (uint32_t)t.prefix;  // for 32 <= shift < 64
+// kTie: the threshold's low word is not 0, so candidates whose score key
+// equals the threshold's compare their low word (low(slot), read only for
+// them); without it the test is branch-free.
+template <bool kTie, typename Low>
+__device__ __forceinline__ bool is_sel(uint32_t sk, int slot, const Thresh& t, Low&& low) {
+  const bool gt = sk > t.hi, eq = (sk == t.hi) & (sk != 0u);
+  if constexpr (kTie) return gt || (eq && low(slot) >= t.lo);
+  else return gt | eq;
 }
 
-// Radix select. each(f) visits slots, every lane of a wavefront the same
-// number of times: f(slot, any, sk) with any = false for a visit past the
-// end, else the score key (0: no candidate; `phantom` such slots are
-// visited); low(slot) gives the low key
-// word (~id), asked for only when equal scores reach the threshold. A slot
-// without candidate has key 0, below every candidate, so it can only sit in
-// the bins of the all-zero prefix, from which pick_digit removes it.
-template <typename Each, typename Low>
-__device__ __forceinline__ Thresh radix_select(uint32_t total, uint32_t phantom, int k, Each&& each, Low&& low,
-                                               SelectLds& sl) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  Thresh t{0, 64};
-  if (total <= (uint32_t)k) return t;
-  if (k <= 0) return Thresh{0, -1};
-  // leading score-key bits shared by every candidate: the first digit starts
-  // below them (the merge's candidates all lie in the upper tail, where the
-  // top digit would put almost everything into one or two bins)
-  uint32_t kand = ~0u, kor = 0u;
-  each([&](int, bool any, uint32_t sk) {
-    if (any && sk != 0) kand &= sk, kor |= sk;
-  });
-  for (int o = 32; o > 0; o >>= 1) {
-    kand &= (uint32_t)__shfl_xor((int)kand, o);
-    kor |= (uint32_t)__shfl_xor((int)kor, o);
-  }
-  if (lane == 0) sl.mask[0][w] = ((uint64_t)kand << 32) | kor;
-  __syncthreads();
+// Leading score-key bits shared by every candidate, from each thread's AND
+// and OR over its own keys (key 0 left out). Every thread returns the count
+// cb and the AND (whose top cb bits are the shared ones).
+__device__ __forceinline__ int common_bits(uint32_t& kand, uint32_t kor, SelectLds& sl) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  kand = wave_scan(kand, ~0u, [](uint32_t a, uint32_t b) { return a & b; });  // lane 63: the wavefront's
+  kor = wave_scan(kor, 0u, [](uint32_t a, uint32_t b) { return a | b; });
+  if (lane == 63) sl.mask[0][w] = ((uint64_t)kand << 32) | kor;
+  __syncthreads();  // (the next write of mask[0] follows several barriers)
   kand = ~0u, kor = 0u;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) kand &= (uint32_t)(sl.mask[0][i] >> 32), kor |= (uint32_t)sl.mask[0][i];
-  __syncthreads();
-  const int cb = (kand ^ kor) ? __clz(kand ^ kor) : 32;  // common leading bits
-  int prev = 64 - cb;                                     // key bits below the common ones
-  t.prefix = (uint64_t)kand >> (32 - cb);
+  return (kand ^ kor) ? __clz(kand ^ kor) : 32;
+}
+
+// Radix select of the k largest keys among `total` candidates. each(f)
+// visits slots, every lane of a wavefront the same number of times: f(slot,
+// any, sk) with any = false for a visit past the end, else the score key
+// (0: no candidate; `phantom` such slots are visited); low(slot) gives the
+// low key word (~id), asked for only when equal scores reach the threshold.
+// kand / kor: this thread's AND and OR over the score keys (key 0 left out).
+// A slot without candidate has key 0, below every candidate, so it can only
+// sit in the bins of the all-zero prefix, from which pick_digit removes it.
+template <typename Each, typename Low>
+__device__ __forceinline__ Thresh radix_select(uint32_t total, uint32_t phantom, int k, uint32_t kand, uint32_t kor,
+                                               Each&& each, Low&& low, SelectLds& sl) {
+  if (total <= (uint32_t)k) return Thresh{0u, 0u};
+  if (k <= 0) return Thresh{~0u, ~0u};
+  // the first digit starts below the shared leading bits (the merge's
+  // candidates all lie in the upper tail, where the top digit would put
+  // almost everything into one or two bins)
+  const int cb = common_bits(kand, kor, sl);
+  int prev = 64 - cb;  // key bits below the known prefix
+  uint64_t prefix = (uint64_t)kand >> (32 - cb);
+  int shift = prev;
   uint32_t need = (uint32_t)k;
   while (prev > 0) {
     const int sh = prev > 32 ? max(prev - 8, 32) : prev - 8;
@@ -149,58 +195,78 @@ __device__ __forceinline__ Thresh radix_select(uint32_t total, uint32_t phantom,
     clear_hist(sl);
     __syncthreads();
     if (sh >= 32) {
-      const int s32 = sh - 32;
-      const uint64_t pre = t.prefix;
-      each([&](int, bool any, uint32_t sk) {
-        hist_add(sl.hist, any && ((uint64_t)sk >> (prev - 32)) == pre, (sk >> s32) & dmask);
-      });
+      // a digit of the score key among the keys whose bits above prev - 32
+      // are the prefix
+      const int s32 = sh - 32, p32 = prev - 32;
+      const uint32_t hmask = p32 >= 32 ? 0u : ~0u << p32;
+      const uint32_t hval = p32 >= 32 ? 0u : (uint32_t)prefix << p32;
+      each([&](int, bool any, uint32_t sk) { hist_add(sl, any && (sk & hmask) == hval, (sk >> s32) & dmask); });
     } else {
-      const uint32_t hi = (uint32_t)(t.prefix >> (32 - prev));  // the full score key
+      // equal score keys at the threshold: a digit of the low word among the
+      // keys with that score key whose low bits above prev are the prefix's
+      const uint32_t hi = (uint32_t)(prefix >> (32 - prev));
+      const uint32_t lmask = prev >= 32 ? 0u : ~0u << prev;
+      const uint32_t lval = prev >= 32 ? 0u : (uint32_t)prefix << prev;
       each([&](int slot, bool any, uint32_t sk) {
-        bool in = any && sk == hi && hi != 0;  // a slot without candidate has key 0
-        uint64_t key = 0;
-        if (in) {
-          key = ((uint64_t)sk << 32) | low(slot);
-          in = (key >> prev) == t.prefix;
+        uint32_t lo = 0u;
+        bool in = false;
+        if (any && sk == hi && hi != 0u) {  // a slot without candidate has key 0
+          lo = low(slot);
+          in = (lo & lmask) == lval;
         }
-        hist_add(sl.hist, in, (uint32_t)(key >> sh) & dmask);
+        hist_add(sl, in, (lo >> sh) & dmask);
       });
     }
     uint32_t d, above, bin;
-    pick_digit(sl, need, t.prefix == 0 ? phantom : 0u, d, above, bin);
+    pick_digit(sl, need, prefix == 0 ? phantom : 0u, d, above, bin);
     need -= above;
-    t.prefix = (t.prefix << (prev - sh)) | d;
-    t.shift = sh;
+    prefix = (prefix << (prev - sh)) | d;
+    shift = sh;
     prev = sh;
-    if (bin == need) return t;  // every entry of this bin is selected
+    if (bin == need) break;  // every entry of this bin is selected
   }
-  return t;
+  const uint64_t thr = prefix << shift;  // prefix holds 64 - shift bits
+  return Thresh{(uint32_t)(thr >> 32), (uint32_t)thr};
 }
 
-template <typename Low>
-__device__ __forceinline__ bool is_sel(uint32_t sk, int slot, const Thresh& t, Low&& low) {
-  if (sk == 0 || t.shift < 0) return false;
-  if (t.shift >= 64) return true;
-  if (t.shift >= 32) return above_hi(sk, t);
-  const uint64_t key = ((uint64_t)sk << 32) | low(slot);
-  return (key >> t.shift) >= t.prefix;
-}
-
-// Stable compaction in candidate order (chunk e holds candidates 256 e +
+// Stable compaction in candidate order (chunk e holds candidates 1024 e +
 // thread, e < nchunk <= kE): sel(e) says whether this thread's candidate of
 // chunk e is selected; emit(e, pos) writes it at output position pos.
-// Returns the number selected.
-template <typename Sel, typename Emit>
+// kAll: all kE chunks, unrolled so their reads overlap (sel must then be
+// safe for every chunk). Returns the number selected.
+template <bool kAll = false, typename Sel, typename Emit>
 __device__ __forceinline__ uint32_t compact(int nchunk, Sel&& sel, Emit&& emit, SelectLds& sl) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if constexpr (kAll) nchunk = kE;
   auto chunks = [&](auto&& f) {
+    if constexpr (kAll) {
+#pragma unroll
+      for (int e = 0; e < kE; ++e) f(e);
+    } else {
 #pragma unroll 4
-    for (int e = 0; e < nchunk; ++e) f(e);
+      for (int e = 0; e < nchunk; ++e) f(e);
+    }
   };
-  chunks([&](int e) {
-    const uint64_t m = __ballot(sel(e));
-    if (lane == 0) sl.mask[e][w] = m;
-  });
+  if constexpr (kAll) {
+    // every chunk's test first (their LDS reads overlap), then lane e keeps
+    // chunk e's ballot and the lanes store them at once
+    bool s[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) s[e] = sel(e);
+    int mlo = 0, mhi = 0;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const uint64_t m = __ballot(s[e]);
+      mlo = lane == e ? (int)(uint32_t)m : mlo;
+      mhi = lane == e ? (int)(uint32_t)(m >> 32) : mhi;
+    }
+    if (lane < kE) sl.mask[lane][w] = ((uint64_t)(uint32_t)mhi << 32) | (uint32_t)mlo;
+  } else {
+    chunks([&](int e) {
+      const uint64_t m = __ballot(sel(e));
+      if (lane == 0) sl.mask[e][w] = m;
+    });
+  }
   __syncthreads();
   // exclusive offsets of the (chunk, wave) cells in candidate order, by
   // wave 0: lane l scans cells 4l .. 4l+3 (kE x kWaves = 256 cells)
@@ -213,11 +279,7 @@ __device__ __forceinline__ uint32_t compact(int nchunk, Sel&& sel, Emit&& emit, 
       c[i] = cell / kWaves < nchunk ? (uint32_t)__popcll(sl.mask[cell / kWaves][cell % kWaves]) : 0u;
       sum += c[i];
     }
-    uint32_t incl = sum;
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
+    const uint32_t incl = wave_incl_sum(sum);
     uint32_t run = incl - sum;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -228,10 +290,25 @@ __device__ __forceinline__ uint32_t compact(int nchunk, Sel&& sel, Emit&& emit, 
     if (lane == 63) sl.wsum[0] = incl;
   }
   __syncthreads();
-  chunks([&](int e) {
-    const uint64_t m = sl.mask[e][w];
-    if ((m >> lane) & 1ull) emit(e, sl.off[e][w] + (uint32_t)__popcll(m & ((1ull << lane) - 1ull)));
-  });
+  if constexpr (kAll) {
+    // lane e reads chunk e's ballot and offset; each chunk takes them from it
+    uint64_t mm = 0;
+    uint32_t oo = 0;
+    if (lane < kE) mm = sl.mask[lane][w], oo = sl.off[lane][w];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mm, e);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mm >> 32), e);
+      const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)oo, e);
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+      if ((((uint64_t)hi << 32 | lo) >> lane) & 1ull) emit(e, o + below);
+    }
+  } else {
+    chunks([&](int e) {
+      const uint64_t m = sl.mask[e][w];
+      if ((m >> lane) & 1ull) emit(e, sl.off[e][w] + (uint32_t)__popcll(m & ((1ull << lane) - 1ull)));
+    });
+  }
   const uint32_t total = sl.wsum[0];
   __syncthreads();
   return total;
@@ -239,78 +316,183 @@ __device__ __forceinline__ uint32_t compact(int nchunk, Sel&& sel, Emit&& emit, 
 
 // ---------------------------------------------------------------- local
 
+// Score keys of a row's first nv slots into LDS, key 0 in the other slots
+// (all 16384 are written, so any slot may be read); returns this thread's AND
+// and OR over its keys (key 0 left out). key(j, v) maps slot j's loaded
+// score v and must be safe for any j < 16384 (v is junk for j >= nv).
+template <typename Addr, typename Key>
+__device__ __forceinline__ void keys_to_lds(uint32_t* skl, int nv, const float* base, Addr&& addr, Key&& key,
+                                            uint32_t& kand, uint32_t& kor) {
+  const int tid = threadIdx.x;
+  kand = ~0u, kor = 0u;
+  float v[kE];  // one batch of 16 loads in flight
+#pragma unroll
+  for (int u = 0; u < kE; ++u) v[u] = nv > 0 ? base[addr(min(tid + kThreads * u, nv - 1))] : 0.f;
+#pragma unroll
+  for (int u = 0; u < kE; ++u) {
+    const int j = tid + kThreads * u;
+    const uint32_t kk = key(j, v[u]);
+    const uint32_t kj = j < nv ? kk : 0u;
+    skl[j] = kj;
+    kor |= kj;
+    kand &= kj ? kj : ~0u;
+  }
+}
+
+// The merge's score keys into LDS: entry s of list p goes to word
+// p k_in + s (key 0 past the list's count), words from P k_in on get key 0;
+// skl holds 1024 more words, written but never read.
+// A batch of 16 loads walks (list, block of 1024 entries) items in order,
+// the same items for every lane, so the list, its count and its base
+// address stay scalar. cntv: lane p holds list p's count.
+__device__ __forceinline__ void merge_keys_to_lds(uint32_t* skl, const cpa::TopkMergeArgs& a, int n, int cntv,
+                                                  uint32_t& kand, uint32_t& kor) {
+  const int tid = threadIdx.x;
+  const int nblk = (a.k_in + kThreads - 1) / kThreads;
+  const int nitem = a.P * nblk;
+  const int64_t plane = (int64_t)a.N * a.k_in;
+  kand = ~0u, kor = 0u;
+  int p = 0, i = 0;  // the next item: list p, entries 1024 i + thread
+  for (int f0 = 0; f0 < nitem; f0 += kE) {
+    float v[kE];
+    int slot[kE];
+    bool ok[kE];
+#pragma unroll
+    for (int u = 0; u < kE; ++u) {
+      const int s = tid + kThreads * i;
+      const bool lst = p < a.P;
+      const int cnt = __builtin_amdgcn_readlane(cntv, p & 63);
+      ok[u] = s < (lst ? cnt : 0);
+      // entries past k_in (the last block of a list) write a dead word
+      slot[u] = lst && s < a.k_in ? p * a.k_in + s : kLdsCands + tid;
+      const int64_t base = (int64_t)p * plane + (int64_t)n * a.k_in;
+      v[u] = a.cand_score[ok[u] ? base + s : 0];  // every lane loads (element 0 stands in)
+      if (++i == nblk) i = 0, ++p;
+    }
+#pragma unroll
+    for (int u = 0; u < kE; ++u) {
+      const uint32_t kj = ok[u] ? score_key(v[u]) : 0u;
+      skl[slot[u]] = kj;
+      kor |= kj;
+      kand &= kj ? kj : ~0u;
+    }
+  }
+  for (int j = a.P * a.k_in + tid; j < kLdsCands; j += kThreads) skl[j] = 0u;
+}
+
+// Sweep over the LDS keys of slots [0, npad): the keys of four chunks are
+// read together so their LDS latencies overlap.
+template <typename F>
+__device__ __forceinline__ void each_lds(const uint32_t* skl, int npad, F&& f) {
+  const int tid = threadIdx.x;
+  for (int j0 = 0; j0 < npad; j0 += kVisit) {
+    uint32_t kk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kk[u] = skl[j0 + tid + u * kThreads];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) f(j0 + tid + u * kThreads, true, kk[u]);
+  }
+}
+
 // kLds: the row's score keys fit LDS (L <= 16384); otherwise they are
 // re-read from memory every pass.
 template <bool kLds>
 __global__ __launch_bounds__(kThreads) void topk_local_kernel(cpa::TopkLocalArgs a) {
   __shared__ SelectLds sl;
-  __shared__ uint32_t skl[kLds ? kLdsCands : 1];  // the row's score bits
+  __shared__ uint32_t skl[kLds ? kLdsCands : 1];  // score keys, then the selected slots
   const int n = blockIdx.x, tid = threadIdx.x;
   int nv = a.n_valid ? a.n_valid[n] : a.L;
   nv = nv < 0 ? 0 : (nv > a.L ? a.L : nv);
   const float* sc = a.scores + (int64_t)n * a.s_n;
   auto id_of = [&](int j) { return (int32_t)(a.id_base + (int64_t)j * a.id_stride); };
-  auto low = [&](int j) { return (uint64_t)(~(uint32_t)id_of(j)); };
-  if constexpr (kLds) {
-    // batches of 16 loads in flight, keys into LDS
-    for (int j0 = 0; j0 < nv; j0 += 16 * kThreads) {
-      float v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = sc[min(j0 + tid + kThreads * u, nv - 1)];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int j = j0 + tid + kThreads * u;
-        if (j < nv) skl[j] = __float_as_uint(v[u]);
-      }
-    }
-  }
-  auto score_at = [&](int j) {
-    if constexpr (kLds) return __uint_as_float(skl[j]);
-    else return sc[j];
-  };
-  auto key_at = [&](int j) { return score_key(score_at(j)); };
-  // every lane runs the same trip count; the keys of four chunks are read
-  // together (unconditionally, clamped) so their LDS latencies overlap
-  auto each = [&](auto&& f) {
-    for (int j0 = 0; j0 < nv; j0 += 4 * kThreads) {
-      uint32_t kk[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) kk[u] = key_at(min(j0 + tid + u * kThreads, nv - 1));
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = j0 + tid + u * kThreads;
-        f(j, j < nv, kk[u]);
-      }
-    }
-  };
-  __syncthreads();
-  const Thresh t = radix_select((uint32_t)nv, 0u, a.k, each, low, sl);
-
+  auto low = [&](int j) { return ~(uint32_t)id_of(j); };
   float* os = a.out_score + (int64_t)n * a.k;
   int32_t* oi = a.out_id + (int64_t)n * a.k;
   int32_t* orow = a.out_row + (int64_t)n * a.k;
-  uint32_t run = 0;
-  const int nchunk = (nv + kThreads - 1) / kThreads;
-  for (int c0 = 0; c0 < nchunk; c0 += kE) {
-    const int nc = min(kE, nchunk - c0);
-    const uint32_t base = run;
-    run += compact(
-        nc,
-        [&](int e) {
-          const int j = tid + kThreads * (c0 + e);
-          const int jc = min(j, nv - 1);  // clamped: the key read and id stay in range
-          return (j < nv) & is_sel(key_at(jc), jc, t, low);
-        },
-        [&](int e, uint32_t pos) {
-          const int j = tid + kThreads * (c0 + e);
-          pos += base;
-          if (pos < (uint32_t)a.k) {
-            os[pos] = score_at(j);
-            oi[pos] = id_of(j);
-            orow[pos] = j;
-          }
-        },
-        sl);
+  uint32_t run;
+  if constexpr (kLds) {
+    const int npad = (nv + kVisit - 1) / kVisit * kVisit;
+    uint32_t kand, kor;
+    keys_to_lds(
+        skl, nv, sc, [](int j) { return j; }, [](int, float v) { return score_key(v); }, kand, kor);
+    __syncthreads();
+    auto each = [&](auto&& f) { each_lds(skl, npad, f); };
+    const Thresh t = radix_select((uint32_t)nv, (uint32_t)(npad - nv), a.k, kand, kor, each, low, sl);
+    // the selected slots in candidate order replace the keys (every key read
+    // is done before the first write: compact synchronises in between)
+    auto emit = [&](int e, uint32_t pos) {
+      if (pos < (uint32_t)a.k) skl[pos] = (uint32_t)(tid + kThreads * e);
+    };
+    auto sel = [&](auto tie) {
+      return [&, tie](int e) {
+        const int j = tid + kThreads * e;
+        return is_sel<decltype(tie)::value>(skl[j], j, t, low);
+      };
+    };
+    run = t.lo ? compact<true>(0, sel(std::true_type{}), emit, sl) : compact<true>(0, sel(std::false_type{}), emit, sl);
+    const int c = run < (uint32_t)a.k ? (int)run : a.k;
+    // scores from the row itself (-0 and NaN bits kept), ids and rows
+    for (int p0 = 0; p0 < c; p0 += 4 * kThreads) {
+      int j[4];
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) j[u] = (int)skl[min(p0 + tid + u * kThreads, c - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = sc[j[u]];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = p0 + tid + u * kThreads;
+        if (p < c) {
+          os[p] = v[u];
+          oi[p] = id_of(j[u]);
+          orow[p] = j[u];
+        }
+      }
+    }
+  } else {
+    auto key_at = [&](int j) { return score_key(sc[j]); };
+    // every lane runs the same trip count; the keys of four chunks are read
+    // together (unconditionally, clamped)
+    auto each = [&](auto&& f) {
+      for (int j0 = 0; j0 < nv; j0 += kVisit) {
+        uint32_t kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kk[u] = key_at(min(j0 + tid + u * kThreads, nv - 1));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = j0 + tid + u * kThreads;
+          f(j, j < nv, kk[u]);
+        }
+      }
+    };
+    uint32_t kand = ~0u, kor = 0u;
+    each([&](int, bool any, uint32_t sk) {
+      if (any && sk != 0u) kand &= sk, kor |= sk;
+    });
+    const Thresh t = radix_select((uint32_t)nv, 0u, a.k, kand, kor, each, low, sl);
+    run = 0;
+    const int nchunk = (nv + kThreads - 1) / kThreads;
+    for (int c0 = 0; c0 < nchunk; c0 += kE) {
+      const int nc = min(kE, nchunk - c0);
+      const uint32_t base = run;
+      run += compact(
+          nc,
+          [&](int e) {
+            const int j = tid + kThreads * (c0 + e);
+            const int jc = min(j, nv - 1);  // clamped: the key read and id stay in range
+            return (j < nv) && is_sel<true>(key_at(jc), jc, t, low);
+          },
+          [&](int e, uint32_t pos) {
+            const int j = tid + kThreads * (c0 + e);
+            pos += base;
+            if (pos < (uint32_t)a.k) {
+              os[pos] = sc[j];
+              oi[pos] = id_of(j);
+              orow[pos] = j;
+            }
+          },
+          sl);
+    }
   }
   const int c = run < (uint32_t)a.k ? (int)run : a.k;
   for (int p = c + tid; p < a.k; p += kThreads) {
@@ -326,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void topk_local_kernel(cpa::TopkLocalArgs
 template <bool kLds>
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(cpa::TopkMergeArgs a) {
   __shared__ SelectLds sl;
-  __shared__ uint32_t skl[kLds ? kLdsCands : 1];
+  __shared__ uint32_t skl[kLds ? kLdsCands + kThreads : 1];  // score keys, then the selected candidates
   const int n = blockIdx.x, tid = threadIdx.x;
   const int M = a.P * a.k_in;
   const int64_t plane = (int64_t)a.N * a.k_in;  // one rank's [N, k_in] block
@@ -338,9 +520,8 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(cpa::TopkMergeArgs
     }
     sl.cnt_in[tid] = c;
     sl.lcnt[tid] = 0;
-    uint32_t t = (uint32_t)c;  // total over the lists (wave 0)
-    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
-    if (tid == 0) sl.wsum[0] = t;
+    const uint32_t t = wave_incl_sum((uint32_t)c);  // lane 63: the total over the lists
+    if (tid == 63) sl.wsum[0] = t;
   }
   __syncthreads();
   const uint32_t total = sl.wsum[0];
@@ -358,99 +539,153 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(cpa::TopkMergeArgs
       return j / a.k_in;
     }
   };
-  auto elem = [&](int j) { const int p = list_of(j); return p * plane + (int64_t)n * a.k_in + (j - p * a.k_in); };
+  auto elem_in = [&](int j, int p) { return p * plane + (int64_t)n * a.k_in + (j - p * a.k_in); };
+  auto elem = [&](int j) { return elem_in(j, list_of(j)); };
   auto exists = [&](int j) { const int p = list_of(j); return j - p * a.k_in < sl.cnt_in[p]; };
-  auto low = [&](int j) { return (uint64_t)(~(uint32_t)a.cand_id[elem(j)]); };
+  auto low = [&](int j) { return ~(uint32_t)a.cand_id[elem(j)]; };
+  int32_t* oid = a.out_id + (int64_t)n * a.k;
   if constexpr (kLds) {
-    for (int j0 = 0; j0 < M; j0 += 16 * kThreads) {
-      float v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = a.cand_score[elem(min(j0 + tid + kThreads * u, M - 1))];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int j = j0 + tid + kThreads * u;
-        if (j < M) skl[j] = exists(j) ? score_key(v[u]) : 0u;
+    const int npad = (M + kVisit - 1) / kVisit * kVisit;
+    uint32_t kand, kor;
+    merge_keys_to_lds(skl, a, n, sl.cnt_in[tid & 63], kand, kor);
+    __syncthreads();
+    auto each = [&](auto&& f) { each_lds(skl, npad, f); };
+    const Thresh t = radix_select(total, (uint32_t)npad - total, a.k, kand, kor, each, low, sl);
+    // the selected candidates in candidate order replace the keys
+    auto emit = [&](int e, uint32_t pos) {
+      if (pos < (uint32_t)a.k) skl[pos] = (uint32_t)(tid + kThreads * e);
+    };
+    auto sel = [&](auto tie) {
+      return [&, tie](int e) {
+        const int j = tid + kThreads * e;
+        return is_sel<decltype(tie)::value>(skl[j], j, t, low);
+      };
+    };
+    const uint32_t run =
+        t.lo ? compact<true>(0, sel(std::true_type{}), emit, sl) : compact<true>(0, sel(std::false_type{}), emit, sl);
+    const int c = run < (uint32_t)a.k ? (int)run : a.k;
+    // the listed candidates run list by list: lane p finds where list p starts
+    if (tid < 64) {
+      if (tid < a.P) {
+        const uint32_t first = (uint32_t)(tid * a.k_in);
+        int lo = 0, hi = c;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (skl[mid] < first) lo = mid + 1;
+          else hi = mid;
+        }
+        sl.lbase[tid] = (uint32_t)lo;
       }
+      if (tid == 0) sl.lbase[a.P] = (uint32_t)c;
     }
-  }
-  auto key_at = [&](int j) {
-    if constexpr (kLds) return skl[j];
-    else return exists(j) ? score_key(a.cand_score[elem(j)]) : 0u;
-  };
-  auto each = [&](auto&& f) {
-    for (int j0 = 0; j0 < M; j0 += 4 * kThreads) {
-      uint32_t kk[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) kk[u] = key_at(min(j0 + tid + u * kThreads, M - 1));
+    __syncthreads();
+    // ids and owner rows of the selection, one batch of loads per 4096
+    for (int p0 = 0; p0 < c; p0 += 4 * kThreads) {
+      int q[4];
+      int32_t id[4], row[4];
+      int64_t el[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int j = j0 + tid + u * kThreads;
-        f(j, j < M, kk[u]);
+        const int j = (int)skl[min(p0 + tid + u * kThreads, c - 1)];
+        q[u] = list_of(j);
+        el[u] = elem_in(j, q[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) id[u] = a.cand_id[el[u]], row[u] = a.cand_row[el[u]];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = p0 + tid + u * kThreads;
+        if (p < c) {
+          oid[p] = id[u];
+          a.owner_row[((int64_t)q[u] * a.N + n) * a.k + (p - (int)sl.lbase[q[u]])] = row[u];
+        }
       }
     }
-  };
-  __syncthreads();
-  const Thresh t = radix_select(total, (uint32_t)M - total, a.k, each, low, sl);
-
-  auto sel_of = [&](int j) {
-    const int jc = min(j, M - 1);  // clamped: the key read and id stay in range
-    return (j < M) & is_sel(key_at(jc), jc, t, low);
-  };
-  // per-list counts: the owners' offsets in the rank-major output. A
-  // wavefront's 64 consecutive candidates span at most two lists when
-  // k_in >= 64: two ballots and two atomics instead of one per candidate.
-  const int lane = tid & 63;
-#pragma unroll 4
-  for (int j0 = 0; j0 < M; j0 += kThreads) {
-    const int j = j0 + tid;
-    const bool sl_j = sel_of(j);
-    if (a.k_in >= 64) {
-      const int jw = j0 + (tid & ~63);  // the wavefront's first candidate
-      const int plo = list_of(jw);
-      const bool lo = list_of(j) == plo;
-      const uint32_t clo = (uint32_t)__popcll(__ballot(sl_j && lo));
-      const uint32_t chi = (uint32_t)__popcll(__ballot(sl_j && !lo));
-      if (lane == 0 && clo) atomicAdd(&sl.lcnt[plo], clo);
-      if (lane == 0 && chi) atomicAdd(&sl.lcnt[plo + 1], chi);
-    } else if (sl_j) {
-      atomicAdd(&sl.lcnt[list_of(j)], 1u);
+    for (int p = 0; p < a.P; ++p) {
+      const int kept = (int)(sl.lbase[p + 1] - sl.lbase[p]);
+      int32_t* orow = a.owner_row + ((int64_t)p * a.N + n) * a.k;
+      for (int q = kept + tid; q < a.k; q += kThreads) orow[q] = -1;
+      if (tid == 0) a.owner_count[(int64_t)p * a.N + n] = kept;
     }
+    for (int q = c + tid; q < a.k; q += kThreads) oid[q] = -1;
+  } else {
+    auto key_at = [&](int j) { return exists(j) ? score_key(a.cand_score[elem(j)]) : 0u; };
+    auto each = [&](auto&& f) {
+      for (int j0 = 0; j0 < M; j0 += kVisit) {
+        uint32_t kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kk[u] = key_at(min(j0 + tid + u * kThreads, M - 1));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = j0 + tid + u * kThreads;
+          f(j, j < M, kk[u]);
+        }
+      }
+    };
+    uint32_t kand = ~0u, kor = 0u;
+    each([&](int, bool any, uint32_t sk) {
+      if (any && sk != 0u) kand &= sk, kor |= sk;
+    });
+    const Thresh t = radix_select(total, (uint32_t)M - total, a.k, kand, kor, each, low, sl);
+    auto sel_of = [&](int j) {
+      const int jc = min(j, M - 1);  // clamped: the key read and id stay in range
+      return (j < M) && is_sel<true>(key_at(jc), jc, t, low);
+    };
+    // per-list counts: the owners' offsets in the rank-major output. A
+    // wavefront's 64 consecutive candidates span at most two lists when
+    // k_in >= 64: two ballots and two atomics instead of one per candidate.
+    const int lane = tid & 63;
+#pragma unroll 4
+    for (int j0 = 0; j0 < M; j0 += kThreads) {
+      const int j = j0 + tid;
+      const bool sl_j = sel_of(j);
+      if (a.k_in >= 64) {
+        const int jw = j0 + (tid & ~63);  // the wavefront's first candidate
+        const int plo = list_of(jw);
+        const bool lo = list_of(j) == plo;
+        const uint32_t clo = (uint32_t)__popcll(__ballot(sl_j && lo));
+        const uint32_t chi = (uint32_t)__popcll(__ballot(sl_j && !lo));
+        if (lane == 0 && clo) atomicAdd(&sl.lcnt[plo], clo);
+        if (lane == 0 && chi) atomicAdd(&sl.lcnt[plo + 1], chi);
+      } else if (sl_j) {
+        atomicAdd(&sl.lcnt[list_of(j)], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t run = 0;
+    const int nchunk = (M + kThreads - 1) / kThreads;
+    for (int c0 = 0; c0 < nchunk; c0 += kE) {
+      const int nc = min(kE, nchunk - c0);
+      const uint32_t base0 = run;
+      run += compact(
+          nc, [&](int e) { return sel_of(tid + kThreads * (c0 + e)); },
+          [&](int e, uint32_t pos) {
+            const int j = tid + kThreads * (c0 + e);
+            pos += base0;
+            if (pos < (uint32_t)a.k) {
+              const int p = list_of(j);
+              uint32_t base = 0;
+              for (int q = 0; q < p; ++q) base += sl.lcnt[q];
+              const int64_t el = elem(j);
+              oid[pos] = a.cand_id[el];
+              a.owner_row[((int64_t)p * a.N + n) * a.k + (pos - base)] = a.cand_row[el];
+            }
+          },
+          sl);
+    }
+    // counts (capped at k over the rank-major order) and padding
+    uint32_t base = 0;
+    for (int p = 0; p < a.P; ++p) {
+      const uint32_t c = sl.lcnt[p];
+      const uint32_t kept = base >= (uint32_t)a.k ? 0u : (base + c <= (uint32_t)a.k ? c : (uint32_t)a.k - base);
+      int32_t* orow = a.owner_row + ((int64_t)p * a.N + n) * a.k;
+      for (int q = (int)kept + tid; q < a.k; q += kThreads) orow[q] = -1;
+      if (tid == 0) a.owner_count[(int64_t)p * a.N + n] = (int32_t)kept;
+      base += c;
+    }
+    const int c = run < (uint32_t)a.k ? (int)run : a.k;
+    for (int q = c + tid; q < a.k; q += kThreads) oid[q] = -1;
   }
-  __syncthreads();
-  int32_t* oid = a.out_id + (int64_t)n * a.k;
-  uint32_t run = 0;
-  const int nchunk = (M + kThreads - 1) / kThreads;
-  for (int c0 = 0; c0 < nchunk; c0 += kE) {
-    const int nc = min(kE, nchunk - c0);
-    const uint32_t base0 = run;
-    run += compact(
-        nc, [&](int e) { return sel_of(tid + kThreads * (c0 + e)); },
-        [&](int e, uint32_t pos) {
-          const int j = tid + kThreads * (c0 + e);
-          pos += base0;
-          if (pos < (uint32_t)a.k) {
-            const int p = list_of(j);
-            uint32_t base = 0;
-            for (int q = 0; q < p; ++q) base += sl.lcnt[q];
-            const int64_t el = elem(j);
-            oid[pos] = a.cand_id[el];
-            a.owner_row[((int64_t)p * a.N + n) * a.k + (pos - base)] = a.cand_row[el];
-          }
-        },
-        sl);
-  }
-  // counts (capped at k over the rank-major order) and padding
-  uint32_t base = 0;
-  for (int p = 0; p < a.P; ++p) {
-    const uint32_t c = sl.lcnt[p];
-    const uint32_t kept = base >= (uint32_t)a.k ? 0u : (base + c <= (uint32_t)a.k ? c : (uint32_t)a.k - base);
-    int32_t* orow = a.owner_row + ((int64_t)p * a.N + n) * a.k;
-    for (int q = (int)kept + tid; q < a.k; q += kThreads) orow[q] = -1;
-    if (tid == 0) a.owner_count[(int64_t)p * a.N + n] = (int32_t)kept;
-    base += c;
-  }
-  const int c = run < (uint32_t)a.k ? (int)run : a.k;
-  for (int q = c + tid; q < a.k; q += kThreads) oid[q] = -1;
 }
 
 }  // namespace

@@ -45,7 +45,7 @@ def _i32(x):
     return H.i32_tensor(np.asarray(x, np.int32))
 
 
-@pytest.mark.parametrize("L,k", [(0, 4), (1, 1), (100, 0), (100, 64), (5000, 2048), (16384, 2048), (3000, 5000)])
+@pytest.mark.parametrize("L,k", [(0, 4), (1, 1), (100, 0), (100, 64), (5000, 2048), (16384, 2048), (3000, 5000), (16385, 700), (40000, 3000)])
 def test_local_topk_bit_exact(cpa, L, k):
     rng = np.random.default_rng(L + k)
     N = 6
@@ -86,7 +86,7 @@ def _local_lists(cpa, s_global, C, k, layout="round_robin"):
 
 
 @pytest.mark.parametrize("layout", ["round_robin", "contiguous"])
-@pytest.mark.parametrize("L,C,k", [(1000, 4, 64), (37, 8, 5), (20000, 8, 2048), (10, 3, 40)])
+@pytest.mark.parametrize("L,C,k", [(1000, 4, 64), (37, 8, 5), (20000, 8, 2048), (10, 3, 40), (70000, 4, 5000)])
 def test_merge_bit_exact_and_exact_global(cpa, layout, L, C, k):
     rng = np.random.default_rng(L * C + k)
     N = 5
