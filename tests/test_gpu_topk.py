@@ -86,7 +86,7 @@ def _local_lists(cpa, s_global, C, k, layout="round_robin"):
 
 
 @pytest.mark.parametrize("layout", ["round_robin", "contiguous"])
-@pytest.mark.parametrize("L,C,k", [(1000, 4, 64), (37, 8, 5), (20000, 8, 2048), (10, 3, 40), (70000, 4, 5000)])
+@pytest.mark.parametrize("L,C,k", [(1000, 4, 64), (37, 8, 5), (20000, 8, 2048), (10, 3, 40), (70000, 4, 5000), (3000, 64, 40)])
 def test_merge_bit_exact_and_exact_global(cpa, layout, L, C, k):
     rng = np.random.default_rng(L * C + k)
     N = 5
