@@ -564,17 +564,14 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(cpa::TopkMergeArgs
     const uint32_t run =
         t.lo ? compact<true>(0, sel(std::true_type{}), emit, sl) : compact<true>(0, sel(std::false_type{}), emit, sl);
     const int c = run < (uint32_t)a.k ? (int)run : a.k;
-    // the listed candidates run list by list: lane p finds where list p starts
+    // where list p's run starts in the output: the selected candidates before
+    // its first one, from the compaction's cell offsets and ballots
     if (tid < 64) {
       if (tid < a.P) {
-        const uint32_t first = (uint32_t)(tid * a.k_in);
-        int lo = 0, hi = c;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (skl[mid] < first) lo = mid + 1;
-          else hi = mid;
-        }
-        sl.lbase[tid] = (uint32_t)lo;
+        const int j0 = tid * a.k_in;  // < 16384
+        const int e = j0 >> 10, cw = (j0 >> 6) & (kWaves - 1), cl = j0 & 63;
+        const uint32_t before = sl.off[e][cw] + (uint32_t)__popcll(sl.mask[e][cw] & ((1ull << cl) - 1ull));
+        sl.lbase[tid] = before < (uint32_t)c ? before : (uint32_t)c;
       }
       if (tid == 0) sl.lbase[a.P] = (uint32_t)c;
     }
