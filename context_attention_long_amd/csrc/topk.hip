@@ -61,6 +61,7 @@ struct alignas(16) SelectLds {
   uint32_t lcnt[64];          // selected per source list (merge of long lists)
   uint32_t lbase[65];         // first output position of each source list (merge)
   int32_t cnt_in[64];         // entries of each source list (merge)
+  uint4 item[64];             // merge load items (see merge_items)
   uint32_t wsum[kWaves];
   uint32_t bcast[4];
 };
@@ -339,35 +340,45 @@ __device__ __forceinline__ void keys_to_lds(uint32_t* skl, int nv, const float* 
   }
 }
 
-// The merge's score keys into LDS: entry s of list p goes to word
-// p k_in + s (key 0 past the list's count), words from P k_in on get key 0;
-// skl holds 1024 more words, written but never read.
-// A batch of 16 loads walks (list, block of 1024 entries) items in order,
-// the same items for every lane, so the list, its count and its base
-// address stay scalar. cntv: lane p holds list p's count.
-__device__ __forceinline__ void merge_keys_to_lds(uint32_t* skl, const cpa::TopkMergeArgs& a, int n, int cntv,
+// The merge loads its P lists as (list p, block i of 1024 entries) items,
+// f = p nblk + i, at most 64 when the keys fit LDS. Lane f of wave 0 writes
+// item f: {element offset of entry 1024 i (2 words), its LDS word p k_in +
+// 1024 i, entries with a score (up to 1024) | entries inside the list << 16};
+// items past P nblk are empty. c: lane p's list count.
+__device__ __forceinline__ void merge_items(const cpa::TopkMergeArgs& a, int n, int c, SelectLds& sl) {
+  const int f = threadIdx.x & 63;
+  const int nblk = (a.k_in + kThreads - 1) / kThreads;
+  const int p = nblk > 0 ? f / nblk : 0, i = f - p * nblk;
+  const int cp = __shfl(c, p & 63);
+  uint4 d = {0u, 0u, (uint32_t)kLdsCands, 0u};
+  if (f < a.P * nblk) {
+    const int64_t e = (int64_t)p * ((int64_t)a.N * a.k_in) + (int64_t)n * a.k_in + kThreads * i;
+    const int has = min(max(cp - kThreads * i, 0), kThreads), in = min(a.k_in - kThreads * i, kThreads);
+    d = uint4{(uint32_t)e, (uint32_t)(e >> 32), (uint32_t)(p * a.k_in + kThreads * i), (uint32_t)has | (uint32_t)in << 16};
+  }
+  sl.item[f] = d;
+}
+
+// The merge's score keys into LDS from the items: entry s of list p goes to
+// word p k_in + s (key 0 past the list's count), words from P k_in on get
+// key 0; skl holds 1024 more words, written but never read (entries past
+// k_in in a list's last block, and empty items, write there).
+__device__ __forceinline__ void merge_keys_to_lds(uint32_t* skl, const cpa::TopkMergeArgs& a, const SelectLds& sl,
                                                   uint32_t& kand, uint32_t& kor) {
   const int tid = threadIdx.x;
-  const int nblk = (a.k_in + kThreads - 1) / kThreads;
-  const int nitem = a.P * nblk;
-  const int64_t plane = (int64_t)a.N * a.k_in;
+  const int nitem = a.P * ((a.k_in + kThreads - 1) / kThreads);
   kand = ~0u, kor = 0u;
-  int p = 0, i = 0;  // the next item: list p, entries 1024 i + thread
-  for (int f0 = 0; f0 < nitem; f0 += kE) {
+  for (int f0 = 0; f0 < nitem; f0 += kE) {  // nitem <= 64: items f0 .. f0 + 15 all exist
     float v[kE];
     int slot[kE];
     bool ok[kE];
 #pragma unroll
     for (int u = 0; u < kE; ++u) {
-      const int s = tid + kThreads * i;
-      const bool lst = p < a.P;
-      const int cnt = __builtin_amdgcn_readlane(cntv, p & 63);
-      ok[u] = s < (lst ? cnt : 0);
-      // entries past k_in (the last block of a list) write a dead word
-      slot[u] = lst && s < a.k_in ? p * a.k_in + s : kLdsCands + tid;
-      const int64_t base = (int64_t)p * plane + (int64_t)n * a.k_in;
-      v[u] = a.cand_score[ok[u] ? base + s : 0];  // every lane loads (element 0 stands in)
-      if (++i == nblk) i = 0, ++p;
+      const uint4 d = sl.item[f0 + u];
+      ok[u] = tid < (int)(d.w & 0xffffu);
+      slot[u] = tid < (int)(d.w >> 16) ? (int)d.z + tid : kLdsCands + tid;
+      const int64_t e = (int64_t)(((uint64_t)d.y << 32) | d.x) + tid;
+      v[u] = a.cand_score[ok[u] ? e : 0];  // every lane loads (element 0 stands in)
     }
 #pragma unroll
     for (int u = 0; u < kE; ++u) {
@@ -522,6 +533,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(cpa::TopkMergeArgs
     sl.lcnt[tid] = 0;
     const uint32_t t = wave_incl_sum((uint32_t)c);  // lane 63: the total over the lists
     if (tid == 63) sl.wsum[0] = t;
+    if constexpr (kLds) merge_items(a, n, c, sl);
   }
   __syncthreads();
   const uint32_t total = sl.wsum[0];
@@ -547,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(cpa::TopkMergeArgs
   if constexpr (kLds) {
     const int npad = (M + kVisit - 1) / kVisit * kVisit;
     uint32_t kand, kor;
-    merge_keys_to_lds(skl, a, n, sl.cnt_in[tid & 63], kand, kor);
+    merge_keys_to_lds(skl, a, sl, kand, kor);
     __syncthreads();
     auto each = [&](auto&& f) { each_lds(skl, npad, f); };
     const Thresh t = radix_select(total, (uint32_t)npad - total, a.k, kand, kor, each, low, sl);
