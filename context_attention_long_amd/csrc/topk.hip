@@ -19,11 +19,10 @@
 // exactly the entries still needed. The selection is then every key at or
 // above one 64-bit threshold; a stable compaction takes it in candidate
 // order. Up to 16384 candidates per row keep their score keys in LDS (64 KB,
-// candidate j at word j, key 0 in the empty words up to a multiple of 4096)
-// for all passes; the compaction then lists the selected candidates in the
-// same words, and their scores, ids and rows are read in one batch. Longer
-// rows are re-read from memory (L2) on every pass and written out chunk by
-// chunk.
+// candidate j at word j, key 0 in the other words) for all passes; the
+// compaction then lists the selected candidates in the same words, and their
+// scores, ids and rows are read in one batch. Longer rows are re-read from
+// memory (L2) on every pass and written out chunk by chunk.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -32,7 +31,7 @@
 
 namespace {
 
-constexpr int kThreads = 1024;            // 16 wavefronts: the passes are latency-bound
+constexpr int kThreads = 1024;            // 16 wavefronts per row
 constexpr int kWaves = kThreads / 64;
 constexpr int kE = 16;                     // chunks of 1024 candidates per compaction round
 constexpr int kLdsCands = kE * kThreads;   // 16384 candidates with keys in LDS
@@ -87,7 +86,7 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
   return wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
-// The digit search of one radix pass over the per-wave histograms: the digit
+// The digit search of one radix pass over the histogram's copies: the digit
 // d holding the need-th largest key, the count of entries in bins above d and
 // in bin d. `phantom` visited slots with key 0 (no candidate) sit in bin 0
 // and are taken out. Every thread returns the result.
