@@ -237,6 +237,7 @@ __device__ __forceinline__ Thresh radix_select(uint32_t total, uint32_t phantom,
 template <bool kAll = false, typename Sel, typename Emit>
 __device__ __forceinline__ uint32_t compact(int nchunk, Sel&& sel, Emit&& emit, SelectLds& sl) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t mine = 0;  // kAll: bit e = this thread's candidate of chunk e is selected
   if constexpr (kAll) nchunk = kE;
   auto chunks = [&](auto&& f) {
     if constexpr (kAll) {
@@ -253,6 +254,8 @@ __device__ __forceinline__ uint32_t compact(int nchunk, Sel&& sel, Emit&& emit, 
     bool s[kE];
 #pragma unroll
     for (int e = 0; e < kE; ++e) s[e] = sel(e);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) mine |= (uint32_t)s[e] << e;
     int mlo = 0, mhi = 0;
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
@@ -291,17 +294,11 @@ __device__ __forceinline__ uint32_t compact(int nchunk, Sel&& sel, Emit&& emit, 
   }
   __syncthreads();
   if constexpr (kAll) {
-    // lane e reads chunk e's ballot and offset; each chunk takes them from it
-    uint64_t mm = 0;
-    uint32_t oo = 0;
-    if (lane < kE) mm = sl.mask[lane][w], oo = sl.off[lane][w];
-#pragma unroll
-    for (int e = 0; e < kE; ++e) {
-      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mm, e);
-      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mm >> 32), e);
-      const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)oo, e);
-      const uint32_t below = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-      if ((((uint64_t)hi << 32 | lo) >> lane) & 1ull) emit(e, o + below);
+    // each lane visits only its selected chunks (a small share of the 16)
+    for (uint32_t bits = mine; bits; bits &= bits - 1u) {
+      const int e = __builtin_ctz(bits);
+      const uint64_t m = sl.mask[e][w];
+      emit(e, sl.off[e][w] + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)));
     }
   } else {
     chunks([&](int e) {
