@@ -117,8 +117,9 @@ __device__ __forceinline__ void pick_digit(SelectLds& sl, uint32_t need, uint32_
     }
   }
   __syncthreads();
+  // (no barrier after the read: bcast is written again only after the next
+  // pass's two barriers, and the histogram reads are done)
   d = sl.bcast[0], above = sl.bcast[1], bin = sl.bcast[2];
-  __syncthreads();
 }
 
 // Histogram add of one digit per lane (lanes with in = false skip): one LDS
