@@ -177,19 +177,31 @@ __device__ __forceinline__ int common_bits(uint32_t& kand, uint32_t kor, SelectL
 // kand / kor: this thread's AND and OR over the score keys (key 0 left out).
 // A slot without candidate has key 0, below every candidate, so it can only
 // sit in the bins of the all-zero prefix, from which pick_digit removes it.
-template <typename Each, typename Low>
+// kTop: the histogram already holds the top 8 bits of every candidate's key
+// (counted while the keys were loaded; empty slots not counted).
+template <bool kTop = false, typename Each, typename Low>
 __device__ __forceinline__ Thresh radix_select(uint32_t total, uint32_t phantom, int k, uint32_t kand, uint32_t kor,
                                                Each&& each, Low&& low, SelectLds& sl) {
   if (total <= (uint32_t)k) return Thresh{0u, 0u};
   if (k <= 0) return Thresh{~0u, ~0u};
-  // the first digit starts below the shared leading bits (the merge's
-  // candidates all lie in the upper tail, where the top digit would put
-  // almost everything into one or two bins)
-  const int cb = common_bits(kand, kor, sl);
+  // the digits start below the shared leading bits (the merge's candidates
+  // all lie in the upper tail, where the top digit would put almost
+  // everything into one or two bins)
+  const int cb = common_bits(kand, kor, sl);  // (its barrier also publishes a kTop histogram)
   int prev = 64 - cb;  // key bits below the known prefix
   uint64_t prefix = (uint64_t)kand >> (32 - cb);
   int shift = prev;
   uint32_t need = (uint32_t)k;
+  if constexpr (kTop) {
+    uint32_t d, above, bin;
+    pick_digit(sl, need, 0u, d, above, bin);
+    need -= above;
+    if (bin == need) {
+      const uint64_t thr = (uint64_t)d << 56;
+      return Thresh{(uint32_t)(thr >> 32), 0u};
+    }
+    if (cb <= 8) prefix = d, prev = 56;  // else the shared bits (d among them) go further
+  }
   while (prev > 0) {
     const int sh = prev > 32 ? max(prev - 8, 32) : prev - 8;
     const uint32_t dmask = (1u << (prev - sh)) - 1u;
@@ -320,7 +332,7 @@ __device__ __forceinline__ uint32_t compact(int nchunk, Sel&& sel, Emit&& emit, 
 // score v and must be safe for any j < 16384 (v is junk for j >= nv).
 template <typename Addr, typename Key>
 __device__ __forceinline__ void keys_to_lds(uint32_t* skl, int nv, const float* base, Addr&& addr, Key&& key,
-                                            uint32_t& kand, uint32_t& kor) {
+                                            uint32_t& kand, uint32_t& kor, SelectLds& sl) {
   const int tid = threadIdx.x;
   kand = ~0u, kor = 0u;
   float v[kE];  // one batch of 16 loads in flight
@@ -334,6 +346,7 @@ __device__ __forceinline__ void keys_to_lds(uint32_t* skl, int nv, const float* 
     skl[j] = kj;
     kor |= kj;
     kand &= kj ? kj : ~0u;
+    hist_add(sl, kj != 0u, kj >> 24);  // the first radix digit
   }
 }
 
@@ -360,7 +373,7 @@ __device__ __forceinline__ void merge_items(const cpa::TopkMergeArgs& a, int n, 
 // word p k_in + s (key 0 past the list's count), words from P k_in on get
 // key 0; skl holds 1024 more words, written but never read (entries past
 // k_in in a list's last block, and empty items, write there).
-__device__ __forceinline__ void merge_keys_to_lds(uint32_t* skl, const cpa::TopkMergeArgs& a, const SelectLds& sl,
+__device__ __forceinline__ void merge_keys_to_lds(uint32_t* skl, const cpa::TopkMergeArgs& a, SelectLds& sl,
                                                   uint32_t& kand, uint32_t& kor) {
   const int tid = threadIdx.x;
   const int nitem = a.P * ((a.k_in + kThreads - 1) / kThreads);
@@ -383,6 +396,7 @@ __device__ __forceinline__ void merge_keys_to_lds(uint32_t* skl, const cpa::Topk
       skl[slot[u]] = kj;
       kor |= kj;
       kand &= kj ? kj : ~0u;
+      hist_add(sl, kj != 0u, kj >> 24);  // the first radix digit
     }
   }
   for (int j = a.P * a.k_in + tid; j < kLdsCands; j += kThreads) skl[j] = 0u;
@@ -421,11 +435,13 @@ __global__ __launch_bounds__(kThreads) void topk_local_kernel(cpa::TopkLocalArgs
   if constexpr (kLds) {
     const int npad = (nv + kVisit - 1) / kVisit * kVisit;
     uint32_t kand, kor;
+    clear_hist(sl);
+    __syncthreads();
     keys_to_lds(
-        skl, nv, sc, [](int j) { return j; }, [](int, float v) { return score_key(v); }, kand, kor);
+        skl, nv, sc, [](int j) { return j; }, [](int, float v) { return score_key(v); }, kand, kor, sl);
     __syncthreads();
     auto each = [&](auto&& f) { each_lds(skl, npad, f); };
-    const Thresh t = radix_select((uint32_t)nv, (uint32_t)(npad - nv), a.k, kand, kor, each, low, sl);
+    const Thresh t = radix_select<true>((uint32_t)nv, (uint32_t)(npad - nv), a.k, kand, kor, each, low, sl);
     // the selected slots in candidate order replace the keys (every key read
     // is done before the first write: compact synchronises in between)
     auto emit = [&](int e, uint32_t pos) {
@@ -532,6 +548,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(cpa::TopkMergeArgs
     if (tid == 63) sl.wsum[0] = t;
     if constexpr (kLds) merge_items(a, n, c, sl);
   }
+  if constexpr (kLds) clear_hist(sl);
   __syncthreads();
   const uint32_t total = sl.wsum[0];
   // candidate j is entry s = j mod k_in of list p = j / k_in. With the keys
@@ -559,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(cpa::TopkMergeArgs
     merge_keys_to_lds(skl, a, sl, kand, kor);
     __syncthreads();
     auto each = [&](auto&& f) { each_lds(skl, npad, f); };
-    const Thresh t = radix_select(total, (uint32_t)npad - total, a.k, kand, kor, each, low, sl);
+    const Thresh t = radix_select<true>(total, (uint32_t)npad - total, a.k, kand, kor, each, low, sl);
     // the selected candidates in candidate order replace the keys
     auto emit = [&](int e, uint32_t pos) {
       if (pos < (uint32_t)a.k) skl[pos] = (uint32_t)(tid + kThreads * e);
