@@ -11,6 +11,9 @@
 // Mixing these loads with compiler-issued vector loads is safe: vector-memory
 // loads complete in issue order, so loads added behind a compiler load can
 // only make the compiler's own vmcnt waits stricter.
+//
+// Every statement sets M0 (the LDS destination) itself and lists it as
+// clobbered, so the compiler never assumes M0 survives one of them.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,12 +40,12 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
                  :
                  : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
+                 : "memory", "m0");
   else
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Same, addressed as a wavefront-uniform 64-bit base plus a per-lane 32-bit
@@ -57,12 +60,12 @@ __device__ __forceinline__ void lds_dma16_sbase(const void* sbase, uint32_t voff
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :
                  : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
+                 : "memory", "m0");
   else
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Same, with the base address and the LDS address already wavefront-uniform
@@ -71,9 +74,9 @@ __device__ __forceinline__ void lds_dma16_sbase(const void* sbase, uint32_t voff
 template <Policy P = Policy::kReuse>
 __device__ __forceinline__ void lds_dma16_s(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
   if constexpr (P == Policy::kStream)
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
   else
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
 }
 
 // Wavefront-uniform copy of a pointer (its SGPR form).
@@ -91,12 +94,12 @@ __device__ __forceinline__ void lds_dma4(const void* gsrc, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off nt"
                  :
                  : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
+                 : "memory", "m0");
   else
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                  :
                  : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Same, addressed as a wavefront-uniform base (SGPRs) plus a per-lane 32-bit
@@ -104,9 +107,9 @@ __device__ __forceinline__ void lds_dma4(const void* gsrc, uint32_t lds_base) {
 template <Policy P = Policy::kReuse>
 __device__ __forceinline__ void lds_dma4_s(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
   if constexpr (P == Policy::kStream)
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1 nt" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1 nt" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
   else
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wavefront are

@@ -66,7 +66,7 @@ typedef struct cpa_tensor {
  * and holds its prefix and new tokens in original order, so the row reads
  * K/V rows [kv_row0, kv_row0 + pos0 + i * pos_stride + 1).
  *   zigzag:     stride 1, one segment per non-empty block; the block's
- *               "where the reads end" (Long Context 2.3) is pos0 + q_len.
+ *               reads stop at position pos0 + q_len (Long Context 2.3).
  *   interleave: stride C, one segment per request (each query's own causal
  *               extent, SGLang docs "Interleave strategy").
  */
@@ -241,10 +241,10 @@ cpa_status attn_merge_states(int32_t n_states, const cpa_tensor* o_parts,
                              const cpa_tensor* lse_out, void* stream);
 
 /*
- * Round-robin decode storage (Long Context 3.1: "it stores token p of a
- * request on GPU p mod C"; the reading and writing code translates a slot
- * into gpu = slot % C and row = slot / C; DeepSeek-V4 notes, section 5:
- * owner(j) = j mod P).
+ * Round-robin decode storage (Long Context 3.1 and Figure 7: slot p of a
+ * request lives on rank p mod C as local row p / C, and both the cache
+ * write and the attention read translate a slot that way; DeepSeek-V4
+ * notes, section 5: owner(j) = j mod P).
  *
  * cp_round_robin_slot: host, pure. *rank = slot % C, *row = slot / C.
  * CPA_E_INVAL if slot < 0, C < 1 or an output is NULL.

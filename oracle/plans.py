@@ -19,8 +19,8 @@ and 2C-1-r, the split restarts for every request; when the length does not
 divide, the early blocks take the remainder. Reading taken: the first
 ``L mod 2C`` blocks get one extra token each. Rows are request-major, the
 early block before the late one. Each non-empty block is one segment with
-stride 1; "where that block's reads end" (*Long Context* 2.3) is
-``pos0 + q_len``. A cached prefix is not split; both blocks read it
+stride 1; the position where the block's key reads stop (*Long Context*
+2.3) is ``pos0 + q_len``. A cached prefix is not split; both blocks read it
 (*Long Context* 2.3, last paragraph; the docs' metadata paragraph).
 
 Interleave -- SGLang prefill CP, "Interleave strategy"; *Long Context* 2.4:
@@ -168,7 +168,7 @@ def causal_pairs(plan):
 #
 # Decode CP with round-robin storage -- *Long Context* 3.1: with C GPUs,
 # token (slot) p of a request is stored on GPU p mod C, as row p // C of
-# that GPU's cache ("slot 9 on 4 GPUs is row 2 on GPU 1"); the
+# that GPU's cache (the page's example: slot 9 with C = 4 is GPU 1, row 2); the
 # "DeepSeek-V4 Attention Inference Systems" notes, section 5, write the same
 # owner rule as owner(j) = j mod P, and 5.3 adds that entries replicated on
 # every rank (a local window, attention sinks) must add their probability

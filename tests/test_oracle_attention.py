@@ -250,3 +250,29 @@ def test_fp8_decode_uses_scale_per_token():
     deq = formats.e4m3_to_f64(codes) * scale[..., None]
     O2, L2 = att.decode_shard(q, deq, [0], [20], 0.25, dv=8)
     assert np.allclose(O, O2, atol=1e-15) and np.allclose(L, L2, atol=1e-15)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (8, 2), (6, 3)])
+def test_decode_equals_library_last_row(Hq, Hkv):
+    """A decode query over the whole cache [0, L) is the causal attention of
+    the sequence's last token (Long Context 1.1 and 3.2): compare
+    decode_shard with torch's float64 causal flash attention, GQA heads
+    broadcast in contiguous groups, and with two shards merged."""
+    rng = np.random.default_rng(40 + Hq + Hkv)
+    L, D = 19, 16
+    G = Hq // Hkv
+    q_all = rng.standard_normal((L, Hq, D))
+    k = rng.standard_normal((L, Hkv, D))
+    v = rng.standard_normal((L, Hkv, D))
+    scale = 0.3
+    kb = np.repeat(k, G, axis=1).transpose(1, 0, 2).copy()
+    vb = np.repeat(v, G, axis=1).transpose(1, 0, 2).copy()
+    o_ref, lse_ref = _lib_causal(q_all.transpose(1, 0, 2).copy(), kb, vb, scale)
+    q = q_all[L - 1][None]                      # [1, Hq, D]
+    O, LSE = att.decode_shard(q, k[None], [0], [L], scale, vcache=v[None])
+    assert np.allclose(O[0], o_ref[:, L - 1], atol=1e-13)
+    assert np.allclose(LSE[0], lse_ref[:, L - 1], atol=1e-13)
+    parts = [att.decode_shard(q, k[None], [s0], [s1], scale, vcache=v[None]) for s0, s1 in ((0, 7), (7, L))]
+    Om, Lm = att.merge_states(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    assert np.allclose(Om[0], o_ref[:, L - 1], atol=1e-13)
+    assert np.allclose(Lm[0], lse_ref[:, L - 1], atol=1e-13)

@@ -63,7 +63,8 @@ def test_brute_force_order_on_tiny_inputs():
     rng = np.random.default_rng(1)
     for _ in range(200):
         n = int(rng.integers(0, 10))
-        s = rng.integers(-2, 3, size=n).astype(np.float64)
+        # values with many ties, -0.0 among them (equal to +0.0 as numbers)
+        s = rng.choice(np.array([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0]), size=n)
         ids = rng.permutation(50)[:n]
         k = int(rng.integers(0, 12))
 
@@ -94,6 +95,7 @@ def test_closed_forms():
     assert topk.select(np.zeros(6), np.arange(6)[::-1], 2).tolist() == [4, 5]   # ids 1 and 0
     assert topk.select(np.array([np.nan, -np.inf]), np.arange(2), 1).tolist() == [1]
     assert topk.select(np.array([-0.0, 0.0]), np.array([1, 0]), 1).tolist() == [1]
+    assert topk.select(np.array([0.0, -0.0]), np.array([1, 0]), 1).tolist() == [1]   # -0 = +0: lower id
 
 
 def test_local_tie_break_by_row_is_detected():
