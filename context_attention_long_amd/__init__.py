@@ -58,7 +58,7 @@ SYMBOLS = ("cpa_last_error", "cpa_abi_version", "cp_plan_zigzag", "cp_plan_inter
            "attn_prefill_shard", "attn_decode_workspace_size", "attn_decode_shard", "attn_merge_states",
            "cp_round_robin_slot", "cp_plan_round_robin", "attn_cache_write_round_robin",
            "attn_decode_shard_mq", "cp_plan_multi_query", "attn_sparse_mla_workspace_size", "attn_sparse_mla",
-           "attn_topk_local", "attn_topk_merge")
+           "attn_topk_local", "attn_topk_merge", "attn_decode_shard_noalloc")
 
 _lib_handle = None
 
@@ -90,6 +90,10 @@ def lib():
         L.attn_decode_shard.argtypes = [P(CpaTensor), P(CpaTensor), P(CpaTensor), P(CpaTensor), ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, P(CpaTensor),
                                         P(CpaTensor), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.attn_decode_shard_noalloc.restype = ctypes.c_int
+        L.attn_decode_shard_noalloc.argtypes = [P(CpaTensor), P(CpaTensor), P(CpaTensor), P(CpaTensor),
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                                P(CpaTensor), P(CpaTensor), ctypes.c_void_p]
         L.attn_decode_shard_mq.restype = ctypes.c_int
         L.attn_decode_shard_mq.argtypes = L.attn_decode_shard.argtypes
         L.cp_plan_multi_query.restype = ctypes.c_int
@@ -319,6 +323,27 @@ def attn_decode_shard(q, kcache, vcache, kv_begin, kv_end, max_shard_len, softma
                                    ctypes.c_void_p(kv_begin.data_ptr()), ctypes.c_void_p(kv_end.data_ptr()),
                                    int(max_shard_len), float(softmax_scale), ctypes.byref(do), ctypes.byref(dl),
                                    ctypes.c_void_p(ws_ptr), ws_bytes, _stream(stream)))
+    return o_part, lse_part
+
+
+def attn_decode_shard_noalloc(q, kcache, vcache, kv_begin, kv_end, max_shard_len, softmax_scale, o_part, lse_part,
+                              kv_scale=None, stream=None, kcache_dtype=None):
+    """attn_decode_shard without a workspace: the split states live in the
+    library's per-device scratch array, so the call allocates nothing (the
+    caller passes o_part [B, Hq, Dv] and lse_part [B, Hq]). Calls that
+    overlap on one GPU race on that array."""
+    torch = _torch()
+    dq, dk = tensor_desc(q), tensor_desc(kcache, kcache_dtype)
+    dv = tensor_desc(vcache) if vcache is not None else None
+    ds = tensor_desc(kv_scale) if kv_scale is not None else None
+    do, dl = tensor_desc(o_part), tensor_desc(lse_part)
+    for t in (kv_begin, kv_end):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != q.device:
+            raise TypeError("kv_begin / kv_end must be contiguous int32 tensors on the query's device")
+    _check(lib().attn_decode_shard_noalloc(ctypes.byref(dq), ctypes.byref(dk), _ptr(dv), _ptr(ds),
+                                           ctypes.c_void_p(kv_begin.data_ptr()), ctypes.c_void_p(kv_end.data_ptr()),
+                                           int(max_shard_len), float(softmax_scale), ctypes.byref(do),
+                                           ctypes.byref(dl), _stream(stream)))
     return o_part, lse_part
 
 

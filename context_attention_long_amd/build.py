@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
 
 SOURCES = ["plan.cpp", "api.cpp", "merge.hip", "decode_gqa.hip", "decode_mla.hip", "prefill.hip", "prefill_mla.hip", "cache_write.hip",
-           "sparse_mla.hip", "topk.hip"]
+           "sparse_mla.hip", "topk.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 ROCM_INCLUDE = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")

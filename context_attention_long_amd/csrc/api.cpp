@@ -211,7 +211,8 @@ cpa_status decode_plan(int64_t rows, const cpa_tensor* kcache, const cpa_tensor*
 cpa_status decode_impl(const cpa_tensor* q, int64_t Q, int64_t q_q, const cpa_tensor* kcache,
                        const cpa_tensor* vcache, const cpa_tensor* kv_scale, const int32_t* kv_begin,
                        const int32_t* kv_end, int64_t max_shard_len, float softmax_scale, const cpa_tensor* o_part,
-                       const cpa_tensor* lse_part, void* workspace, size_t ws_bytes, void* stream) {
+                       const cpa_tensor* lse_part, void* workspace, size_t ws_bytes, void* stream,
+                       bool lib_scratch = false) {
   CPA_TRY(check_tensor(q, "decode q", (1u << CPA_F32) | (1u << CPA_BF16), 3));
   CPA_TRY(check_tensor(kcache, "decode kcache", (1u << CPA_F32) | (1u << CPA_BF16) | (1u << CPA_FP8_E4M3), 4));
   CPA_TRY(check_tensor(o_part, "decode o_part", 1u << CPA_F32, 3));
@@ -272,6 +273,11 @@ cpa_status decode_impl(const cpa_tensor* q, int64_t Q, int64_t q_q, const cpa_te
   const int64_t n_wg = p.mla ? ((B * p.nsplit + 7) / 8 * 8 * Q) : R * Hkv * p.nsplit;
   if (n_wg > INT32_MAX) return fail(CPA_E_INVAL, "decode: %lld workgroups exceed the grid limit", (long long)n_wg);
   const size_t need = decode_ws_bytes(R, Hq, Dv, p.nsplit);
+  if (lib_scratch && need > ws_bytes)
+    return fail(CPA_E_CAPACITY,
+                "decode_noalloc: this shape needs %zu bytes of split scratch, the library holds %zu per device; "
+                "use attn_decode_shard with a workspace",
+                need, ws_bytes);
   if (ws_bytes < need || (need > 0 && workspace == nullptr))
     return fail(CPA_E_CAPACITY, "decode: workspace of %zu bytes needed, %zu given", need, ws_bytes);
   if (need > 0 && ((uintptr_t)workspace) % 256) return fail(CPA_E_INVAL, "decode: workspace must be 256-byte aligned");
@@ -389,6 +395,19 @@ extern "C" cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* k
   cpa::clear_error();
   return decode_impl(q, 1, 0, kcache, vcache, kv_scale, kv_begin, kv_end, max_shard_len, softmax_scale, o_part,
                      lse_part, workspace, ws_bytes, stream);
+}
+
+extern "C" cpa_status attn_decode_shard_noalloc(const cpa_tensor* q, const cpa_tensor* kcache,
+                                                const cpa_tensor* vcache, const cpa_tensor* kv_scale,
+                                                const int32_t* kv_begin, const int32_t* kv_end,
+                                                int64_t max_shard_len, float softmax_scale,
+                                                const cpa_tensor* o_part, const cpa_tensor* lse_part,
+                                                void* stream) {
+  cpa::clear_error();
+  void* scratch = nullptr;
+  CPA_TRY(hip_status(cpa::noalloc_scratch(&scratch), "decode_noalloc: scratch lookup"));
+  return decode_impl(q, 1, 0, kcache, vcache, kv_scale, kv_begin, kv_end, max_shard_len, softmax_scale, o_part,
+                     lse_part, scratch, cpa::kNoAllocScratchBytes, stream, true);
 }
 
 extern "C" cpa_status attn_decode_shard_mq(const cpa_tensor* q, const cpa_tensor* kcache,

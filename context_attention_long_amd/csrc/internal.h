@@ -145,6 +145,15 @@ struct CacheWriteArgs {
   int32_t vec16;        // 16-byte lanes (row size and strides multiples of 16)
 };
 
+// ---- library-owned scratch of the entry points that allocate nothing ----
+// Bytes of the per-device scratch array (noalloc.hip): the split states of
+// one decode launch, e.g. 4 splits of 64 requests x 64 heads x 512 dims
+// (33.6 MB) fit; 2 splits of 200 requests (52 MB) do not.
+constexpr size_t kNoAllocScratchBytes = (size_t)48 << 20;
+// Device address of the current device's scratch array (looked up once per
+// device); returns hipSuccess or the lookup's error.
+int noalloc_scratch(void** ptr);
+
 // ---- launchers (return hipSuccess or the launch error) ----
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_decode_gqa(const DecodeGqaArgs& a, void* stream);

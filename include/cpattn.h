@@ -197,6 +197,23 @@ cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* kcache, cons
                              size_t ws_bytes, void* stream);
 
 /*
+ * attn_decode_shard for callers that cannot allocate device memory (code
+ * under HIP stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and results as
+ * attn_decode_shard, without workspace arguments. The internal split's
+ * partial states live in a scratch array the library holds on every device
+ * it runs on (48 MiB per device, kept until the process ends); the call
+ * allocates nothing. A shape whose split states need more than that returns
+ * CPA_E_CAPACITY (attn_decode_shard with a workspace takes any size). The
+ * array is shared by every call on a GPU: calls that overlap on one GPU
+ * (e.g. on two streams) race and must be serialised by the caller.
+ */
+cpa_status attn_decode_shard_noalloc(const cpa_tensor* q, const cpa_tensor* kcache, const cpa_tensor* vcache,
+                                     const cpa_tensor* kv_scale, const int32_t* kv_begin, const int32_t* kv_end,
+                                     int64_t max_shard_len, float softmax_scale, const cpa_tensor* o_part,
+                                     const cpa_tensor* lse_part, void* stream);
+
+/*
  * Multi-query split-KV decode (speculative / MTP decode under decode CP:
  * Long Context 9 lists it; DeepSeek-V4 notes, 11, sweeps the query/spec
  * width 1, 2, 4, 8). Request b has Q query rows; row k attends cache rows
