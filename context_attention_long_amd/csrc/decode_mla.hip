@@ -7,9 +7,10 @@
 // 5.3 -- one latent vector per token is read by all heads.
 //
 // One workgroup per (query row, split): the split's contiguous token range
-// runs through the wave-specialised MLA core (mla_ws.h), which reads every
-// cache byte from HBM once per workgroup (nontemporal when one query row
-// reads it: the shard is read once per launch). The workgroup writes its
+// runs through the wave-specialised MLA core (mla_ws.h for a bf16 cache,
+// mla_fp8.h for FP8), which reads every cache byte from HBM once per
+// workgroup (nontemporal when one query row reads it: the shard is read once
+// per launch). The workgroup writes its
 // split's normalised output and LSE; the splits of a row are merged by the
 // LSE merge.
 #include <hip/hip_runtime.h>
@@ -17,21 +18,25 @@
 #include "internal.h"
 #include "mla_core.h"
 #include "mla_ws.h"
+#include "mla_fp8.h"
 
 namespace {
 
 using namespace cpa::mla;
 
-// 8 wavefronts: bf16 tiles arrive by direct loads, FP8 tiles are converted
-// into LDS by the PV wavefronts. kP: kStream (one query row per request:
-// every cache byte is read once) or kReuse (several query rows read each
-// tile through the shared L2).
+// 8 wavefronts. bf16 cache: tiles arrive by direct loads (mla_ws.h). FP8
+// cache: the raw codes stay FP8 in LDS and QK runs on the FP8 matrix cores
+// (mla_fp8.h). kP: kStream (one query row per request: every cache byte is
+// read once) or kReuse (several query rows read each tile through the
+// shared L2).
 template <bool kFp8, cpa::Policy kP>
 __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::DecodeMlaArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  constexpr int kTileLds = kFp8 ? f8::kStages * f8::kTileBytes : kSmemBytes;
+  constexpr int kScaleLds = kFp8 ? f8::kStages * f8::kScaleSlot : 16;
+  __shared__ __attribute__((aligned(16))) char smem[kTileLds];
+  __shared__ __attribute__((aligned(16))) char ssc[kScaleLds];
   __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
   __shared__ float alpha_s[2 * kH], lsum_s[kH];
-  const Lds S{smem, plds, alpha_s, lsum_s};
 
   const int u = (int)(blockIdx.x / (8 * a.Q)) * 8 + (int)(blockIdx.x % 8);
   const int k = (int)(blockIdx.x / 8) % a.Q;
@@ -48,52 +53,24 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
   end = end < beg ? beg : (end > a.Lmax ? a.Lmax : end);
   const int64_t len = end - beg;
   const Tiles T(beg + len * split / a.nsplit, beg + len * (split + 1) / a.nsplit, (unsigned)u * 2654435761u >> 7);
-  const LdsBases L = lds_bases(w, g, c);
 
   if (qk_role) {
-    bf16x8 qreg[kQSteps];
-    load_q(a.q + (int64_t)b * a.q_b + (int64_t)k * a.q_q + (int64_t)(16 * w + c) * a.q_h, g, qreg);
+    const uint16_t* qhead = a.q + (int64_t)b * a.q_b + (int64_t)k * a.q_q + (int64_t)(16 * w + c) * a.q_h;
     QkStat st{-INFINITY, 0.f};
     if constexpr (kFp8) {
-      const float* sbase = a.kv_scale + (int64_t)b * a.s_b;
-      const uint32_t st32 = (uint32_t)a.s_t;  // the host bounds the scale stride
-      auto scales = [&](int i, TokScale& ts) {  // the 8 tokens whose scores this lane holds
-        const int64_t tok0 = T.t0 + (int64_t)T.phys(i) * kBN;
-        const int lim = (int)min((int64_t)(kBN - 1), T.t1 - 1 - tok0);
-        const float* sb = sbase + tok0 * a.s_t;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t r = (uint32_t)min(16 * (j >> 2) + 4 * g + (j & 3), lim);
-          if constexpr (kP == cpa::Policy::kStream) ts.v[j] = __builtin_nontemporal_load(sb + r * st32);
-          else ts.v[j] = sb[r * st32];
-        }
-      };
-      // this role's share of the FP8 conversion, 4 units per thread: step i
-      // (before the barrier that publishes tile i+1) converts tile i+1 into
-      // stage (i+1) % 3 from set (i+1) & 1 and refills that set with tile
-      // i+3; the PV role converts its units of the same tile in the same
-      // interval.
-      Fp8Units<4, kP> U;
-      U.base = reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, U.c_t = a.c_t, U.t = tid;
-      if (T.ntiles > 0) U.template prologue<1>(T, S);
-      auto convert_ahead = [&](int i, auto parity) {
-        constexpr int P = decltype(parity)::value;
-        char* dst = S.tiles + ((i + 1) % 3) * kTileBytes;
-        const int refill_t = min(i + 3, T.ntiles - 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          U.convert(j, P ^ 1, dst);
-          U.load(T, refill_t, j, P ^ 1);
-        }
-      };
-      ws_qk<true>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return S.tiles + (i % 3) * kTileBytes; },
-                  scales, [](int) { return 0xffffffffu; }, convert_ahead);
+      const f8::Lds S{smem, ssc, plds, alpha_s, lsum_s};
+      f8::Query Q;
+      f8::load_query(qhead, g, Q);
+      f8::ws_qk(T, w, g, c, f8::bases(w, g, c), Q, a.scale_log2, st, S);
     } else {
-      ws_qk<false>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); },
+      const Lds S{smem, plds, alpha_s, lsum_s};
+      bf16x8 qreg[kQSteps];
+      load_q(qhead, g, qreg);
+      ws_qk<false>(T, w, g, c, lds_bases(w, g, c), qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); },
                    [](int, TokScale&) {}, [](int) { return 0xffffffffu; });
     }
     const float l = sum4_rows(st.l_run);
-    if (g == 0) S.lsum[16 * w + c] = l;
+    if (g == 0) lsum_s[16 * w + c] = l;
     __syncthreads();
     if (g == 0)
       a.lse[(int64_t)split * a.l_s + (int64_t)row * a.l_b + (int64_t)(16 * w + c) * a.l_h] =
@@ -104,12 +81,15 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
     for (int m = 0; m < kMv; ++m)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) oacc[m][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (kFp8)
-      ws_pv_fp8<kP>(T, reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, tid - 256, w, g, c, L,
-                    oacc, S);
-    else
-      ws_pv<kP>(T, reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, tid - 256, w, g, c, L,
-                oacc, S);
+    if constexpr (kFp8) {
+      const f8::Lds S{smem, ssc, plds, alpha_s, lsum_s};
+      f8::ws_pv<kP>(T, reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t,
+                    a.kv_scale + (int64_t)b * a.s_b, a.s_t, tid - 256, w, g, c, f8::bases(w, g, c), oacc, S);
+    } else {
+      const Lds S{smem, plds, alpha_s, lsum_s};
+      ws_pv<kP>(T, reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, tid - 256, w, g, c,
+                lds_bases(w, g, c), oacc, S);
+    }
     __syncthreads();
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
