@@ -13,10 +13,16 @@
 // only make the compiler's own vmcnt waits stricter.
 //
 // Every statement sets M0 (the LDS destination) itself and lists it as
-// clobbered, so the compiler never assumes M0 survives one of them.
+// clobbered, so the compiler never assumes M0 survives one of them. (M0 is
+// a reserved register, for which clang warns that it will not save and
+// restore it around the statement; nothing here needs it restored, so that
+// warning is silenced for this header.)
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace cpa {
 
@@ -120,3 +126,5 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 }  // namespace cpa
+
+#pragma clang diagnostic pop
