@@ -148,8 +148,9 @@ def decode_shard(q, kcache, begin, end, scale, vcache=None, dv=None, decode=None
     kcache  [B, Lmax, Hkv, Dqk]   (decode turns a slice into float64 values,
                                    e.g. fp8 codes times the per-token scale)
     vcache  [B, Lmax, Hkv, Dv] or None for MLA (v = k[..., :dv])
-    kv_scale [B, Lmax] per-token scale or None: the entry of token t is
-            decode(code_t) * kv_scale[b, t] (FP8 cache)
+    kv_scale [B, Lmax] per-token scale or None: every entry of token t's
+            cache row -- its key and, for a GQA cache, its value -- is
+            decode(code) * kv_scale[b, t] (FP8 cache)
     Returns O [B, Hq, Dv] (0 for an empty range), LSE [B, Hq] (-inf if empty).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -164,9 +165,11 @@ def decode_shard(q, kcache, begin, end, scale, vcache=None, dv=None, decode=None
         if s1 <= s0:
             continue
         keys = _f64(kcache[b, s0:s1], decode)  # [n, Hkv, Dqk]
-        if kv_scale is not None:
-            keys = keys * np.asarray(kv_scale[b, s0:s1], np.float32).astype(np.float64)[:, None, None]
         vals = keys[..., :Dv] if vcache is None else _f64(vcache[b, s0:s1], decode)
+        if kv_scale is not None:
+            tok_scale = np.asarray(kv_scale[b, s0:s1], np.float32).astype(np.float64)[:, None, None]
+            keys = keys * tok_scale
+            vals = vals * tok_scale
         for h in range(Hq):
             o, lse = attend(q[b, h], keys[:, h // G, :], vals[:, h // G, :], scale)
             O[b, h] = o

@@ -252,6 +252,34 @@ def test_fp8_decode_uses_scale_per_token():
     assert np.allclose(O, O2, atol=1e-15) and np.allclose(L, L2, atol=1e-15)
 
 
+def test_fp8_gqa_decode_scales_keys_and_values():
+    """GQA FP8 cache: the token's scale multiplies its key and its value
+    (one scale per cache row). Pinned to plain decode over the explicitly
+    dequantised K and V, and to the fact that a common scale c on every
+    token equals decode with the query times c and the output times c."""
+    from oracle import formats
+    import synth
+    rng = np.random.default_rng(81)
+    B, L, Hkv, Hq, D = 2, 23, 2, 6, 16
+    kx = rng.standard_normal((B, L, Hkv, D)).astype(np.float32)
+    vx = rng.standard_normal((B, L, Hkv, D)).astype(np.float32)
+    kc, _ = synth.f32_to_e4m3(kx)
+    vc, _ = synth.f32_to_e4m3(vx)
+    scale = rng.uniform(0.25, 3.0, (B, L)).astype(np.float32)
+    q = rng.standard_normal((B, Hq, D))
+    beg, end = [0, 5], [23, 17]
+    O, Lse = att.decode_shard(q, kc, beg, end, 0.3, vcache=vc, decode=formats.e4m3_to_f64, kv_scale=scale)
+    s64 = scale.astype(np.float64)[:, :, None, None]
+    kd, vd = formats.e4m3_to_f64(kc) * s64, formats.e4m3_to_f64(vc) * s64
+    O2, L2 = att.decode_shard(q, kd, beg, end, 0.3, vcache=vd)
+    assert np.allclose(O, O2, atol=1e-14) and np.allclose(Lse, L2, atol=1e-13)
+    c = 4.0
+    Oc, Lc = att.decode_shard(q, kc, beg, end, 0.3, vcache=vc, decode=formats.e4m3_to_f64,
+                              kv_scale=np.full((B, L), c, np.float32))
+    O3, L3 = att.decode_shard(q * c, formats.e4m3_to_f64(kc), beg, end, 0.3, vcache=formats.e4m3_to_f64(vc))
+    assert np.allclose(Oc, c * O3, atol=1e-12) and np.allclose(Lc, L3, atol=1e-12)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 1), (8, 2), (6, 3)])
 def test_decode_equals_library_last_row(Hq, Hkv):
     """A decode query over the whole cache [0, L) is the causal attention of

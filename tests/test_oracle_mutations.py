@@ -57,8 +57,9 @@ MUTATIONS = [
      "vals = keys[..., :Dv] if v is None else _f64(v[kv0:kv0 + p_hi + 1], decode)",
      "vals = keys[..., -Dv:] if v is None else _f64(v[kv0:kv0 + p_hi + 1], decode)", ATT),
     ("FP8 per-token scale left out", "attention.py",
-     "            keys = keys * np.asarray(kv_scale[b, s0:s1], np.float32).astype(np.float64)[:, None, None]",
-     "            keys = keys", ATT),
+     "            keys = keys * tok_scale\n", "            keys = keys\n", ATT),
+    ("FP8 per-token scale left out of GQA values", "attention.py",
+     "            vals = vals * tok_scale\n", "            vals = vals\n", ATT),
     ("sparse list: last cache row treated as padding", "attention.py",
      "if 0 <= int(t) < Lmax]", "if 0 <= int(t) < Lmax - 1]", SPARSE),
     ("sparse list: entries deduplicated", "attention.py",
