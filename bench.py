@@ -474,6 +474,139 @@ def bench_round_robin(cpa, torch, c, q, cache, steps, warmup, warmup_ms):
                 cache_write_bytes=write_bytes)
 
 
+GQA_SERVING = dict(B=8, Hq=32, Hkv=8, D=128, L=131072, C=8)
+
+
+def _gqa_step_bytes(B, Hq, Hkv, D, L, C, entry, qsz):
+    """Algorithmic bytes of a GQA decode step (C partial launches + merge):
+    the cache read once (`entry` bytes per token and kv head, K and V and any
+    scale share), the queries of every launch, the partial states written and
+    read by the merge, and the merged result."""
+    kv = B * L * Hkv * entry
+    q = C * B * Hq * D * qsz
+    part = C * B * Hq * (D + 1) * 4
+    return kv + q + 2 * part + B * Hq * (D + 1) * 4, kv / C + B * Hq * D * qsz + B * Hq * (D + 1) * 4
+
+
+def _gqa_run(cpa, torch, q, k, v, kvs, L, C, scale, steps, warmup, warmup_ms, flush=None):
+    """Time C partial decode launches over the contiguous shards plus the
+    merge. Returns (ms per step, mean ms per partial launch)."""
+    dev = q.device
+    B, Hq, D = q.shape
+    shards = cpa.cp_decode_shards(L, C)
+    begins = [torch.full((B,), s0, dtype=torch.int32, device=dev) for s0, _ in shards]
+    ends = [torch.full((B,), s1, dtype=torch.int32, device=dev) for _, s1 in shards]
+    max_len = max(s1 - s0 for s0, s1 in shards)
+    po = torch.empty((C, B, Hq, D), dtype=torch.float32, device=dev)
+    pl = torch.empty((C, B, Hq), dtype=torch.float32, device=dev)
+    mo = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ml = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, cpa.attn_decode_workspace_size(B, Hq, D, max_len)), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        for i in range(C):
+            if ev is not None:
+                ev[i][0].record()
+            cpa.attn_decode_shard(q, k, v, begins[i], ends[i], max_len, scale, kv_scale=kvs,
+                                  o_part=po[i], lse_part=pl[i], workspace=ws)
+            if ev is not None:
+                ev[i][1].record()
+        cpa.attn_merge_states(po, pl, out=mo, lse_out=ml)
+
+    _warm(torch, step, warmup, warmup_ms)
+    if flush is None:
+        sev = _events(torch, 1)[0]
+        sev[0].record()
+        for _ in range(steps):
+            step()
+        sev[1].record()
+        torch.cuda.synchronize()
+        ms = sev[0].elapsed_time(sev[1]) / steps
+    else:  # every step after a cache flush, timed alone
+        sevs = _events(torch, steps)
+        for i in range(steps):
+            flush(i)
+            sevs[i][0].record()
+            step()
+            sevs[i][1].record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in sevs]))
+    nl = max(3, steps // 4)
+    evs = [_events(torch, C) for _ in range(nl)]
+    for i in range(nl):
+        if flush is not None:
+            flush(i)
+        step(evs[i])
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([a.elapsed_time(b) for ev in evs for a, b in ev]))
+    return ms, launch_ms
+
+
+def bench_gqa_decode(cpa, torch, steps, warmup, warmup_ms):
+    """Split-KV GQA decode at a serving shape: batch 8, 32 query heads on 8
+    kv heads, head dim 128, a 131072-token context per request cut into C=8
+    contiguous shards, run as 8 partial launches plus the merge; bf16 cache,
+    and FP8 E4M3 with one scale per token (key and value). Inputs: seeded
+    N(0,1) drawn on the device (the 4.3 GB bf16 cache would take a minute
+    on the host). GB/s of algorithmic bytes."""
+    w = GQA_SERVING
+    B, Hq, Hkv, D, L, C = w["B"], w["Hq"], w["Hkv"], w["D"], w["L"], w["C"]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260)
+    q = torch.randn((B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, L, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    v = torch.randn((B, L, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    res = {"workload": "GQA split-KV decode: batch 8, 32 q / 8 kv heads, d=128, 131072-token context, "
+                       "C=8 contiguous shards as 8 partial launches + merge"}
+    ms, lms = _gqa_run(cpa, torch, q, k, v, None, L, C, scale, steps, warmup, warmup_ms)
+    sb, lb = _gqa_step_bytes(B, Hq, Hkv, D, L, C, 2 * D * 2, 2)
+    res["bf16"] = dict(ms_per_step=ms, gbs=sb / (ms * 1e-3) / 1e9, frac_of_hbm_peak=sb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                       algorithmic_bytes=sb, launch_ms=lms, launch_gbs=lb / (lms * 1e-3) / 1e9, launch_bytes=lb)
+    # FP8: one scale per token over its key and value rows (amax / 448)
+    amax = torch.maximum(k.abs().amax(dim=(2, 3)), v.abs().amax(dim=(2, 3))).float()
+    sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).contiguous()
+    kc = (k.float() / sc[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    vc = (v.float() / sc[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    del k, v
+    torch.cuda.empty_cache()
+    ms, lms = _gqa_run(cpa, torch, q, kc, vc, sc, L, C, scale, steps, warmup, warmup_ms)
+    sb, lb = _gqa_step_bytes(B, Hq, Hkv, D, L, C, 2 * D + 4 / Hkv, 2)
+    res["fp8"] = dict(ms_per_step=ms, gbs=sb / (ms * 1e-3) / 1e9, frac_of_hbm_peak=sb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      algorithmic_bytes=sb, launch_ms=lms, launch_gbs=lb / (lms * 1e-3) / 1e9, launch_bytes=lb)
+    del kc, vc, sc
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode_config1(cpa, torch, synth, steps, warmup, warmup_ms):
+    """Split-KV decode + LSE merge, fp32: batch 1, 8 query heads on 1 kv head,
+    head dim 128, 4096-token context as C=4 contiguous 1024-token shards (4
+    partial launches + merge per step), with the last-level cache flushed
+    (a 512 MiB write) before every timed step, and cache-hot."""
+    c = synth.config(1)
+    B, Hq, Hkv, D, L, C = c["B"], c["Hq"], c["Hkv"], c["Dqk"], c["L"], c["C"]
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(synth.f32_normal(1, 1, (B, Hq, D))).to(dev)
+    k = torch.from_numpy(synth.f32_normal(1, 2, (B, L, Hkv, D), chunk=1)).to(dev)
+    v = torch.from_numpy(synth.f32_normal(1, 3, (B, L, Hkv, D), chunk=1)).to(dev)
+    scratch = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+    sb, lb = _gqa_step_bytes(B, Hq, Hkv, D, L, C, 2 * D * 4, 4)
+    out = {"workload": c["name"]}
+    for name, flush in (("cache_flushed", lambda i: scratch.fill_(float(i))), ("cache_hot", None)):
+        ms, lms = _gqa_run(cpa, torch, q, k, v, None, L, C, c["scale"], steps, warmup, warmup_ms, flush=flush)
+        out[name] = dict(ms_per_step=ms, gbs=sb / (ms * 1e-3) / 1e9, frac_of_hbm_peak=sb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         launch_ms=lms, launch_gbs=lb / (lms * 1e-3) / 1e9)
+    out["algorithmic_bytes"] = sb
+    out["launch_bytes"] = lb
+    out["note"] = ("4.2 MB per step: the step is bound by launch and merge latency (5 dependent kernels), "
+                   "not by HBM bandwidth")
+    del scratch
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(synth, prefill, seconds):
     """The float64 oracle on rows of the same zigzag workload until ~`seconds`
     of CPU work, as TFLOP/s of algorithmic work done."""
@@ -523,6 +656,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--decode-only", action="store_true", help="time only the MLA decode (profiling)")
+    ap.add_argument("--gqa-only", action="store_true", help="time only the GQA decode figures (profiling)")
     ap.add_argument("--no-extra-prefill", action="store_true",
                     help="skip the MLA zigzag (prefix) and ragged interleave prefill figures")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -556,6 +690,11 @@ def main():
     if args.decode_only:
         dec = bench_decode(cpa, torch, synth, args.steps, args.warmup, args.warmup_ms)
         print(json.dumps({"decode": dec}), flush=True)
+        return
+    if args.gqa_only:
+        g = bench_gqa_decode(cpa, torch, args.steps, args.warmup, args.warmup_ms)
+        c1 = bench_decode_config1(cpa, torch, synth, args.steps, args.warmup, args.warmup_ms)
+        print(json.dumps({"decode_gqa": g, "decode_config1": c1}), flush=True)
         return
 
     log("[bench] zigzag prefill shard ...")

@@ -298,8 +298,10 @@ def attn_decode_workspace_size(batch, n_heads_q, head_dim_v, max_shard_len):
 def attn_decode_shard(q, kcache, vcache, kv_begin, kv_end, max_shard_len, softmax_scale, kv_scale=None,
                       o_part=None, lse_part=None, workspace=None, stream=None, kcache_dtype=None):
     """Split-KV decode of one shard. q [B, Hq, Dqk]; kcache [B, Lmax, Hkv, Dqk]
-    (torch.uint8 = FP8 E4M3 bytes, then kv_scale [B, Lmax] f32); vcache or None
-    (MLA); kv_begin / kv_end int32 device tensors [B]. Returns (o_part, lse_part)."""
+    (torch.uint8 = FP8 E4M3 bytes, then kv_scale [B, Lmax] f32, one scale per
+    token for its key and value); vcache [B, Lmax, Hkv, Dv] of the same dtype,
+    or None (MLA); kv_begin / kv_end int32 device tensors [B]. Returns
+    (o_part, lse_part)."""
     torch = _torch()
     B, Hq = q.shape[0], q.shape[1]
     Dv = vcache.shape[-1] if vcache is not None else 512

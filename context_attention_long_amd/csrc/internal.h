@@ -31,8 +31,10 @@ struct MergeArgs {
 
 struct DecodeGqaArgs {
   const void* q;        // [B, Hq, D] f32 or bf16
-  const void* k;        // [B, Lmax, Hkv, D]
-  const void* v;        // [B, Lmax, Hkv, D]
+  const void* k;        // [B, Lmax, Hkv, D] f32, bf16 or E4M3 bytes
+  const void* v;        // [B, Lmax, Hkv, D] same dtype as k
+  const float* kv_scale;  // [B, Lmax] per-token scale of an FP8 cache (key and value), else null
+  int64_t s_b, s_t;
   const int32_t* kv_begin;
   const int32_t* kv_end;
   float* o;             // [nsplit, B, Hq, D] (or o_part when nsplit == 1)
@@ -157,6 +159,8 @@ int noalloc_scratch(void** ptr);
 // ---- launchers (return hipSuccess or the launch error) ----
 int launch_merge(const MergeArgs& a, void* stream);
 int launch_decode_gqa(const DecodeGqaArgs& a, void* stream);
+// Query-head blocks (workgroups per kv head and split) of a GQA group of G heads.
+int gqa_head_blocks(int G);
 int launch_decode_mla(const DecodeMlaArgs& a, void* stream);
 int launch_prefill_gqa(const PrefillGqaArgs& a, const cpa_segment* seg, int n_seg, void* stream);
 int launch_prefill_mla(const PrefillMlaArgs& a, const cpa_segment* seg, int n_seg, void* stream);

@@ -33,9 +33,13 @@
 #include <type_traits>
 
 #include "lds_dma.h"
+#include "wave_ops.h"
 
 namespace cpa {
 namespace mla {
+
+using cpa::max4_rows;
+using cpa::sum4_rows;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -109,26 +113,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
   return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
                                                  pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])));
-}
-
-// Maximum / sum over the four lanes l, l^16, l^32, l^48 (one head's four
-// score groups), with the gfx950 row-swap permutes instead of LDS round trips.
-// (compare-select rather than fmaxf: the swapped values are not known to be
-// canonical floats, and fmaxf would canonicalise both operands first)
-__device__ __forceinline__ float max4_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float a0 = __uint_as_float(a[0]), a1 = __uint_as_float(a[1]);
-  const float y = a0 > a1 ? a0 : a1;
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  const float b0 = __uint_as_float(b[0]), b1 = __uint_as_float(b[1]);
-  return b0 > b1 ? b0 : b1;
-}
-
-__device__ __forceinline__ float sum4_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Per-lane LDS byte offsets inside a tile. Every operand read of a tile is

@@ -178,7 +178,9 @@ size_t attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t head
  *   vcache   [B, Lmax, Hkv, Dv]    same dtype as kcache, or NULL for MLA
  *                                  (value = first Dv dims of the latent)
  *   kv_scale [B, Lmax] f32         per-token scale, required for FP8 and
- *                                  otherwise NULL: entry = e4m3 * scale
+ *                                  otherwise NULL: every entry of token t
+ *                                  (its key and, for GQA, its value) is
+ *                                  e4m3 * scale[b, t]
  *   kv_begin, kv_end [B] int32     DEVICE arrays; clamped to [0, Lmax] and
  *                                  an empty range gives O = 0, LSE = -inf
  *   max_shard_len                  upper bound of kv_end - kv_begin, used to
@@ -188,7 +190,9 @@ size_t attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t head
  *   workspace / ws_bytes           device scratch of at least
  *                                  attn_decode_workspace_size(...) bytes
  * Supported: MLA (Hkv = 1, Dqk = 576, Dv = 512, q bf16, cache bf16 or FP8)
- * and GQA (Dqk = Dv <= 256, any dtype listed).
+ * and GQA (Dqk = Dv in {64, 128, 256}, any Hq / Hkv group, cache f32, bf16
+ * or FP8; K/V data pointers and strides in bytes multiples of 16). Other
+ * shapes return CPA_E_UNSUPPORTED, misaligned K/V CPA_E_INVAL.
  */
 cpa_status attn_decode_shard(const cpa_tensor* q, const cpa_tensor* kcache, const cpa_tensor* vcache,
                              const cpa_tensor* kv_scale, const int32_t* kv_begin,

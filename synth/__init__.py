@@ -67,6 +67,19 @@ def f32_to_e4m3(x):
     return codes, scale
 
 
+def gqa_kv_to_e4m3(k, v):
+    """FP8 form of a GQA cache with one scale per token: the scale covers the
+    token's key and value rows over all kv heads (amax / 448), the codes are
+    E4M3 bytes. k, v [B, L, Hkv, D] float32 -> (k codes, v codes uint8
+    [B, L, Hkv, D], scale float32 [B, L])."""
+    k = np.asarray(k, np.float32)
+    v = np.asarray(v, np.float32)
+    B, L, Hkv, D = k.shape
+    n = Hkv * D
+    codes, scale = f32_to_e4m3(np.concatenate([k.reshape(B, L, n), v.reshape(B, L, n)], axis=-1))
+    return codes[..., :n].reshape(B, L, Hkv, D), codes[..., n:].reshape(B, L, Hkv, D), scale
+
+
 def _slabs(n, chunk):
     return [(i, i * chunk, min(n, (i + 1) * chunk)) for i in range(-(-n // chunk))]
 

@@ -74,20 +74,26 @@ def _decode_case(cpa, B, Hq, Hkv, D, L, shards, qdt, kvdt, seed, ragged=False):
         qd, qv = H.bf16_tensor(qb), formats.bf16_bits_to_f64(qb)
     kx = rng.standard_normal((B, L, Hkv, D)).astype(np.float32)
     vx = rng.standard_normal((B, L, Hkv, D)).astype(np.float32)
+    sd, sc = None, None  # FP8: per-token scale (device, host)
     if kvdt == "f32":
         kd, vd, kv64, vv64 = H.f32_tensor(kx), H.f32_tensor(vx), kx.astype(np.float64), vx.astype(np.float64)
+    elif kvdt == "fp8":
+        kc, vc, sc = synth.gqa_kv_to_e4m3(kx, vx)
+        kd, vd, sd = H.u8_tensor(kc), H.u8_tensor(vc), H.f32_tensor(sc)
+        kv64, vv64 = kc, vc  # the oracle decodes the codes itself
     else:
         kb, vb = synth.f32_to_bf16_bits(kx), synth.f32_to_bf16_bits(vx)
         kd, vd, kv64, vv64 = H.bf16_tensor(kb), H.bf16_tensor(vb), formats.bf16_bits_to_f64(kb), formats.bf16_bits_to_f64(vb)
+    odec = dict(decode=formats.e4m3_to_f64, kv_scale=sc) if kvdt == "fp8" else {}
     parts_o, parts_l = [], []
     for (s0, s1) in shards:
         beg = np.full(B, s0, np.int32)
         end = np.full(B, s1, np.int32)
         if ragged:  # per-request ranges inside the shard, one empty
             end = np.minimum(end, s0 + (np.arange(B) * 37) % max(1, s1 - s0 + 1)).astype(np.int32)
-        o, l = cpa.attn_decode_shard(qd, kd, vd, H.i32_tensor(beg), H.i32_tensor(end), s1 - s0, scale)
+        o, l = cpa.attn_decode_shard(qd, kd, vd, H.i32_tensor(beg), H.i32_tensor(end), s1 - s0, scale, kv_scale=sd)
         _sync()
-        ro, rl = att.decode_shard(qv, kv64, beg, end, scale, vcache=vv64)
+        ro, rl = att.decode_shard(qv, kv64, beg, end, scale, vcache=vv64, **odec)
         chk = H.check_f32 if (qdt == "f32" and kvdt == "f32") else H.check_lowp
         chk(H.host(o), H.host(l), ro, rl, f"shard {s0}:{s1}")
         parts_o.append(o)
@@ -95,7 +101,7 @@ def _decode_case(cpa, B, Hq, Hkv, D, L, shards, qdt, kvdt, seed, ragged=False):
     if not ragged:
         mo, ml = cpa.attn_merge_states(torch.stack(parts_o), torch.stack(parts_l))
         _sync()
-        fo, fl = att.decode_shard(qv, kv64, [0] * B, [L] * B, scale, vcache=vv64)
+        fo, fl = att.decode_shard(qv, kv64, [0] * B, [L] * B, scale, vcache=vv64, **odec)
         chk = H.check_f32 if (qdt == "f32" and kvdt == "f32") else H.check_lowp
         chk(H.host(mo), H.host(ml), fo, fl, "merged vs unsharded")
 
@@ -133,6 +139,38 @@ def test_decode_gqa_f32_shapes(cpa, B, Hq, Hkv, D, L, nsh):
 def test_decode_gqa_bf16_and_ragged(cpa):
     _decode_case(cpa, 3, 16, 4, 128, 700, plans.contiguous_shards(700, 3), "bf16", "bf16", 17)
     _decode_case(cpa, 5, 8, 1, 128, 500, [(100, 400)], "bf16", "bf16", 18, ragged=True)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,L,nsh,qdt", [(3, 16, 4, 128, 700, 3, "bf16"), (2, 8, 2, 64, 300, 2, "f32"),
+                                                  (1, 4, 4, 256, 77, 2, "bf16")])
+def test_decode_gqa_fp8(cpa, B, Hq, Hkv, D, L, nsh, qdt):
+    """GQA over an FP8 E4M3 cache with one scale per token for its key and
+    value (bf16 and f32 queries, head dims 64 / 128 / 256), every shard and
+    the merge against the oracle, and ragged per-request ranges."""
+    _decode_case(cpa, B, Hq, Hkv, D, L, plans.contiguous_shards(L, nsh), qdt, "fp8", 31 + D)
+    _decode_case(cpa, 5, 8, 2, D, 500, [(100, 400)], qdt, "fp8", 32 + D, ragged=True)
+
+
+@pytest.mark.parametrize("kvdt", ["bf16", "fp8", "f32"])
+def test_decode_gqa_group_over_16_heads(cpa, kvdt):
+    """A GQA group wider than the 16 heads of one workgroup (40 query heads on
+    2 kv heads: 20 per group, two head blocks, the second with 4 heads)."""
+    qdt = "f32" if kvdt == "f32" else "bf16"
+    _decode_case(cpa, 2, 40, 2, 128, 400, plans.contiguous_shards(400, 2), qdt, kvdt, 55)
+
+
+def test_decode_gqa_rejects_misaligned_rows(cpa):
+    """K/V rows are streamed in 16-byte pieces: a cache view whose token
+    stride is not a multiple of 16 bytes is rejected before any launch."""
+    import torch
+    q = torch.zeros((1, 8, 64), dtype=torch.bfloat16, device="cuda")
+    base = torch.zeros((1, 40, 1, 68), dtype=torch.bfloat16, device="cuda")
+    k = base[..., :64]  # token stride 68 elements = 136 bytes
+    be = H.i32_tensor([0])
+    en = H.i32_tensor([40])
+    with pytest.raises(cpa.CpaError) as ex:
+        cpa.attn_decode_shard(q, k, k, be, en, 40, 0.125)
+    assert ex.value.status == cpa.CPA_E_INVAL
 
 
 def _mla_inputs(B, L, fp8, seed, std=0.5):
