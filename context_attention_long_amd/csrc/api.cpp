@@ -113,15 +113,13 @@ int mla_nsplit(int64_t B, int64_t max_len) {
   return (int)ns;
 }
 
-// GQA: units = rows x kv heads x query-head blocks. One 4-wavefront
-// workgroup per CU for tiles of 8 KB or more (whole-machine streaming
-// measured 6.0 TB/s against 5.7 with two), two for smaller tiles (FP8 at
-// d = 128: 5.1 against 3.6 TB/s with one); at least two 16-token tiles per
-// wavefront.
-int gqa_nsplit(int64_t units, int64_t max_len, int64_t tile_bytes = 0) {
+// GQA: units = rows x kv heads x query-head blocks; one 4-wavefront
+// workgroup per CU (with 8 requests x 8 kv heads x 16384 tokens, bf16
+// streamed at 6.0 TB/s with one per CU against 5.4 with two, FP8 at 4.9
+// against 4.1), and at least 128 tokens per split.
+int gqa_nsplit(int64_t units, int64_t max_len) {
   if (units <= 0) return 1;
-  const int64_t per_cu = tile_bytes >= 8192 ? 1 : 2;
-  int64_t ns = (per_cu * (int64_t)num_cus() + units - 1) / units;
+  int64_t ns = ((int64_t)num_cus() + units - 1) / units;
   const int64_t by_len = (max_len + 127) / 128;
   if (ns > by_len) ns = by_len;
   if (ns < 1) ns = 1;
@@ -208,8 +206,7 @@ cpa_status decode_plan(int64_t rows, int64_t Hq, const cpa_tensor* kcache, const
     p->nsplit = mla_nsplit(rows, max_len);
   } else {
     p->head_blocks = cpa::gqa_head_blocks((int)(Hq / Hkv));
-    const int64_t esz = kcache->dtype == CPA_FP8_E4M3 ? 1 : (kcache->dtype == CPA_BF16 ? 2 : 4);
-    p->nsplit = gqa_nsplit(rows * Hkv * p->head_blocks, max_len, 16 * 2 * kcache->shape[3] * esz);
+    p->nsplit = gqa_nsplit(rows * Hkv * p->head_blocks, max_len);
   }
   return CPA_OK;
 }

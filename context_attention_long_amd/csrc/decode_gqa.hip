@@ -13,12 +13,14 @@
 // row, kv head, block of up to 16 query heads, split); the split is an even
 // share of the row's [begin, end) range. Decode is HBM-bound (a few FLOP
 // per cache byte), so the design is about streaming:
-//  * Every wavefront runs its own pipeline over the split's 16-token tiles
-//    w, w + 4, w + 8, ...: direct global -> LDS loads (16 bytes per lane)
-//    into stages that only it reads, waited with its own vmcnt, so the main
-//    loop has no barrier. Two workgroups fit a CU for the bf16 / FP8 head
-//    dims up to 128 (64-66 KB of stages), i.e. eight independent
-//    streams per CU with one to three tiles in flight each.
+//  * Every wavefront runs its own pipeline over the split's tiles w, w + 4,
+//    w + 8, ... (32 tokens for bf16 / FP8 rows up to 256 bytes, else 16):
+//    direct global -> LDS loads (16 bytes per lane) into two stages that
+//    only it reads, waited with its own vmcnt, so the main loop has no
+//    barrier. The host sizes the split for one workgroup per CU: more
+//    concurrent streams (two workgroups per CU, eight wavefronts per
+//    workgroup, deeper stages) all measured slower on the whole-machine
+//    stream.
 //  * Both contractions run on MFMA with the 16 query heads as the N
 //    dimension (heads past the group are zero columns): S^T = K Q^T with
 //    16x16x32 bf16 (an f32 query against a bf16 / FP8 cache as bf16 hi + lo
@@ -61,9 +63,7 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 enum Dt { kF32 = 0, kBf16 = 1, kFp8 = 2 };
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTok = 16;  // tokens per tile (one MFMA block)
+constexpr int kMaxThreads = 256;
 constexpr int kHB = 16;   // query heads per workgroup (MFMA columns)
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -71,15 +71,25 @@ template <int DT, int D>
 struct Cfg {
   static constexpr int esz = DT == kF32 ? 4 : (DT == kBf16 ? 2 : 1);
   static constexpr int row = D * esz;             // bytes of one token's K (or V) row
-  static constexpr int kv_bytes = kTok * row;     // K (or V) part of a tile
+  // tokens per tile: two 16-token MFMA blocks for rows up to 256 bytes (bf16
+  // and FP8 caches), one for longer rows and f32 -- a tile carries 8 KB or
+  // more of K + V, so the per-tile work (waits, softmax reductions) is
+  // spread over enough bytes
+  static constexpr int tok = (DT != kF32 && row <= 256) ? 32 : 16;
+  static constexpr int nb = tok / 16;             // MFMA row blocks per tile
+  static constexpr int kv_bytes = tok * row;      // K (or V) part of a tile
   static constexpr int loads = kv_bytes / 1024;   // wave-wide 16-byte loads per part
-  static constexpr int scale_bytes = DT == kFp8 ? 64 : 0;
+  static constexpr int scale_bytes = DT == kFp8 ? 4 * tok : 0;
   static constexpr int tile = 2 * kv_bytes + scale_bytes;
-  static constexpr int stages = tile <= 4096 + 64 ? 4 : (tile <= 16384 + 64 ? 2 : 1);
+  static constexpr int stages = tile <= 4096 + 128 ? 4 : (tile <= 16384 + 128 ? 2 : 1);
+  // wavefronts per workgroup, each with its own pipeline (eight, where they
+  // fit, streamed the FP8 d = 128 cache at 4.5 TB/s against 4.9 with four)
+  static constexpr int waves = 4;
+  static constexpr int threads = 64 * waves;
   static constexpr int vm = 2 * loads + (DT == kFp8 ? 1 : 0);  // vector-memory ops per tile
   static constexpr int nacc = D / 16;             // O^T accumulators (16 dims x 16 heads each)
-  static constexpr int stage_lds = kWaves * stages * tile;
-  static constexpr int merge_lds = kWaves * kHB * (D + 2) * 4;
+  static constexpr int stage_lds = waves * stages * tile;
+  static constexpr int merge_lds = waves * kHB * (D + 2) * 4;
   static constexpr int lds = stage_lds > merge_lds ? stage_lds : merge_lds;
   static_assert(loads >= 1 && kv_bytes % 1024 == 0, "whole wave-wide loads per tile part");
   static_assert((stages - 1) * vm <= 63, "vmcnt range");
@@ -153,7 +163,7 @@ __device__ __forceinline__ int tile_off(int t, int u) {
 }
 
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void decode_gqa_kernel(cpa::DecodeGqaArgs a) {
+__global__ __launch_bounds__(kMaxThreads) void decode_gqa_kernel(cpa::DecodeGqaArgs a) {
   using C = Cfg<DT, D>;
   __shared__ __attribute__((aligned(16))) char smem[C::lds];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -183,8 +193,10 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(cpa::DecodeGqaArgs
   const int64_t len = end - beg;
   const int64_t t0 = beg + len * split / a.nsplit;
   const int64_t t1 = beg + len * (split + 1) / a.nsplit;
+  constexpr int kTok = C::tok;
   const int nt_all = (int)((t1 - t0 + kTok - 1) / kTok);
-  const int nt = nt_all > w ? (nt_all - w + kWaves - 1) / kWaves : 0;  // tiles w, w + 4, ...
+  constexpr int kWaves = C::waves;
+  const int nt = nt_all > w ? (nt_all - w + kWaves - 1) / kWaves : 0;  // tiles w, w + waves, ...
 
   // ---- this wavefront's loads ----
   const uint64_t kb = cpa::uniform_ptr(reinterpret_cast<const char*>(a.k) +
@@ -194,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(cpa::DecodeGqaArgs
   const uint32_t kt = (uint32_t)(a.k_t * C::esz), vt = (uint32_t)(a.v_t * C::esz);  // token strides (bytes)
   char* wlds = smem + w * C::stages * C::tile;
   // cache policy: the Q rows of a request share tiles through L2; FP8 tiles
-  // also stream faster without the nontemporal hint (5.1 against 4.8 TB/s
-  // at 8 requests x 8 kv heads x 16384 tokens), bf16 faster with it (5.8
+  // also stream faster without the nontemporal hint (4.9 against 4.6 TB/s
+  // at 8 requests x 8 kv heads x 16384 tokens), bf16 faster with it (5.7
   // against 5.0)
   const bool reuse = a.Q > 1 || DT == kFp8;
   auto dma = [&](uint64_t base, uint32_t off, uint32_t dst) {
@@ -296,106 +308,127 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(cpa::DecodeGqaArgs
     const int64_t tok0 = t0 + (int64_t)(w + kWaves * j) * kTok;
     const int lim = (int)min((int64_t)(kTok - 1), t1 - 1 - tok0);
 
-    // S^T (16 tokens x 16 heads): lane (head c, group g) gets tokens 4g .. 4g+3
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (DT == kF32) {
+    // S^T per 16-token block bk (16 tokens x 16 heads): lane (head c, group
+    // g) gets tokens 16 bk + 4g .. + 3
+    f32x4 s[C::nb];
 #pragma unroll
-      for (int m = 0; m < D / 16; ++m) {
-        const f32x4 kv = lds_ld<f32x4>(T + tile_off<C::row>(c, 4 * m + g));  // dims 16m + 4g .. + 3 of token c
+    for (int bk = 0; bk < C::nb; ++bk) {
+      const char* Tb = T + 16 * bk * C::row;
+      s[bk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (DT == kF32) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) s = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[x], qf[m][x], s, 0, 0, 0);
-      }
-    } else if constexpr (DT == kBf16) {
+        for (int m = 0; m < D / 16; ++m) {
+          const f32x4 kv = lds_ld<f32x4>(Tb + tile_off<C::row>(c, 4 * m + g));  // dims 16m + 4g .. + 3 of token c
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        const bf16x8 kv = lds_ld<bf16x8>(T + tile_off<C::row>(c, 4 * ks + g));  // dims 32ks + 8g .. + 7
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[ks], s, 0, 0, 0);
-        if (!qbf) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[ks], s, 0, 0, 0);
-      }
-    } else {
+          for (int x = 0; x < 4; ++x) s[bk] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[x], qf[m][x], s[bk], 0, 0, 0);
+        }
+      } else if constexpr (DT == kBf16) {
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        const u32x2 raw = lds_ld<u32x2>(T + tile_off<C::row>(c, 2 * ks + (g >> 1)) + 8 * (g & 1));
-        const u32x2 lo = fp8x4_to_bf16(raw[0]), hi = fp8x4_to_bf16(raw[1]);
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], hi[0], hi[1]));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[ks], s, 0, 0, 0);
-        if (!qbf) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[ks], s, 0, 0, 0);
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const bf16x8 kv = lds_ld<bf16x8>(Tb + tile_off<C::row>(c, 4 * ks + g));  // dims 32ks + 8g .. + 7
+          s[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[ks], s[bk], 0, 0, 0);
+          if (!qbf) s[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[ks], s[bk], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const u32x2 raw = lds_ld<u32x2>(Tb + tile_off<C::row>(c, 2 * ks + (g >> 1)) + 8 * (g & 1));
+          const u32x2 lo = fp8x4_to_bf16(raw[0]), hi = fp8x4_to_bf16(raw[1]);
+          const bf16x8 kv = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], hi[0], hi[1]));
+          s[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[ks], s[bk], 0, 0, 0);
+          if (!qbf) s[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qlo[ks], s[bk], 0, 0, 0);
+        }
       }
     }
 
     // online softmax (log2 domain) of head c over the tile
-    f32x4 ts = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (DT == kFp8) ts = lds_ld<f32x4>(T + 2 * C::kv_bytes + 16 * g);
-    float x[4];
+    f32x4 ts[C::nb];
+    float x[C::nb][4];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = s[i] * ts[i] * sl2;
-      if (lim < kTok - 1 && 4 * g + i > lim) x[i] = -INFINITY;
+    for (int bk = 0; bk < C::nb; ++bk) {
+      ts[bk] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (DT == kFp8) ts[bk] = lds_ld<f32x4>(T + 2 * C::kv_bytes + 64 * bk + 16 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[bk][i] = s[bk][i] * ts[bk][i] * sl2;
+        if (lim < kTok - 1 && 16 * bk + 4 * g + i > lim) x[bk][i] = -INFINITY;
+        mx = fmaxf(mx, x[bk][i]);
+      }
     }
-    const float mt = max4_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    const float mt = max4_rows(mx);
     // the reference max moves only when a score passes it by 2^8 (p <= 256
     // meanwhile; O and the sum share the reference), so rescaling is rare
     const float m_new = mt > m_run + 8.f ? mt : m_run;  // finite: every tile holds a valid token
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
-    float p[4];
+    float p[C::nb][4], psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
-    l_part = l_part * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    for (int bk = 0; bk < C::nb; ++bk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[bk][i] = __builtin_amdgcn_exp2f(x[bk][i] - m_new);
+        psum += p[bk][i];
+      }
+    l_part = l_part * alpha + psum;
     m_run = m_new;
     if (__any(alpha != 1.f)) {
 #pragma unroll
       for (int n = 0; n < C::nacc; ++n) acc[n] *= alpha;
     }
 
-    // O^T += V^T P^T
-    if constexpr (DT == kF32) {
-      // token-major V: k-step e takes token 4g + e of every group; lane (c, g)
-      // reads dims 64N + 4c .. + 3, feeding MFMA (N, x) at row c (dim 64N + 4c + x)
+    // O^T += V^T P^T, block by block
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+    for (int bk = 0; bk < C::nb; ++bk) {
+      const char* Vb = V + 16 * bk * C::row;
+      if constexpr (DT == kF32) {
+        // k-step e takes token 4g + e of every group; lane (c, g) reads dims
+        // 64N + 4c .. + 3, feeding MFMA (N, x) at row c (dim 64N + 4c + x)
 #pragma unroll
-        for (int N = 0; N < D / 64; ++N) {
-          const f32x4 vv = lds_ld<f32x4>(V + tile_off<C::row>(4 * g + e, 16 * N + c));
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int xx = 0; xx < 4; ++xx)
-            acc[4 * N + xx] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[xx], p[e], acc[4 * N + xx], 0, 0, 0);
-        }
-    } else {
-      float pw[4];
+          for (int N = 0; N < D / 64; ++N) {
+            const f32x4 vv = lds_ld<f32x4>(Vb + tile_off<C::row>(4 * g + e, 16 * N + c));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pw[i] = p[i] * ts[i];
-      const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3])});
-      if constexpr (DT == kBf16) {
-        // lane 4j + i of group g addresses token 4g + j, dims 16n + 4i .. + 3
-        const int tk = 4 * g + (c >> 2);
-#pragma unroll
-        for (int n = 0; n < C::nacc; ++n) {
-          const i16x4 va = lds_read_tr16(V + tile_off<C::row>(tk, 2 * n + ((c & 3) >> 1)) + 8 * (c & 1));
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[n], 0, 0, 0);
-        }
+            for (int xx = 0; xx < 4; ++xx)
+              acc[4 * N + xx] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[xx], p[bk][e], acc[4 * N + xx], 0, 0, 0);
+          }
       } else {
-        // lanes 2j, 2j + 1 of group g address row j: token 4g + (j & 3),
-        // dims of unit n + (j >> 2); one read feeds n-blocks n and n + 1
-        const int jr = c >> 1, tk = 4 * g + (jr & 3);
+        float pw[4];
 #pragma unroll
-        for (int n = 0; n < C::nacc; n += 2) {
-          const i32x2 raw = lds_read_tr8(V + tile_off<C::row>(tk, n + (jr >> 2)) + 8 * (c & 1));
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, fp8x4_to_bf16(raw[0])), pb,
-                                                              acc[n], 0, 0, 0);
-          acc[n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, fp8x4_to_bf16(raw[1])),
-                                                                  pb, acc[n + 1], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) pw[i] = p[bk][i] * ts[bk][i];
+        const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3])});
+        if constexpr (DT == kBf16) {
+          // lane 4j + i of group g addresses token 4g + j, dims 16n + 4i .. + 3
+          const int tk = 4 * g + (c >> 2);
+#pragma unroll
+          for (int n = 0; n < C::nacc; ++n) {
+            const i16x4 va = lds_read_tr16(Vb + tile_off<C::row>(tk, 2 * n + ((c & 3) >> 1)) + 8 * (c & 1));
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[n], 0, 0, 0);
+          }
+        } else {
+          // lanes 2j, 2j + 1 of group g address row j: token 4g + (j & 3),
+          // dims of unit n + (j >> 2); one read feeds n-blocks n and n + 1
+          const int jr = c >> 1, tk = 4 * g + (jr & 3);
+#pragma unroll
+          for (int n = 0; n < C::nacc; n += 2) {
+            const i32x2 raw = lds_read_tr8(Vb + tile_off<C::row>(tk, n + (jr >> 2)) + 8 * (c & 1));
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, fp8x4_to_bf16(raw[0])), pb,
+                                                                acc[n], 0, 0, 0);
+            acc[n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(i16x4, fp8x4_to_bf16(raw[1])), pb, acc[n + 1], 0, 0, 0);
+          }
         }
       }
     }
     if (j + C::stages < nt) issue(j + C::stages);
   }
 
-  // ---- merge the four wavefronts' states and write the split's result ----
+  // ---- merge the wavefronts' states and write the split's result ----
   const float l_run = sum4_rows(l_part);
   __syncthreads();  // every wavefront is done with its stages
-  float* mo = reinterpret_cast<float*>(smem);       // [4][16][D] unnormalised O
-  float* mm = mo + kWaves * kHB * D;                // [4][16] running max
-  float* ml = mm + kWaves * kHB;                    // [4][16] running sum
+  float* mo = reinterpret_cast<float*>(smem);       // [waves][16][D] unnormalised O
+  float* mm = mo + kWaves * kHB * D;                // [waves][16] running max
+  float* ml = mm + kWaves * kHB;                    // [waves][16] running sum
 #pragma unroll
   for (int n = 0; n < C::nacc; ++n)
 #pragma unroll
@@ -410,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(cpa::DecodeGqaArgs
   }
   __syncthreads();
   float* o = a.o + (int64_t)split * a.o_s + (int64_t)row * a.o_b;
-  for (int e = tid; e < nh * D; e += kThreads) {
+  for (int e = tid; e < nh * D; e += C::threads) {
     const int h = e / D, d = e % D;
     float M = -INFINITY;
 #pragma unroll
@@ -435,9 +468,9 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(cpa::DecodeGqaArgs
 template <int DT>
 int launch_dt(const cpa::DecodeGqaArgs& a, dim3 grid, hipStream_t st) {
   switch (a.D) {
-    case 64: hipLaunchKernelGGL((decode_gqa_kernel<DT, 64>), grid, dim3(kThreads), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((decode_gqa_kernel<DT, 128>), grid, dim3(kThreads), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((decode_gqa_kernel<DT, 256>), grid, dim3(kThreads), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((decode_gqa_kernel<DT, 64>), grid, dim3(Cfg<DT, 64>::threads), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((decode_gqa_kernel<DT, 128>), grid, dim3(Cfg<DT, 128>::threads), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((decode_gqa_kernel<DT, 256>), grid, dim3(Cfg<DT, 256>::threads), 0, st, a); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
