@@ -32,13 +32,11 @@ using namespace cpa::mla;
 template <bool kFp8, cpa::Policy kP>
 __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::DecodeMlaArgs a) {
   constexpr int kTileLds = kFp8 ? f8::kStages * f8::kTileBytes : kSmemBytes;
-  constexpr int kScaleLds = kFp8 ? f8::kScaleSlots * f8::kScaleSlot : 16;
-  constexpr int kPLds = kFp8 ? f8::kWBytes : 2 * kH * kPRowBytes;
+  constexpr int kScaleLds = kFp8 ? f8::kStages * f8::kScaleSlot : 16;
   __shared__ __attribute__((aligned(16))) char smem[kTileLds];
   __shared__ __attribute__((aligned(16))) char ssc[kScaleLds];
-  __shared__ __attribute__((aligned(16))) char plds[kPLds];
+  __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
   __shared__ float alpha_s[2 * kH], lsum_s[kH];
-  __shared__ int wexp_s[kH];
 
   const int u = (int)(blockIdx.x / (8 * a.Q)) * 8 + (int)(blockIdx.x % 8);
   const int k = (int)(blockIdx.x / 8) % a.Q;
@@ -60,16 +58,16 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
     const uint16_t* qhead = a.q + (int64_t)b * a.q_b + (int64_t)k * a.q_q + (int64_t)(16 * w + c) * a.q_h;
     QkStat st{-INFINITY, 0.f};
     if constexpr (kFp8) {
-      const f8::Lds S{smem, ssc, plds, alpha_s, wexp_s, lsum_s};
+      const f8::Lds S{smem, ssc, plds, alpha_s, lsum_s};
       f8::Query Q;
       f8::load_query(qhead, g, Q);
-      f8::ws_qk(T, w, g, c, f8::bases(w, lane), Q, a.scale_log2, st, S);
+      f8::ws_qk(T, w, g, c, f8::bases(w, g, c), Q, a.scale_log2, st, S);
     } else {
       const Lds S{smem, plds, alpha_s, lsum_s};
       bf16x8 qreg[kQSteps];
       load_q(qhead, g, qreg);
-      ws_qk<false>(T, w, g, c, lds_bases(w, g, c), qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); },
-                   [](int, TokScale&) {}, [](int) { return 0xffffffffu; });
+      ws_qk(T, w, g, c, lds_bases(w, g, c), qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); },
+            [](int) { return 0xffffffffu; });
     }
     const float l = sum4_rows(st.l_run);
     if (g == 0) lsum_s[16 * w + c] = l;
@@ -77,43 +75,21 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
     if (g == 0)
       a.lse[(int64_t)split * a.l_s + (int64_t)row * a.l_b + (int64_t)(16 * w + c) * a.l_h] =
           l > 0.f ? (st.m_run + log2f(l)) * kLn2 : -INFINITY;
-  } else if constexpr (kFp8) {
-    // O^T tiles of 32 dims x 32 heads: lane l, register r holds dim
-    // 8 (r / 4) + 4 (l / 32) + r % 4 of m-tile m, head 32 n + l % 32
-    f8::f32x16 oacc[f8::kPvM][2];
-#pragma unroll
-    for (int m = 0; m < f8::kPvM; ++m)
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[m][n][r] = 0.f;
-    const f8::Lds S{smem, ssc, plds, alpha_s, wexp_s, lsum_s};
-    f8::ws_pv<kP>(T, reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t,
-                  a.kv_scale + (int64_t)b * a.s_b, a.s_t, tid - 256, w, f8::bases(w, lane), oacc, S);
-    __syncthreads();
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int head = 32 * n + (lane & 31);
-      const float lh = lsum_s[head];
-      const float inv = lh > 0.f ? 1.f / lh : 0.f;
-      float* op = a.o + (int64_t)split * a.o_s + (int64_t)row * a.o_b + (int64_t)head * a.o_h + 128 * w +
-                  4 * (lane >> 5);
-#pragma unroll
-      for (int m = 0; m < f8::kPvM; ++m)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4*>(op + 32 * m + 8 * q) =
-              f32x4{oacc[m][n][4 * q], oacc[m][n][4 * q + 1], oacc[m][n][4 * q + 2], oacc[m][n][4 * q + 3]} * inv;
-    }
   } else {
     f32x4 oacc[kMv][4];
 #pragma unroll
     for (int m = 0; m < kMv; ++m)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) oacc[m][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const Lds S{smem, plds, alpha_s, lsum_s};
-    ws_pv<kP>(T, reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, tid - 256, w, g, c,
-              lds_bases(w, g, c), oacc, S);
+    if constexpr (kFp8) {
+      const f8::Lds S{smem, ssc, plds, alpha_s, lsum_s};
+      f8::ws_pv<kP>(T, reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t,
+                    a.kv_scale + (int64_t)b * a.s_b, a.s_t, tid - 256, w, g, c, f8::bases(w, g, c), oacc, S);
+    } else {
+      const Lds S{smem, plds, alpha_s, lsum_s};
+      ws_pv<kP>(T, reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, tid - 256, w, g, c,
+                lds_bases(w, g, c), oacc, S);
+    }
     __syncthreads();
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {

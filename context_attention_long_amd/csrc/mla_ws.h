@@ -57,101 +57,25 @@ struct Tiles {
 
 __device__ __forceinline__ const char* ws_tile(const Lds& S, int i) { return S.tiles + (i & 3) * kTileBytes; }
 
-// FP8 tiles: a 32-token tile is 2304 units of 8 cache bytes (unit u: row
-// u / 72, chunk u % 72). The 512 threads share them: QK threads (t < 256)
-// take units 512 j + t (j < 4), PV threads also 512 j + t and one more,
-// 2048 + t - 256, so the raw registers of two tiles in flight stay small in
-// both roles. A unit is streamed into registers two tiles ahead and, two
-// steps later, converted exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8, scale
-// 1) into its swizzled LDS slot. Loads are unconditional (past the last tile
-// they re-read it) so the compiler never falls back to draining every load.
-template <int NU, Policy kPol>
-struct Fp8Units {
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  u32x2 raw[2][NU];
-  const uint8_t* base;
-  int64_t c_t;
-  int t;  // thread index in the workgroup
-  __device__ __forceinline__ int unit(int j) const { return j < 4 ? 512 * j + t : 2048 + t - 256; }
-  __device__ __forceinline__ void load(const Tiles& T, int i, int j, int set) {
-    const int64_t tok0 = T.t0 + (int64_t)T.phys(i) * kBN;
-    const int lim = (int)min((int64_t)(kBN - 1), T.t1 - 1 - tok0);
-    const int u = unit(j);
-    const uint8_t* tb = base + tok0 * c_t;
-    // the host bounds the token stride so that 32 rows fit 32-bit offsets
-    const uint32_t off = (uint32_t)min(u / kRowChunks, lim) * (uint32_t)c_t + (uint32_t)(u % kRowChunks) * 8u;
-    if constexpr (kPol == Policy::kStream)
-      raw[set][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tb + off));
-    else
-      raw[set][j] = *reinterpret_cast<const u32x2*>(tb + off);
-  }
-  __device__ __forceinline__ void convert(int j, int set, char* tile) const {
-    const u32x2 r = raw[set][j];
-    const uint32_t o0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, false));
-    const uint32_t o1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[0], 1.0f, true));
-    const uint32_t o2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, false));
-    const uint32_t o3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r[1], 1.0f, true));
-    const int u = unit(j), row = u / kRowChunks;
-    *reinterpret_cast<uint4*>(tile + row * (kRowChunks * 16) + swz(row, u % kRowChunks) * 16) =
-        make_uint4(o0, o1, o2, o3);
-  }
-  // prologue, kConv = 2 (PV role): tiles 0 and 1 converted into stages 0 and
-  // 1, tile 2 in set 0, tile 3 in set 1. kConv = 1 (QK role, which converts
-  // one tile less ahead): tile 0 converted, tile 1 in set 1, tile 2 in set 0.
-  template <int kConv>
-  __device__ __forceinline__ void prologue(const Tiles& T, const Lds& S) {
-    const int n = T.ntiles;
-#pragma unroll
-    for (int j = 0; j < NU; ++j) load(T, 0, j, 0);
-#pragma unroll
-    for (int j = 0; j < NU; ++j) load(T, min(1, n - 1), j, 1);
-#pragma unroll
-    for (int j = 0; j < NU; ++j) {
-      convert(j, 0, S.tiles);
-      load(T, min(2, n - 1), j, 0);
-    }
-    if constexpr (kConv == 2) {
-#pragma unroll
-      for (int j = 0; j < NU; ++j) {
-        convert(j, 1, S.tiles + kTileBytes);
-        load(T, min(3, n - 1), j, 1);
-      }
-    }
-  }
-};
-
 // QK role. Barriers: 1 (tile 0) + (ntiles - 1) (loop) + 1 (after the loop).
-// tile(i): LDS bf16 tile of step i. kFp8: scales(i, ts) loads the per-token
-// scales of tile i (two steps ahead of their use), folded into the scores
-// and P. kMask: mask(i) gives the selection bits of tile i (index lists).
-// extra(i, parity) runs after the softmax of tile i (the FP8 path converts
-// its share of tile i+2 there).
-template <bool kFp8, bool kMask = false, typename TileFn, typename ScaleFn, typename MaskFn,
-          typename ExtraFn = void (*)(int, std::integral_constant<int, 0>)>
+// tile(i): LDS bf16 tile of step i. kMask: mask(i) gives the selection bits
+// of tile i (index lists).
+template <bool kMask = false, typename TileFn, typename MaskFn>
 __device__ __forceinline__ void ws_qk(const Tiles& T, int w, int g, int c, const LdsBases& L,
                                       const bf16x8 (&qreg)[kQSteps], float scale_log2, QkStat& st, const Lds& S,
-                                      TileFn&& tile, ScaleFn&& scales, MaskFn&& mask, ExtraFn&& extra = nullptr) {
+                                      TileFn&& tile, MaskFn&& mask) {
   if (T.ntiles <= 0) return;
-  TokScale tsc[2];
-  auto clampt = [&](int i) { return min(i, T.ntiles - 1); };
-  if constexpr (kFp8) {
-    scales(0, tsc[0]);
-    scales(clampt(1), tsc[1]);
-  }
+  const TokScale tsc{};  // unused: bf16 caches carry no scale
   auto step = [&](int i, auto parity) {  // scores and P of tile i; parity = i & 1
     constexpr int P = decltype(parity)::value;
     f32x4 sacc[2];
     qk_tile(tile(i), L, qreg, sacc, [](int) {}, [](int) {});
     Soft sm;
-    soft_scores<kFp8, kMask>(sm, sacc, T.nvalid(i), g, scale_log2, tsc[P], kMask ? mask(i) : 0xffffffffu);
+    soft_scores<false, kMask>(sm, sacc, T.nvalid(i), g, scale_log2, tsc, kMask ? mask(i) : 0xffffffffu);
     soft_ref(sm, st, scale_log2);
-    soft_exp<kFp8, 0, kMask>(sm, st, tsc[P], scale_log2);
-    soft_exp<kFp8, 4, kMask>(sm, st, tsc[P], scale_log2);
+    soft_exp<false, 0, kMask>(sm, st, tsc, scale_log2);
+    soft_exp<false, 4, kMask>(sm, st, tsc, scale_log2);
     soft_store(sm, st, S.p + kH * kPRowBytes * P, S.alpha + kH * P, w, g, c);
-    if constexpr (kFp8) {
-      scales(clampt(i + 2), tsc[P]);  // tile i's scales are spent
-      extra(i, parity);
-    }
   };
   __syncthreads();  // tile 0 ready
   step(0, std::integral_constant<int, 0>{});
@@ -259,83 +183,6 @@ __device__ __forceinline__ void ws_pv(const Tiles& T, const uint16_t* base, int6
         lds_dma16_s<P>(ntb, toff[m + 1], ndst + kThreads * (m + 1) * 16);
       }
     });
-  }
-  __syncthreads();  // P of the last tile visible
-  pv(n - 1, [](int) {});
-}
-
-// PV role over an FP8 E4M3 cache (entry = e4m3 * scale_t; the scale is
-// folded into P by the QK role). During the PV MFMAs of step i each of this
-// thread's units of tile i+2 is converted into stage (i+2) % 3 and its
-// register refilled with tile i+4 (Fp8Units; the QK role does its share in
-// the same step).
-template <Policy kPol>
-__device__ __forceinline__ void ws_pv_fp8(const Tiles& T, const uint8_t* base, int64_t c_t, int tp, int w, int g,
-                                          int c, const LdsBases& L, f32x4 (&oacc)[kMv][4], const Lds& S) {
-  if (T.ntiles <= 0) return;
-  auto stage = [&](int i) -> char* { return S.tiles + (i % 3) * kTileBytes; };
-  Fp8Units<5, kPol> U;
-  U.base = base, U.c_t = c_t, U.t = 256 + tp;
-  const int n = T.ntiles;
-  auto clampt = [&](int i) { return min(i, n - 1); };
-  U.template prologue<2>(T, S);
-  __syncthreads();
-
-  constexpr int kAheadV = 2;  // V operands read ahead (registers are tight next to the FP8 units)
-  auto pv = [&](int i, auto&& hook) {
-    const char* cur = stage(i);
-    const float* acur = S.alpha + kH * (i & 1);
-    const char* pcur = S.p + kH * kPRowBytes * (i & 1);
-    float al[4];
-    bf16x8 pb[4];
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-      al[hb] = acur[16 * hb + c];
-      pb[hb] = *reinterpret_cast<const bf16x8*>(pcur + p_off(16 * hb + c, g));
-    }
-    bf16x8 va[kMv];
-    auto load_v = [&](int m) {
-      va[m] = join_tr(lds_read_tr(cur + L.pv[0][m & 3] + 128 * (m >> 2)),
-                      lds_read_tr(cur + L.pv[1][m & 3] + 128 * (m >> 2)));
-    };
-#pragma unroll
-    for (int m = 0; m < kAheadV; ++m) load_v(m);
-    if (__any(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
-#pragma unroll
-      for (int m = 0; m < kMv; ++m)
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) oacc[m][hb] *= al[hb];
-    }
-#pragma unroll
-    for (int m = 0; m < kMv; ++m) {
-      if (m + kAheadV < kMv) load_v(m + kAheadV);
-      hook(m);
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb)
-        oacc[m][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[m], pb[hb], oacc[m][hb], 0, 0, 0);
-    }
-  };
-  // step i: PV of tile i, conversion of tile i+2 from raw[i & 1], refill with tile i+4
-  auto step = [&](int i, auto parity) {
-    constexpr int P = decltype(parity)::value;
-    __syncthreads();  // P_i visible; every wave is done with tile i-1's stage
-    const int refill_t = clampt(i + 4);
-    char* dst = stage(i + 2);
-    pv(i, [&](int m) {  // one unit per m-step from m-step 1
-      if (m >= 1 && m <= 5) {
-        U.convert(m - 1, P, dst);
-        U.load(T, refill_t, m - 1, P);
-      }
-    });
-  };
-  int i = 0;
-  for (; i + 2 < n; i += 2) {
-    step(i, std::integral_constant<int, 0>{});
-    step(i + 1, std::integral_constant<int, 1>{});
-  }
-  if (i + 1 < n) {
-    step(i, std::integral_constant<int, 0>{});
-    ++i;
   }
   __syncthreads();  // P of the last tile visible
   pv(n - 1, [](int) {});

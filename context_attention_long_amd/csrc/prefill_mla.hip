@@ -70,8 +70,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void prefill_mla_kernel(Args a) {
     bf16x8 qreg[kQSteps];
     load_q(a.q + q_row * a.q_n + (int64_t)(16 * w + c) * a.q_h, g, qreg);
     QkStat st{-INFINITY, 0.f};
-    ws_qk<false>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); },
-                 [](int, TokScale&) {}, [](int) { return 0xffffffffu; });
+    ws_qk(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); },
+          [](int) { return 0xffffffffu; });
     const float l = sum4_rows(st.l_run);
     if (g == 0) S.lsum[16 * w + c] = l;
     __syncthreads();

@@ -56,8 +56,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void sparse_mla_kernel(cpa::SparseMl
       const int v = *reinterpret_cast<const int*>(wring + (i % kIdxSlots) * kIdxSlotBytes + 4 * (lane & 31));
       return (uint32_t)__ballot((uint32_t)v < (uint32_t)a.Lmax);
     };
-    ws_qk<false, true>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); },
-                       [](int, TokScale&) {}, mask);
+    ws_qk<true>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); }, mask);
     const float l = sum4_rows(st.l_run);
     if (g == 0) S.lsum[16 * w + c] = l;
     __syncthreads();
