@@ -12,7 +12,10 @@ Secondary (``decode`` object): split-KV MLA decode, batch 64, 64 heads,
 576/512 latent, 131072-token context cut into C=8 contiguous shards, run as 8
 partial launches on one device plus the exact merge; bf16 cache and FP8 E4M3
 cache with per-token scale, in GB/s of algorithmic bytes (cache bytes read
-once, plus queries, partial outputs/LSEs and the merge).
+once, plus queries, partial outputs/LSEs and the merge). ``decode_gqa``: the
+same step for a GQA cache at a serving shape (batch 8, 32/8 heads, d=128,
+131072 tokens, C=8), bf16 and FP8; ``decode_config1``: the fp32 GQA decode of
+batch 1, 8/1 heads, 4096 tokens, C=4, with the last-level cache flushed.
 
 Also reported: the dominant kernel's roofline (live HIP-event timing on the
 launch stream); the same prefill kernel with the 256 MB last-level cache
@@ -607,42 +610,152 @@ def bench_decode_config1(cpa, torch, synth, steps, warmup, warmup_ms):
     return out
 
 
-def cpu_baseline(synth, prefill, seconds):
-    """The float64 oracle on rows of the same zigzag workload until ~`seconds`
-    of CPU work, as TFLOP/s of algorithmic work done."""
+def _cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _decode_flops(L, Hq, Dqk, Dv):
+    return L * Hq * 2 * (Dqk + Dv)
+
+
+def _oracle_decode_all_shards(att, q, cache, L, C, scale, **kw):
+    """The oracle's C contiguous partial decodes of the range [0, L) and
+    their merge (what one step of the GPU path computes)."""
+    from oracle import plans
+    B = q.shape[0]
+    parts = [att.decode_shard(q, cache, [s0] * B, [s1] * B, scale, **kw) for s0, s1 in plans.contiguous_shards(L, C)]
+    return att.merge_states(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+
+
+def _oracle_rows(att, q, k, v, plan, c, rows_order, seconds, min_rows, decode):
+    """Run the oracle's prefill shard on batches of 4 local rows from
+    rows_order until `seconds` have passed and at least `min_rows` are done."""
+    pos = plan.pos_id.astype(np.int64)
+    done, flops = 0, 0
+    t0 = time.perf_counter()
+    while done < len(rows_order) and (time.perf_counter() - t0 < seconds or done < min_rows):
+        rows = sorted(int(r) for r in rows_order[done:done + 4])
+        att.prefill_shard(q, k, plan.segments, c["scale"], v=v, dv=c["Dv"], rows=rows, decode=decode)
+        flops += int(np.sum(pos[rows] + 1)) * c["Hq"] * 2 * (c["Dqk"] + c["Dv"])
+        done += len(rows)
+    return done, flops, time.perf_counter() - t0
+
+
+def _segment_end_rows(plan):
+    rows = []
+    for (_req, r0, n, _p0, _st, _kv0) in plan.segments:
+        rows += [r0, r0 + n - 1]
+    return list(dict.fromkeys(rows))
+
+
+def cpu_baseline(synth, prefill, seconds, per_config_seconds=5.0, min_rows=0):
+    """The float64 oracle, as it stands, on this host's cores, on bounded
+    samples of every workload: the zigzag GQA prefill shard (the headline
+    comparison, ``value``), and per configuration: the fp32 GQA decode in
+    full, one request of the MLA decode (bf16 and FP8, extrapolated to the
+    batch), and sampled local rows of the MLA zigzag and ragged interleave
+    prefill shards (segment ends first, then random rows; extrapolated to
+    the whole shard from the FLOP rate)."""
     from oracle import attention as att
     from oracle import formats, plans
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cores = _cores()
     try:
         from threadpoolctl import threadpool_limits
         limiter = threadpool_limits(cores)
     except Exception:  # pragma: no cover
         limiter = None
+    per = {}
+
+    # config 2: zigzag GQA prefill shard (headline)
     c = prefill["cfg"]
     ref = plans.plan_zigzag(c["C"], c["rank"], c["new_len"], c["prefix_len"])
     T = sum(c["new_len"])
     qb = synth.bf16_normal(2, 1, (ref.n_local, c["Hq"], c["Dqk"]))
     kb = synth.bf16_normal(2, 2, (T, c["Hkv"], c["Dqk"]))
     vb = synth.bf16_normal(2, 3, (T, c["Hkv"], c["Dv"]))
-    # rows spread over both blocks, cheap and expensive alike, 16 at a time
     order = synth.rng(2, 9).permutation(ref.n_local)
-    done_rows, flops = 0, 0
-    t0 = time.perf_counter()
-    while done_rows < ref.n_local and time.perf_counter() - t0 < seconds:
-        rows = sorted(int(r) for r in order[done_rows:done_rows + 16])
-        att.prefill_shard(qb, kb, ref.segments, c["scale"], v=vb, rows=rows, decode=formats.bf16_bits_to_f64)
-        flops += int(np.sum(ref.pos_id[rows].astype(np.int64) + 1)) * c["Hq"] * 2 * (c["Dqk"] + c["Dv"])
-        done_rows += len(rows)
-    dt = time.perf_counter() - t0
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    done_rows, flops, dt = _oracle_rows(att, qb, kb, vb, ref, c, order, seconds, 0, formats.bf16_bits_to_f64)
+    del qb, kb, vb
+    head = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{done_rows} of {ref.n_local} local query rows (all 32 heads, random order) of the same "
                       f"zigzag workload in {dt:.1f} s; float64 numpy; the full step would take "
                       f"{prefill['flops'] / (flops / dt):.0f} s"}
+    per["config2"] = dict(rows=done_rows, rows_total=ref.n_local, seconds=round(dt, 2),
+                          rows_per_s=round(done_rows / dt, 2), fp64_gflops=round(flops / dt / 1e9, 2),
+                          full_step_seconds_extrapolated=round(prefill["flops"] / (flops / dt), 1))
+
+    # config 1: fp32 GQA decode, 4 shards + merge, in full
+    c1 = synth.config(1)
+    q = synth.f32_normal(1, 1, (c1["B"], c1["Hq"], c1["Dqk"])).astype(np.float64)
+    k = synth.f32_normal(1, 2, (c1["B"], c1["L"], c1["Hkv"], c1["Dqk"]), chunk=1).astype(np.float64)
+    v = synth.f32_normal(1, 3, (c1["B"], c1["L"], c1["Hkv"], c1["Dv"]), chunk=1).astype(np.float64)
+    t0 = time.perf_counter()
+    _oracle_decode_all_shards(att, q, k, c1["L"], c1["C"], c1["scale"], vcache=v)
+    dt = time.perf_counter() - t0
+    fl = _decode_flops(c1["L"], c1["Hq"], c1["Dqk"], c1["Dv"]) * c1["B"]
+    per["config1"] = dict(sample="the whole step (4 shard decodes + merge)", seconds=round(dt, 4),
+                          fp64_gflops=round(fl / dt / 1e9, 3),
+                          cache_gbs=round(c1["B"] * c1["L"] * c1["Hkv"] * (c1["Dqk"] + c1["Dv"]) * 4 / dt / 1e9, 3))
+
+    # config 3: MLA decode, request 0 of the batch (its draw is that of the
+    # full cache), 8 shards + merge, bf16 and FP8; extrapolated to 64 requests
+    c3 = synth.config(3)
+    q3 = synth.bf16_normal(3, 1, (c3["B"], c3["Hq"], c3["Dqk"]))[:1]
+    bits, codes, scales = synth.latent_cache_both(3, 2, 1, c3["L"], c3["Dqk"], c3["std"])
+    fl = _decode_flops(c3["L"], c3["Hq"], c3["Dqk"], c3["Dv"])
+    per["config3"] = {}
+    for name, cache, kw in (("bf16", bits, dict(decode=formats.bf16_bits_to_f64)),
+                            ("fp8", codes, dict(decode=formats.e4m3_to_f64, kv_scale=scales))):
+        t0 = time.perf_counter()
+        _oracle_decode_all_shards(att, formats.bf16_bits_to_f64(q3), cache, c3["L"], c3["C"], c3["scale"],
+                                  dv=c3["Dv"], **kw)
+        dt = time.perf_counter() - t0
+        per["config3"][name] = dict(sample="request 0 of 64: 64 heads x 131072 tokens, 8 shard decodes + merge",
+                                    seconds=round(dt, 2), fp64_gflops=round(fl / dt / 1e9, 2),
+                                    full_step_seconds_extrapolated=round(dt * c3["B"], 1))
+    del bits, codes, scales
+
+    # configs 4 and 5: sampled local rows of the prefill shards
+    for kcfg in (4, 5):
+        ck = synth.config(kcfg)
+        planner = plans.plan_zigzag if ck["strategy"] == "zigzag" else plans.plan_interleave
+        pk = planner(ck["C"], ck["rank"], ck["new_len"], ck["prefix_len"])
+        Tk = sum(ck["new_len"]) + sum(ck["prefix_len"])
+        ends = _segment_end_rows(pk)
+        rest = [int(r) for r in synth.rng(kcfg, 9).permutation(pk.n_local) if int(r) not in set(ends)]
+        order = ends + rest
+        # draw only the query slabs (256 rows) and key/value slabs (4096
+        # tokens) the sampled rows read, as the full draw has them
+        est = max(min_rows, 64) + len(ends)
+        rows_needed = order[:est]
+        qk = synth.bf16_normal_slabs(kcfg, 1, (pk.n_local, ck["Hq"], ck["Dqk"]), [r // 256 for r in rows_needed],
+                                     chunk=256)
+        where = {}
+        for (_req, r0, n, p0, st, kv0) in pk.segments:
+            for r in range(r0, r0 + n):
+                where[r] = (kv0, p0 + (r - r0) * st)
+        kv_slabs = set()
+        for r in rows_needed:
+            kv0, p = where[r]
+            kv_slabs.update(range(kv0 // 4096, (kv0 + p) // 4096 + 1))
+        kk = synth.bf16_normal_slabs(kcfg, 2, (Tk, ck["Hkv"], ck["Dqk"]), kv_slabs)
+        vk = None if ck["Hkv"] == 1 else synth.bf16_normal_slabs(kcfg, 3, (Tk, ck["Hkv"], ck["Dv"]), kv_slabs)
+        done_rows, flops, dt = _oracle_rows(att, qk, kk, vk, pk, ck, rows_needed, per_config_seconds, min_rows,
+                                            formats.bf16_bits_to_f64)
+        total = int(np.sum(pk.pos_id.astype(np.int64) + 1)) * ck["Hq"] * 2 * (ck["Dqk"] + ck["Dv"])
+        per[f"config{kcfg}"] = dict(
+            sample=f"{done_rows} local rows ({min(done_rows, len(ends))} of them segment ends, the rest random) "
+                   f"of {pk.n_local}, all heads",
+            rows=done_rows, rows_total=pk.n_local, seconds=round(dt, 2), rows_per_s=round(done_rows / dt, 3),
+            fp64_gflops=round(flops / dt / 1e9, 2), full_step_seconds_extrapolated=round(total / (flops / dt), 0))
+        del qk, kk, vk
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    head["per_config"] = per
+    return head
 
 
 def main():
@@ -655,6 +768,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the secondary MLA decode figures")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-config-seconds", type=float, default=5.0,
+                    help="CPU oracle time per sampled configuration (MLA and interleave prefill)")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="sample at least this many local rows of the MLA / interleave prefill shards")
+    ap.add_argument("--cpu-only", action="store_true", help="only the CPU oracle baselines (no GPU figures)")
     ap.add_argument("--decode-only", action="store_true", help="time only the MLA decode (profiling)")
     ap.add_argument("--gqa-only", action="store_true", help="time only the GQA decode figures (profiling)")
     ap.add_argument("--no-extra-prefill", action="store_true",
@@ -667,8 +785,18 @@ def main():
               "(shards are evaluated as partial launches on one device). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import torch
     import synth
+    if args.cpu_only:
+        from oracle import plans as oplans
+        c2 = synth.config(2)
+        ref = oplans.plan_zigzag(c2["C"], c2["rank"], c2["new_len"], c2["prefix_len"])
+        flops = int(np.sum(ref.pos_id.astype(np.int64) + 1)) * c2["Hq"] * 2 * (c2["Dqk"] + c2["Dv"])
+        base = cpu_baseline(synth, {"cfg": c2, "flops": flops}, args.cpu_seconds, args.cpu_config_seconds,
+                            args.cpu_rows)
+        print(json.dumps({"cpu_baseline": base}), flush=True)
+        return
+
+    import torch
     import context_attention_long_amd as cpa
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -783,6 +911,16 @@ def main():
             f"{dec['multi_query_bf16']['tflops']:.0f} TFLOP/s; sparse top-2048 decode "
             f"{dec['sparse_bf16']['decode']['gbs']:.0f} GB/s, prefill {dec['sparse_bf16']['prefill']['gbs']:.0f} GB/s")
 
+    if not args.no_decode:
+        log("[bench] split-KV GQA decode (serving shape, bf16 and FP8) and config 1 (fp32) ...")
+        g = bench_gqa_decode(cpa, torch, max(3, args.steps // 2), args.warmup, args.warmup_ms)
+        rnd = lambda d: {k: round(v, 4) if isinstance(v, float) else v for k, v in d.items()}
+        line["decode_gqa"] = {"workload": g["workload"], "unit": "GB/s", "bf16": rnd(g["bf16"]), "fp8": rnd(g["fp8"])}
+        c1 = bench_decode_config1(cpa, torch, synth, max(3, args.steps // 2), args.warmup, args.warmup_ms)
+        line["decode_config1"] = {k: (rnd(v) if isinstance(v, dict) else v) for k, v in c1.items()}
+        log(f"[bench] GQA decode bf16 {g['bf16']['gbs']:.0f} GB/s/step, fp8 {g['fp8']['gbs']:.0f} GB/s/step; "
+            f"config 1 (cache flushed) {c1['cache_flushed']['gbs']:.1f} GB/s/step")
+
     if not args.no_extra_prefill:
         for k, key in ((4, "prefill_mla_zigzag"), (5, "prefill_interleave")):
             log(f"[bench] {key} (config {k}) ...")
@@ -791,7 +929,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
-        line["cpu_baseline"] = cpu_baseline(synth, pre, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(synth, pre, args.cpu_seconds, args.cpu_config_seconds, args.cpu_rows)
     print(json.dumps(line), flush=True)
 
 

@@ -109,6 +109,23 @@ def normal(config, stream, shape, std=1.0, chunk=4096, out_fn=None, out_dtype=No
     return out
 
 
+def bf16_normal_slabs(config, stream, shape, slabs, std=1.0, chunk=4096, out=None):
+    """Only the slabs ``slabs`` (``chunk`` rows each along the first axis) of
+    bf16_normal(config, stream, shape, std, chunk), drawn alone into ``out``
+    (a lazily allocated uint16 array of ``shape`` if None, other rows left
+    unset). The rows are identical to those of the full draw."""
+    shape = tuple(int(s) for s in shape)
+    if out is None:
+        out = np.empty(shape, dtype=np.uint16)
+    for i in sorted(set(int(x) for x in slabs)):
+        a, b = i * chunk, min(shape[0], (i + 1) * chunk)
+        x = rng(config, stream, i).standard_normal((b - a,) + shape[1:], dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        out[a:b] = f32_to_bf16_bits(x)
+    return out
+
+
 def bf16_normal(config, stream, shape, std=1.0, chunk=4096):
     """N(0, std^2) rounded to bf16; returns uint16 words."""
     return normal(config, stream, shape, std, chunk, f32_to_bf16_bits, np.uint16)
