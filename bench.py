@@ -263,6 +263,7 @@ def bench_decode(cpa, torch, synth, steps, warmup, warmup_ms):
                          gpu_ms_per_step=gpu_step_ms,
                          launch_ms=lm, launch_gbs=launch_bytes / (lm * 1e-3) / 1e9,
                          launch_bytes=launch_bytes)
+    res["sparse_fp8"] = bench_sparse(cpa, torch, synth, c, cache_fp8, steps, warmup, warmup_ms, kv_scale=sc)
     del cache_fp8, sc
     torch.cuda.empty_cache()
     res["round_robin_bf16"] = bench_round_robin(cpa, torch, c, q, cache_bf16, steps, warmup, warmup_ms)
@@ -336,7 +337,7 @@ def bench_topk(cpa, torch, synth, c, steps, warmup, warmup_ms):
 SPARSE_K = 2048
 
 
-def bench_sparse(cpa, torch, synth, c, cache, steps, warmup, warmup_ms):
+def bench_sparse(cpa, torch, synth, c, cache, steps, warmup, warmup_ms, kv_scale=None):
     """Sparse (top-k index list) MLA attention on the same latent cache:
     (a) decode: one query per request, 2,048 rows drawn from its 131072;
     (b) prefill: 4,096 queries of request 0 at positions 8j (j = 12288 ..
@@ -344,8 +345,10 @@ def bench_sparse(cpa, torch, synth, c, cache, steps, warmup, warmup_ms):
     rows at or below its position. Algorithmic bytes per query: the listed
     rows (1,152 B) and their 4-byte indices, plus per head the bf16 query
     (1,152 B), the f32 output (2,048 B) and its LSE; FLOPs: 2,176 per row
-    and head (QK over 576, PV over 512)."""
+    and head (QK over 576, PV over 512). With kv_scale the cache is FP8:
+    a row is 576 code bytes plus its 4-byte scale."""
     B, L, H = c["B"], c["L"], c["Hq"]
+    row_bytes = 1152 if kv_scale is None else 576 + 4
     dev = cache.device
     out = {}
     cases = (("decode", B, None, None), ("prefill", 4096, np.zeros(4096, np.int32),
@@ -362,7 +365,7 @@ def bench_sparse(cpa, torch, synth, c, cache, steps, warmup, warmup_ms):
         ws = torch.empty(max(1, cpa.attn_sparse_mla_workspace_size(N, SPARSE_K)), dtype=torch.uint8, device=dev)
 
         def step():
-            cpa.attn_sparse_mla(q, cache, idx_d, c["scale"], req=req_d, out=o, lse=l, workspace=ws)
+            cpa.attn_sparse_mla(q, cache, idx_d, c["scale"], req=req_d, out=o, lse=l, workspace=ws, kv_scale=kv_scale)
 
         _warm(torch, step, warmup, warmup_ms)
         n_steps = steps if name == "decode" else max(3, steps // 4)
@@ -374,7 +377,7 @@ def bench_sparse(cpa, torch, synth, c, cache, steps, warmup, warmup_ms):
         torch.cuda.synchronize()
         ms = sev[0].elapsed_time(sev[1]) / n_steps
         rows = int(cnt.sum())
-        nbytes = rows * (1152 + 4) + N * H * (1152 + 2048 + 4)
+        nbytes = rows * (row_bytes + 4) + N * H * (1152 + 2048 + 4)
         flops = rows * H * 2176
         out[name] = dict(queries=N, k=SPARSE_K, ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9,
                          tflops=flops / (ms * 1e-3) / 1e12, algorithmic_bytes=nbytes, flops=flops)
@@ -898,6 +901,9 @@ def main():
             "sparse_bf16": {k: dict({kk: round(vv, 4) if isinstance(vv, float) else vv for kk, vv in v.items()},
                                     frac_of_hbm_peak=round(v["gbs"] / PEAK_HBM_GBS, 4))
                             for k, v in dec["sparse_bf16"].items()},
+            "sparse_fp8": {k: dict({kk: round(vv, 4) if isinstance(vv, float) else vv for kk, vv in v.items()},
+                                   frac_of_hbm_peak=round(v["gbs"] / PEAK_HBM_GBS, 4))
+                           for k, v in dec["sparse_fp8"].items()},
             "multi_query_bf16": dict(
                 {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["multi_query_bf16"].items()},
                 workload="4 query rows per request (MTP3), causal among them; same cache and shards",
@@ -909,7 +915,8 @@ def main():
             f"(cache write {dec['round_robin_bf16']['cache_write_gbs']:.0f} GB/s), "
             f"multi-query Q=4 {dec['multi_query_bf16']['gbs']:.0f} GB/s/step, "
             f"{dec['multi_query_bf16']['tflops']:.0f} TFLOP/s; sparse top-2048 decode "
-            f"{dec['sparse_bf16']['decode']['gbs']:.0f} GB/s, prefill {dec['sparse_bf16']['prefill']['gbs']:.0f} GB/s")
+            f"{dec['sparse_bf16']['decode']['gbs']:.0f} GB/s (FP8 {dec['sparse_fp8']['decode']['gbs']:.0f}), "
+            f"prefill {dec['sparse_bf16']['prefill']['gbs']:.0f} GB/s (FP8 {dec['sparse_fp8']['prefill']['gbs']:.0f})")
 
     if not args.no_decode:
         log("[bench] split-KV GQA decode (serving shape, bf16 and FP8) and config 1 (fp32) ...")

@@ -103,9 +103,9 @@ def lib():
         L.attn_sparse_mla_workspace_size.restype = ctypes.c_size_t
         L.attn_sparse_mla_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32]
         L.attn_sparse_mla.restype = ctypes.c_int
-        L.attn_sparse_mla.argtypes = [P(CpaTensor), P(CpaTensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, P(CpaTensor), P(CpaTensor),
-                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.attn_sparse_mla.argtypes = [P(CpaTensor), P(CpaTensor), P(CpaTensor), ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, P(CpaTensor),
+                                      P(CpaTensor), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         vp = ctypes.c_void_p
         L.attn_topk_local.restype = ctypes.c_int
         L.attn_topk_local.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int32,
@@ -387,12 +387,12 @@ def attn_sparse_mla_workspace_size(n_queries, k):
 
 
 def attn_sparse_mla(q, cache, idx, softmax_scale, n_idx=None, req=None, out=None, lse=None, workspace=None,
-                    stream=None):
+                    stream=None, kv_scale=None, cache_dtype=None):
     """Sparse MLA attention: query n of q [N, 64, 576] bf16 attends the rows
-    idx[n, :n_idx[n]] of request req[n] of cache [B, Lmax, 1, 576] bf16.
-    idx: int32 device tensor [N, k] (last dim contiguous); n_idx / req:
-    int32 device tensors [N] or None. Returns (out [N, 64, 512] f32,
-    lse [N, 64] f32)."""
+    idx[n, :n_idx[n]] of request req[n] of cache [B, Lmax, 1, 576] (bf16, or
+    torch.uint8 FP8 E4M3 bytes with kv_scale [B, Lmax] f32). idx: int32
+    device tensor [N, k] (last dim contiguous); n_idx / req: int32 device
+    tensors [N] or None. Returns (out [N, 64, 512] f32, lse [N, 64] f32)."""
     torch = _torch()
     N = q.shape[0]
     if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != N or (idx.shape[1] > 1 and idx.stride(1) != 1):
@@ -410,9 +410,10 @@ def attn_sparse_mla(q, cache, idx, softmax_scale, n_idx=None, req=None, out=None
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() if workspace is not None else 0
-    dq, dc, do, dl = tensor_desc(q), tensor_desc(cache), tensor_desc(out), tensor_desc(lse)
+    dq, dc, do, dl = tensor_desc(q), tensor_desc(cache, cache_dtype), tensor_desc(out), tensor_desc(lse)
+    ds = tensor_desc(kv_scale) if kv_scale is not None else None
     ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
-    _check(lib().attn_sparse_mla(ctypes.byref(dq), ctypes.byref(dc), ptr(req), ptr(idx),
+    _check(lib().attn_sparse_mla(ctypes.byref(dq), ctypes.byref(dc), _ptr(ds), ptr(req), ptr(idx),
                                  int(idx.stride(0)) if N > 0 else int(k), int(k), ptr(n_idx), float(softmax_scale),
                                  ctypes.byref(do), ctypes.byref(dl), ctypes.c_void_p(ws_ptr), ws_bytes,
                                  _stream(stream)))

@@ -138,7 +138,7 @@ size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Dv, int nsplit) {
 
 extern "C" const char* cpa_last_error(void) { return cpa::g_err.c_str(); }
 
-extern "C" int32_t cpa_abi_version(void) { return 100; }
+extern "C" int32_t cpa_abi_version(void) { return 101; }
 
 // --------------------------------------------------------------------- merge
 
@@ -470,13 +470,13 @@ extern "C" size_t attn_sparse_mla_workspace_size(int64_t n_queries, int32_t k) {
   return decode_ws_bytes(n_queries, 64, 512, mla_nsplit(n_queries, k));
 }
 
-extern "C" cpa_status attn_sparse_mla(const cpa_tensor* q, const cpa_tensor* cache, const int32_t* req,
-                                      const int32_t* idx, int64_t idx_stride, int32_t k, const int32_t* n_idx,
-                                      float softmax_scale, const cpa_tensor* out, const cpa_tensor* lse,
-                                      void* workspace, size_t ws_bytes, void* stream) {
+extern "C" cpa_status attn_sparse_mla(const cpa_tensor* q, const cpa_tensor* cache, const cpa_tensor* kv_scale,
+                                      const int32_t* req, const int32_t* idx, int64_t idx_stride, int32_t k,
+                                      const int32_t* n_idx, float softmax_scale, const cpa_tensor* out,
+                                      const cpa_tensor* lse, void* workspace, size_t ws_bytes, void* stream) {
   cpa::clear_error();
   CPA_TRY(check_tensor(q, "sparse q", 1u << CPA_BF16, 3));
-  CPA_TRY(check_tensor(cache, "sparse cache", 1u << CPA_BF16, 4));
+  CPA_TRY(check_tensor(cache, "sparse cache", (1u << CPA_BF16) | (1u << CPA_FP8_E4M3), 4));
   CPA_TRY(check_tensor(out, "sparse out", 1u << CPA_F32, 3));
   CPA_TRY(check_tensor(lse, "sparse lse", 1u << CPA_F32, 2, 0));
   const int64_t N = q->shape[0], B = cache->shape[0], Lmax = cache->shape[1];
@@ -491,9 +491,23 @@ extern "C" cpa_status attn_sparse_mla(const cpa_tensor* q, const cpa_tensor* cac
   if (N > 0 && k > 0 && idx == nullptr) return fail(CPA_E_INVAL, "sparse: idx is NULL");
   if (req == nullptr && N > B && Lmax > 0) return fail(CPA_E_INVAL, "sparse: without req, query n uses request n < B");
   if ((uintptr_t)idx % 4) return fail(CPA_E_INVAL, "sparse: idx must be 4-byte aligned");
+  const bool fp8 = cache->dtype == CPA_FP8_E4M3;
+  const int64_t esz = fp8 ? 1 : 2;
   // rows are addressed with 32-bit byte offsets from the request's base
-  if (Lmax > 0 && (Lmax - 1) * cache->stride[1] * 2 + 2 * 576 > (int64_t)UINT32_MAX)
+  if (Lmax > 0 && (Lmax - 1) * cache->stride[1] * esz + esz * 576 > (int64_t)UINT32_MAX)
     return fail(CPA_E_INVAL, "sparse: a request's cache spans more than 4 GiB");
+  if (fp8) {
+    if (kv_scale == nullptr || kv_scale->data == nullptr) return fail(CPA_E_INVAL, "sparse: FP8 cache needs kv_scale");
+    CPA_TRY(check_tensor(kv_scale, "sparse kv_scale", 1u << CPA_F32, 2, 0));
+    if (kv_scale->shape[0] != B || kv_scale->shape[1] != Lmax)
+      return fail(CPA_E_INVAL, "sparse: kv_scale must be f32 [B, Lmax]");
+    if (Lmax > 0 && (Lmax - 1) * kv_scale->stride[1] * 4 + 4 > (int64_t)UINT32_MAX)
+      return fail(CPA_E_INVAL, "sparse: a request's scales span more than 4 GiB");
+    if (cache->stride[1] % 16 || cache->stride[0] % 16)
+      return fail(CPA_E_INVAL, "sparse: FP8 rows must start on 16-byte boundaries");
+  } else if (kv_scale != nullptr && kv_scale->data != nullptr) {
+    return fail(CPA_E_INVAL, "sparse: kv_scale is only for an FP8 cache");
+  }
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(CPA_E_INVAL, "sparse: softmax_scale must be finite and > 0");
   if (N == 0) return CPA_OK;
@@ -521,6 +535,10 @@ extern "C" cpa_status attn_sparse_mla(const cpa_tensor* q, const cpa_tensor* cac
   }
   a.q = static_cast<const uint16_t*>(q->data);
   a.cache = cache->data;
+  a.kv_scale = fp8 ? static_cast<const float*>(kv_scale->data) : nullptr;
+  a.s_b = fp8 ? kv_scale->stride[0] : 0;
+  a.s_t = fp8 ? kv_scale->stride[1] : 0;
+  a.fp8 = fp8;
   a.req = req;
   a.idx = idx;
   a.n_idx = n_idx;

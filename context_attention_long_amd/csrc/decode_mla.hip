@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
     const uint16_t* qhead = a.q + (int64_t)b * a.q_b + (int64_t)k * a.q_q + (int64_t)(16 * w + c) * a.q_h;
     QkStat st{-INFINITY, 0.f};
     if constexpr (kFp8) {
-      const f8::Lds S{smem, ssc, plds, alpha_s, lsum_s};
+      const f8::Lds S{smem, ssc, plds, alpha_s, lsum_s, f8::kStages - 1};
       f8::Query Q;
       f8::load_query(qhead, g, Q);
       f8::ws_qk(T, w, g, c, f8::bases(w, g, c), Q, a.scale_log2, st, S);
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) oacc[m][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (kFp8) {
-      const f8::Lds S{smem, ssc, plds, alpha_s, lsum_s};
+      const f8::Lds S{smem, ssc, plds, alpha_s, lsum_s, f8::kStages - 1};
       f8::ws_pv<kP>(T, reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t,
                     a.kv_scale + (int64_t)b * a.s_b, a.s_t, tid - 256, w, g, c, f8::bases(w, g, c), oacc, S);
     } else {

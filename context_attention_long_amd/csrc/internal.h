@@ -77,7 +77,9 @@ struct DecodeMlaArgs {
 
 struct SparseMlaArgs {
   const uint16_t* q;      // [N, 64, 576] bf16
-  const void* cache;      // [B, Lmax, 576] bf16 words (one kv head)
+  const void* cache;      // [B, Lmax, 576] bf16 words or E4M3 bytes (one kv head)
+  const float* kv_scale;  // [B, Lmax] per-token scale of an FP8 cache, else null
+  int64_t s_b, s_t;
   const int32_t* req;     // [N] request of each query, or null (query n -> request n)
   const int32_t* idx;     // [N, K] selected cache rows
   const int32_t* n_idx;   // [N] entries that count, or null (all K)
@@ -90,6 +92,7 @@ struct SparseMlaArgs {
   int64_t l_s, l_n, l_h;
   int32_t N, B, K, Lmax, nsplit;
   int32_t reuse;          // several queries share a request's rows: cached loads
+  int32_t fp8;
   float scale_log2;
 };
 

@@ -63,11 +63,12 @@ static_assert(kTileUnits == 4 * kThreads + kThreads / 2, "unit split over the PV
 static_assert(kRowUnits % 4 == 0, "swizzle groups of four units");
 
 struct Lds {
-  char* tiles;   // kStages x kTileBytes
-  char* scales;  // kStages x kScaleSlot (f32 token scales of the tile, 32 used)
+  char* tiles;   // stages x kTileBytes
+  char* scales;  // stages x kScaleSlot (f32 token scales of the tile, 32 used)
   char* p;       // [2][64 heads][64 B] bf16 probabilities
   float* alpha;  // [2][64]
   float* lsum;   // [64]
+  int stage_mask;  // stages - 1 (a power of two: kStages for ranges, fewer for index lists)
 };
 
 // Swizzle of row r: the physical unit of logical unit u is u ^ swz(r).
@@ -220,15 +221,17 @@ __device__ __forceinline__ void qk_tile(const char* tile, const Bases& L, const 
   }
 }
 
-__device__ __forceinline__ char* stage(const Lds& S, int i) { return S.tiles + (i & (kStages - 1)) * kTileBytes; }
+__device__ __forceinline__ char* stage(const Lds& S, int i) { return S.tiles + (i & S.stage_mask) * kTileBytes; }
 __device__ __forceinline__ char* scale_slot(const Lds& S, int i) {
-  return S.scales + (i & (kStages - 1)) * kScaleSlot;
+  return S.scales + (i & S.stage_mask) * kScaleSlot;
 }
 
 // QK role. Barriers: 1 (tile 0) + (ntiles - 1) (loop) + 1 (after the loop),
-// the same sequence as the PV role's.
+// the same sequence as the PV role's. kMask: mask(i) gives the selection
+// bits of tile i (index lists).
+template <bool kMask = false, typename MaskFn = uint32_t (*)(int)>
 __device__ __forceinline__ void ws_qk(const Tiles& T, int w, int g, int c, const Bases& L, const Query& Q,
-                                      float scale_log2, QkStat& st, const Lds& S) {
+                                      float scale_log2, QkStat& st, const Lds& S, MaskFn&& mask = nullptr) {
   if (T.ntiles <= 0) return;
   const float sl2 = scale_log2 * Q.inv_scale;
   auto step = [&](int i, auto parity) {
@@ -241,10 +244,11 @@ __device__ __forceinline__ void ws_qk(const Tiles& T, int w, int g, int c, const
 #pragma unroll
     for (int j = 0; j < 4; ++j) ts.v[j] = s0[j], ts.v[4 + j] = s1[j];
     Soft sm;
-    soft_scores<true>(sm, sacc, T.nvalid(i), g, sl2, ts);
+    if constexpr (kMask) soft_scores<true, true>(sm, sacc, T.nvalid(i), g, sl2, ts, mask(i));
+    else soft_scores<true>(sm, sacc, T.nvalid(i), g, sl2, ts);
     soft_ref(sm, st, sl2);
-    soft_exp<true, 0>(sm, st, ts, sl2);
-    soft_exp<true, 4>(sm, st, ts, sl2);
+    soft_exp<true, 0, kMask>(sm, st, ts, sl2);
+    soft_exp<true, 4, kMask>(sm, st, ts, sl2);
     soft_store(sm, st, S.p + kH * kPRowBytes * P, S.alpha + kH * P, w, g, c);
   };
   __syncthreads();  // tile 0 ready
@@ -388,6 +392,140 @@ __device__ __forceinline__ void ws_pv(const Tiles& T, const uint8_t* base, int64
   }
   __syncthreads();  // P of the last tile visible
   pv(n - 1, [](int) {});
+}
+
+// Stages of the index-list role (4: tiles i .. i+3 in LDS).
+constexpr int kGatherStages = 4;
+
+// PV role over the FP8 rows an index list names (sparse attention): tile t
+// holds list entries [32 t, 32 t + 32) of the range. Each PV wavefront
+// copies the 32 entries of a tile into its own LDS ring slot with one
+// 4-byte-per-lane direct load, five tiles ahead; the row loads of tile t
+// (three tiles ahead, the same units and swizzle as ws_pv) and the token
+// scales take their row numbers from the ring. An entry outside [0, nrows)
+// reads row 0 (its score is masked by the QK role). Loads per PV thread and
+// tile: one entry copy and kLoads rows / scales, in that order.
+template <Policy kPol>
+__device__ __forceinline__ void ws_pv_gather(const Tiles& T, const uint8_t* base, int64_t c_t, const float* sbase,
+                                             int64_t s_t, const int32_t* ilist, int nrows, int tp, int w, int g,
+                                             int c, const Bases& L, f32x4 (&oacc)[kMv][4], const Lds& S,
+                                             char* ring) {
+  if (T.ntiles <= 0) return;
+  const int lane = tp & 63;
+  const int n = T.ntiles;
+  const bool unit5 = w < 2;  // wave-uniform: waves 0, 1 load a fifth unit, waves 2, 3 the scales
+  uint32_t rinfo[kLoads];    // tile row (high half) and swizzled byte offset in the row of this thread's units
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) {
+    const int U = k < 4 ? tp + kThreads * k : 4 * kThreads + tp;  // k = 4 only where unit5
+    const int r = U / kRowUnits, pu = U % kRowUnits;
+    rinfo[k] = ((uint32_t)r << 16) | (uint32_t)(16 * (pu ^ swz(r)));
+  }
+  const char* wring = ring + w * (kIdxSlots * kIdxSlotBytes);
+  const uint32_t wring_lds = __builtin_amdgcn_readfirstlane(lds_addr(wring));
+  const uint64_t ibase = uniform_ptr(ilist), cbase = uniform_ptr(base), sb = uniform_ptr(sbase);
+  const uint32_t rowbytes = (uint32_t)c_t;  // the host bounds nrows * c_t below 2^32
+  const uint32_t sstride = (uint32_t)(s_t * 4);
+  auto slot = [&](int t) { return (t % kIdxSlots) * kIdxSlotBytes; };
+  auto issue_idx = [&](int t) {
+    const int tc = t < n ? t : n - 1;  // past the end: re-read the last tile's entries
+    const int e = min(kBN * T.phys(tc) + (lane & 31), T.ntok - 1);
+    lds_dma4_s<Policy::kReuse>(ibase, (uint32_t)e * 4u, wring_lds + (uint32_t)slot(t));
+  };
+  auto row_of = [&](int t, int row) -> uint32_t {
+    const int v = *reinterpret_cast<const int*>(wring + slot(t) + 4 * row);
+    return (uint32_t)v < (uint32_t)nrows ? (uint32_t)v : 0u;
+  };
+  auto dst = [&](int t, int k) -> uint32_t {  // LDS byte address of this wave's load k of tile t
+    return __builtin_amdgcn_readfirstlane(lds_addr(stage(S, t) + 16 * (kThreads * k + 64 * w)));
+  };
+  // source offsets of tile t's loads (rows, or the scales of waves 2 and 3)
+  auto offsets = [&](int t, uint32_t (&voff)[kLoads]) {
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k)
+      voff[k] = (k == 4 && !unit5) ? row_of(t, lane & 31) * sstride
+                                   : row_of(t, (int)(rinfo[k] >> 16)) * rowbytes + (rinfo[k] & 0xffffu);
+  };
+  auto load = [&](int t, int k, const uint32_t (&voff)[kLoads]) {
+    if (k < 4 || unit5) lds_dma16_s<kPol>(cbase, voff[k], dst(t, k));
+    else lds_dma4_s<kPol>(sb, voff[k], __builtin_amdgcn_readfirstlane(lds_addr(scale_slot(S, t))));
+  };
+  auto issue_tile = [&](int t) {
+    uint32_t voff[kLoads];
+    offsets(t, voff);
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) load(t, k, voff);
+  };
+  // ---- prologue: entries of tiles 0..4, rows of tiles 0..2 ----
+  issue_idx(0);
+  issue_idx(1);
+  issue_idx(2);
+  wait_vmcnt<2>();  // entries of tile 0
+  issue_tile(0);
+  issue_idx(3);
+  if (n > 1) {
+    wait_vmcnt<kLoads + 2>();  // entries of tile 1 (then: 2, rows 0, 3)
+    issue_tile(1);
+  }
+  issue_idx(4);
+  if (n > 2) {
+    wait_vmcnt<2 * kLoads + 2>();  // entries of tile 2 (then: rows 0, 3, rows 1, 4)
+    issue_tile(2);
+  }
+  // rows of tile 0 landed (after them: entries 3, rows 1, entries 4, rows 2)
+  if (n > 2) wait_vmcnt<2 * kLoads + 2>();
+  else if (n == 2) wait_vmcnt<kLoads + 2>();
+  else wait_vmcnt<2>();
+  __syncthreads();
+
+  constexpr int kAheadV = 4;
+  auto pv = [&](int i, auto&& hook) {
+    const char* cur = stage(S, i);
+    const float* acur = S.alpha + kH * (i & 1);
+    const char* pcur = S.p + kH * kPRowBytes * (i & 1);
+    float al[4];
+    bf16x8 pb[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      al[hb] = acur[16 * hb + c];
+      pb[hb] = *reinterpret_cast<const bf16x8*>(pcur + p_off(16 * hb + c, g));
+    }
+    i32x2 vr[kMv];
+    auto load_v = [&](int m) { vr[m] = lds_read_tr8(cur + L.pv[m & 3] + 64 * (m >> 2)); };
+#pragma unroll
+    for (int m = 0; m < kAheadV; ++m) load_v(m);
+    if (__any(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
+#pragma unroll
+      for (int m = 0; m < kMv; ++m)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) oacc[m][hb] *= al[hb];
+    }
+#pragma unroll
+    for (int m = 0; m < kMv; ++m) {
+      if (m + kAheadV < kMv) load_v(m + kAheadV);
+      hook(m);
+      const bf16x8 va = codes_to_bf16(vr[m]);
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        oacc[m][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hb], oacc[m][hb], 0, 0, 0);
+    }
+  };
+  for (int i = 0; i + 1 < n; ++i) {
+    // rows of tile i+1 landed: after them only the entries of tile i+4 and the rows of tile i+2
+    if (i + 2 < n) wait_vmcnt<kLoads + 1>();
+    else wait_vmcnt<1>();
+    __syncthreads();  // P_i and tile i+1 visible; every wave is done with tile i-1 and P_{i-1}
+    issue_idx(i + 5);
+    const bool more = i + 3 < n;
+    uint32_t voff[kLoads];
+    if (more) offsets(i + 3, voff);
+    pv(i, [&](int m) {
+      if (more && m < kLoads) load(i + 3, m, voff);
+    });
+  }
+  __syncthreads();  // P of the last tile visible
+  pv(n - 1, [](int) {});
+  wait_vmcnt<0>();  // entry loads issued past the last tile have landed
 }
 
 }  // namespace f8

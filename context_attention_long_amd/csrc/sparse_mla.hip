@@ -8,7 +8,8 @@
 // several ranks combine with the LSE merge (DeepSeek-V4 notes, 5.2).
 //
 // One workgroup per (query, split): the split's share of the query's list
-// runs through the wave-specialised MLA core (mla_ws.h, ws_pv_gather), which
+// runs through the wave-specialised MLA core (mla_ws.h, ws_pv_gather; for an
+// FP8 cache with per-token scales the FP8-resident core, mla_fp8.h), which
 // gathers the listed rows into LDS tiles with direct loads whose addresses
 // come from the list itself (staged in LDS ahead of use). The splits of a
 // query are merged by the LSE merge.
@@ -16,15 +17,18 @@
 
 #include "internal.h"
 #include "mla_core.h"
+#include "mla_fp8.h"
 #include "mla_ws.h"
 
 namespace {
 
 using namespace cpa::mla;
 
-template <cpa::Policy kP>
+template <bool kFp8, cpa::Policy kP>
 __global__ __launch_bounds__(kWsThreads, 1) void sparse_mla_kernel(cpa::SparseMlaArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  constexpr int kTileLds = kFp8 ? f8::kGatherStages * f8::kTileBytes : kSmemBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kTileLds];
+  __shared__ __attribute__((aligned(16))) char ssc[kFp8 ? f8::kGatherStages * f8::kScaleSlot : 16];
   __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
   __shared__ __attribute__((aligned(16))) char ring[kIdxRingBytes];
   __shared__ float alpha_s[2 * kH], lsum_s[kH];
@@ -46,31 +50,50 @@ __global__ __launch_bounds__(kWsThreads, 1) void sparse_mla_kernel(cpa::SparseMl
   const Tiles T(0, e1 - e0, blockIdx.x * 2654435761u >> 7);
   const LdsBases L = lds_bases(w, g, c);
 
-  if (qk_role) {
-    bf16x8 qreg[kQSteps];
-    load_q(a.q + (int64_t)n * a.q_n + (int64_t)(16 * w + c) * a.q_h, g, qreg);
-    QkStat st{-INFINITY, 0.f};
-    // selection bits of tile i from the entry ring of PV wavefront w
-    const char* wring = ring + w * (kIdxSlots * kIdxSlotBytes);
-    auto mask = [&](int i) -> uint32_t {
-      const int v = *reinterpret_cast<const int*>(wring + (i % kIdxSlots) * kIdxSlotBytes + 4 * (lane & 31));
-      return (uint32_t)__ballot((uint32_t)v < (uint32_t)a.Lmax);
-    };
-    ws_qk<true>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); }, mask);
+  // selection bits of tile i from the entry ring of PV wavefront w
+  const char* wring = ring + w * (kIdxSlots * kIdxSlotBytes);
+  auto mask = [&](int i) -> uint32_t {
+    const int v = *reinterpret_cast<const int*>(wring + (i % kIdxSlots) * kIdxSlotBytes + 4 * (lane & 31));
+    return (uint32_t)__ballot((uint32_t)v < (uint32_t)a.Lmax);
+  };
+  const int32_t* ilist = a.idx + (int64_t)n * a.i_n + e0;
+  auto finish_lse = [&](const QkStat& st) {
     const float l = sum4_rows(st.l_run);
     if (g == 0) S.lsum[16 * w + c] = l;
     __syncthreads();
     if (g == 0)
       a.lse[(int64_t)split * a.l_s + (int64_t)n * a.l_n + (int64_t)(16 * w + c) * a.l_h] =
           l > 0.f ? (st.m_run + log2f(l)) * kLn2 : -INFINITY;
+  };
+  if (qk_role) {
+    QkStat st{-INFINITY, 0.f};
+    const uint16_t* qhead = a.q + (int64_t)n * a.q_n + (int64_t)(16 * w + c) * a.q_h;
+    if constexpr (kFp8) {
+      const f8::Lds S8{smem, ssc, plds, alpha_s, lsum_s, f8::kGatherStages - 1};
+      f8::Query Q;
+      f8::load_query(qhead, g, Q);
+      f8::ws_qk<true>(T, w, g, c, f8::bases(w, g, c), Q, a.scale_log2, st, S8, mask);
+    } else {
+      bf16x8 qreg[kQSteps];
+      load_q(qhead, g, qreg);
+      ws_qk<true>(T, w, g, c, L, qreg, a.scale_log2, st, S, [&](int i) { return ws_tile(S, i); }, mask);
+    }
+    finish_lse(st);
   } else {
     f32x4 oacc[kMv][4];
 #pragma unroll
     for (int m = 0; m < kMv; ++m)
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) oacc[m][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    ws_pv_gather<kP>(T, reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t,
-                     a.idx + (int64_t)n * a.i_n + e0, a.Lmax, tid - 256, w, g, c, L, oacc, S, ring);
+    if constexpr (kFp8) {
+      const f8::Lds S8{smem, ssc, plds, alpha_s, lsum_s, f8::kGatherStages - 1};
+      f8::ws_pv_gather<kP>(T, reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t,
+                           a.kv_scale + (int64_t)b * a.s_b, a.s_t, ilist, a.Lmax, tid - 256, w, g, c,
+                           f8::bases(w, g, c), oacc, S8, ring);
+    } else {
+      ws_pv_gather<kP>(T, reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, ilist, a.Lmax,
+                       tid - 256, w, g, c, L, oacc, S, ring);
+    }
     __syncthreads();
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
@@ -91,10 +114,16 @@ namespace cpa {
 int launch_sparse_mla(const SparseMlaArgs& a, void* stream) {
   const dim3 grid((unsigned)((int64_t)a.N * a.nsplit));
   hipStream_t st = (hipStream_t)stream;
-  if (a.reuse)
-    hipLaunchKernelGGL((sparse_mla_kernel<Policy::kReuse>), grid, dim3(kWsThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((sparse_mla_kernel<Policy::kStream>), grid, dim3(kWsThreads), 0, st, a);
+  if (a.fp8) {
+    if (a.reuse)
+      hipLaunchKernelGGL((sparse_mla_kernel<true, Policy::kReuse>), grid, dim3(kWsThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((sparse_mla_kernel<true, Policy::kStream>), grid, dim3(kWsThreads), 0, st, a);
+  } else if (a.reuse) {
+    hipLaunchKernelGGL((sparse_mla_kernel<false, Policy::kReuse>), grid, dim3(kWsThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((sparse_mla_kernel<false, Policy::kStream>), grid, dim3(kWsThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

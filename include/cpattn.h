@@ -302,7 +302,10 @@ cpa_status cp_plan_round_robin(int32_t C, int32_t rank, int32_t n_req, const int
  * its LSE, so lists split by owner across ranks combine exactly with
  * attn_merge_states (DeepSeek-V4 notes, 5.2).
  *   q       [N, 64, 576] bf16
- *   cache   [B, Lmax, 1, 576] bf16 (one latent per token)
+ *   cache   [B, Lmax, 1, 576] bf16, or FP8 E4M3 (one latent per token;
+ *           FP8 row strides multiples of 16 bytes)
+ *   kv_scale [B, Lmax] f32 per-token scale, required for FP8 and otherwise
+ *           NULL: entry = e4m3 * scale (as for attn_decode_shard)
  *   req     [N] int32 DEVICE, or NULL: query n uses request n (then N <= B)
  *   idx     DEVICE int32, row n at idx + n * idx_stride, k entries per row
  *           (idx_stride >= k); an entry outside [0, Lmax) is no selection
@@ -318,10 +321,10 @@ cpa_status cp_plan_round_robin(int32_t C, int32_t rank, int32_t n_req, const int
  * sizes outside these; CPA_E_CAPACITY for a short workspace.
  */
 size_t attn_sparse_mla_workspace_size(int64_t n_queries, int32_t k);
-cpa_status attn_sparse_mla(const cpa_tensor* q, const cpa_tensor* cache, const int32_t* req, const int32_t* idx,
-                           int64_t idx_stride, int32_t k, const int32_t* n_idx, float softmax_scale,
-                           const cpa_tensor* out, const cpa_tensor* lse, void* workspace, size_t ws_bytes,
-                           void* stream);
+cpa_status attn_sparse_mla(const cpa_tensor* q, const cpa_tensor* cache, const cpa_tensor* kv_scale,
+                           const int32_t* req, const int32_t* idx, int64_t idx_stride, int32_t k,
+                           const int32_t* n_idx, float softmax_scale, const cpa_tensor* out, const cpa_tensor* lse,
+                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Exact distributed top-k for sparse attention with a split index

@@ -334,12 +334,20 @@ static void check_sparse_topk_cachewrite() {
   const int32_t* idx = static_cast<const int32_t*>(dev());
   const size_t need = attn_sparse_mla_workspace_size(N, K);
   void* ws = dev(1 << 12);
-  EXPECT_CALL(attn_sparse_mla(&q, &cache, nullptr, idx, K, K, nullptr, 0.05f, &o, &l, ws, need, nullptr), CPA_OK,
+  EXPECT_CALL(attn_sparse_mla(&q, &cache, nullptr, nullptr, idx, K, K, nullptr, 0.05f, &o, &l, ws, need, nullptr), CPA_OK,
               true);
-  EXPECT_CALL(attn_sparse_mla(&q, &cache, nullptr, idx, K - 1, K, nullptr, 0.05f, &o, &l, ws, need, nullptr),
+  EXPECT_CALL(attn_sparse_mla(&q, &cache, nullptr, nullptr, idx, K - 1, K, nullptr, 0.05f, &o, &l, ws, need, nullptr),
               CPA_E_INVAL, false);  // stride < k
-  EXPECT_CALL(attn_sparse_mla(&q, &cache, nullptr, nullptr, K, K, nullptr, 0.05f, &o, &l, ws, need, nullptr),
+  EXPECT_CALL(attn_sparse_mla(&q, &cache, nullptr, nullptr, nullptr, K, K, nullptr, 0.05f, &o, &l, ws, need, nullptr),
               CPA_E_INVAL, false);
+
+  cpa_tensor cache8 = tensor(CPA_FP8_E4M3, {B, L, 1, 576}), scale8 = tensor(CPA_F32, {B, L});
+  EXPECT_CALL(attn_sparse_mla(&q, &cache8, &scale8, nullptr, idx, K, K, nullptr, 0.05f, &o, &l, ws, need, nullptr),
+              CPA_OK, true);
+  EXPECT_CALL(attn_sparse_mla(&q, &cache8, nullptr, nullptr, idx, K, K, nullptr, 0.05f, &o, &l, ws, need, nullptr),
+              CPA_E_INVAL, false);  // FP8 without its scales
+  EXPECT_CALL(attn_sparse_mla(&q, &cache, &scale8, nullptr, idx, K, K, nullptr, 0.05f, &o, &l, ws, need, nullptr),
+              CPA_E_INVAL, false);  // scales with a bf16 cache
 
   float* sc = static_cast<float*>(dev());
   int32_t* i32 = static_cast<int32_t*>(dev(1 << 8));

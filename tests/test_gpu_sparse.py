@@ -170,3 +170,65 @@ def test_sparse_rejects_bad_arguments(cpa):
     with pytest.raises(cpa.CpaError):   # short workspace
         cpa.attn_sparse_mla(q, c, H.i32_tensor(np.zeros((N, 2048), np.int32)), 0.1,
                             workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+
+
+def _fp8_inputs(N, B, L, seed, std=0.5):
+    rng = np.random.default_rng(seed)
+    qb = synth.f32_to_bf16_bits(rng.standard_normal((N, 64, 576)).astype(np.float32))
+    codes, sc = synth.f32_to_e4m3((rng.standard_normal((B, L, 1, 576)) * std).astype(np.float32))
+    return rng, qb, codes, sc[..., 0]
+
+
+def _run_fp8(cpa, qb, codes, sc, idx, scale, n_idx=None, req=None):
+    o, l = cpa.attn_sparse_mla(H.bf16_tensor(qb), H.u8_tensor(codes), H.i32_tensor(idx), scale,
+                               n_idx=H.i32_tensor(n_idx) if n_idx is not None else None,
+                               req=H.i32_tensor(req) if req is not None else None, kv_scale=H.f32_tensor(sc))
+    _sync()
+    ro, rl = att.sparse_mla(formats.bf16_bits_to_f64(qb), codes, idx, scale, n_idx=n_idx, req=req,
+                            decode=formats.e4m3_to_f64, kv_scale=sc)
+    return H.host(o), H.host(l), ro, rl
+
+
+@pytest.mark.parametrize("K", [1, 33, 2048])
+def test_sparse_fp8_decode_shaped(cpa, K):
+    """FP8 E4M3 cache with per-token scales: one query per request, tile-exact,
+    ragged and long lists (2,048 entries: several splits plus the merge)."""
+    N, L = 4, 5000
+    rng, qb, codes, sc = _fp8_inputs(N, N, L, 300 + K)
+    idx = np.stack([rng.choice(L, K, replace=False) for _ in range(N)]).astype(np.int32)
+    o, l, ro, rl = _run_fp8(cpa, qb, codes, sc, idx, 1 / 24)
+    H.check_lowp(o, l, ro, rl, f"sparse fp8 K={K}")
+
+
+def test_sparse_fp8_ragged_padding_and_shared_requests(cpa):
+    """FP8: five queries on three requests (rows shared through L2), counts
+    0, 1, 33, 100 and 64, padding entries (-1, Lmax, a huge value) and a
+    first tile that is all padding."""
+    N, B, L, K = 5, 3, 300, 100
+    rng, qb, codes, sc = _fp8_inputs(N, B, L, 12)
+    idx = np.stack([rng.choice(L, K, replace=False) for _ in range(N)]).astype(np.int32)
+    idx[1, 5] = -1
+    idx[2, 7] = L
+    idx[4, 0] = 2 ** 30
+    idx[3, :32] = -3
+    req = np.array([2, 0, 1, 1, 0], np.int32)
+    n_idx = np.array([0, 1, 33, 100, 64], np.int32)
+    o, l, ro, rl = _run_fp8(cpa, qb, codes, sc, idx, 1 / 24, n_idx=n_idx, req=req)
+    H.check_lowp(o, l, ro, rl, "sparse fp8 ragged")
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+
+
+def test_sparse_fp8_full_list_matches_fp8_decode(cpa):
+    """Listing every row of a request in order is the FP8 dense decode."""
+    N, L = 2, 777
+    rng, qb, codes, sc = _fp8_inputs(N, N, L, 6)
+    idx = np.tile(np.arange(L, dtype=np.int32), (N, 1))
+    o, l = cpa.attn_sparse_mla(H.bf16_tensor(qb), H.u8_tensor(codes), H.i32_tensor(idx), 1 / 24,
+                               kv_scale=H.f32_tensor(sc))
+    od, ld = cpa.attn_decode_shard(H.bf16_tensor(qb), H.u8_tensor(codes), None, H.i32_tensor([0, 0]),
+                                   H.i32_tensor([L, L]), L, 1 / 24, kv_scale=H.f32_tensor(sc))
+    _sync()
+    ro, rl = att.decode_shard(formats.bf16_bits_to_f64(qb), codes, [0, 0], [L, L], 1 / 24, dv=512,
+                              decode=formats.e4m3_to_f64, kv_scale=sc)
+    H.check_lowp(H.host(o), H.host(l), ro, rl, "sparse fp8 full list")
+    H.check_lowp(H.host(od), H.host(ld), ro, rl, "fp8 dense decode")
