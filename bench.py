@@ -53,13 +53,17 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # they were measured at; after any change the field is null until re-measured.
 TRAFFIC = {
     # profiles/prefill_gqa_zigzag_16k_c4_rank1.md
-    "prefill_gqa_kernel": dict(digest="81b1083652492a8d", fetch_kib=67673.6, write_kib=33792.7,
-                               fetch_scale=1.99994, write_scale=1.0,
-                               fetch_bytes=138591435, write_bytes=34603733),
+    "prefill_gqa_kernel": dict(digest="430ae3ec42fd765b", fetch_kib=67683.4, write_kib=33792.5,
+                              fetch_scale=1.99994, write_scale=1.0,
+                              fetch_bytes=138611445, write_bytes=34603520),
     # profiles/decode_mla_b64_h64_ctx131072_c8.md
-    "decode_mla_kernel<bf16>": dict(digest="7c6e7b0beed0a69e", fetch_kib=599183.0, write_kib=32833.1,
-                                    fetch_scale=1.99994, write_scale=1.0,
-                                    fetch_bytes=1227089957, write_bytes=33621060),
+    "decode_mla_kernel<bf16>": dict(digest="9f32b9aa1f4d02d0", fetch_kib=599186.4, write_kib=32833.1,
+                                   fetch_scale=1.99994, write_scale=1.0,
+                                   fetch_bytes=1227096933, write_bytes=33621094),
+    # profiles/decode_gqa_b8_h32_kv8_ctx131072_c8.md
+    "decode_gqa_kernel<bf16>": dict(digest="103ea9ce126df465", fetch_kib=262384.9, write_kib=520.0,
+                                   fetch_scale=1.99994, write_scale=1.0,
+                                   fetch_bytes=537348154, write_bytes=532480),
 }
 
 
@@ -74,7 +78,8 @@ def _src_digest(files):
 
 KERNEL_SOURCES = {
     "prefill_gqa_kernel": ("prefill.hip", "lds_dma.h"),
-    "decode_mla_kernel<bf16>": ("decode_mla.hip", "mla_core.h", "mla_ws.h", "lds_dma.h"),
+    "decode_mla_kernel<bf16>": ("decode_mla.hip", "mla_core.h", "mla_ws.h", "lds_dma.h", "wave_ops.h"),
+    "decode_gqa_kernel<bf16>": ("decode_gqa.hip", "lds_dma.h", "wave_ops.h"),
 }
 
 
@@ -922,7 +927,13 @@ def main():
         log("[bench] split-KV GQA decode (serving shape, bf16 and FP8) and config 1 (fp32) ...")
         g = bench_gqa_decode(cpa, torch, max(3, args.steps // 2), args.warmup, args.warmup_ms)
         rnd = lambda d: {k: round(v, 4) if isinstance(v, float) else v for k, v in d.items()}
-        line["decode_gqa"] = {"workload": g["workload"], "unit": "GB/s", "bf16": rnd(g["bf16"]), "fp8": rnd(g["fp8"])}
+        line["decode_gqa"] = {"workload": g["workload"], "unit": "GB/s", "bf16": rnd(g["bf16"]), "fp8": rnd(g["fp8"]),
+                              "roofline": {
+                                  "kernel": "decode_gqa_kernel (bf16 cache)", "bound": "hbm",
+                                  "achieved": round(g["bf16"]["launch_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(g["bf16"]["launch_gbs"] / PEAK_HBM_GBS, 4),
+                                  "traffic": traffic("decode_gqa_kernel<bf16>")[0],
+                                  "traffic_detail": traffic("decode_gqa_kernel<bf16>")[1]}}
         c1 = bench_decode_config1(cpa, torch, synth, max(3, args.steps // 2), args.warmup, args.warmup_ms)
         line["decode_config1"] = {k: (rnd(v) if isinstance(v, dict) else v) for k, v in c1.items()}
         log(f"[bench] GQA decode bf16 {g['bf16']['gbs']:.0f} GB/s/step, fp8 {g['fp8']['gbs']:.0f} GB/s/step; "
