@@ -71,8 +71,16 @@ struct Lds {
   int stage_mask;  // stages - 1 (a power of two: kStages for ranges, fewer for index lists)
 };
 
-// Swizzle of row r: the physical unit of logical unit u is u ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return ((r >> 2) & 1) | ((((r >> 3) ^ (r >> 4)) & 1) << 1); }
+// Swizzle of row r: the physical unit of logical unit u is u ^ swz(r). Rows
+// are 144 words long, so row r starts at bank 16 (r & 3). A 16-byte read is
+// served 16 lanes at a time (lanes 4p..4p+3 of each group of 16): the K reads
+// of rows 4p..4p+3 at units 2g + h then fill all 64 banks when bit 0 of the
+// swizzle follows bit 0 of the row. An 8-byte read is served 32 lanes at a
+// time: the rope reads (16 consecutive rows, one unit) and the transposing
+// value reads (rows 4g + (0..3) and 16 + 4g + (0..3), one unit) need the
+// swizzle to be one-to-one over bits 2 and 3, and over bits 2 and 4, of the
+// row; bit 0 takes r0 ^ r2 and bit 1 takes r3 ^ r4.
+__device__ __forceinline__ int swz(int r) { return ((r ^ (r >> 2)) & 1) | ((((r >> 3) ^ (r >> 4)) & 1) << 1); }
 
 __device__ __forceinline__ int unit_off(int r, int u) { return r * kRowBytes + 16 * (u ^ swz(r)); }
 
