@@ -20,7 +20,8 @@ Each function states the passage of the source pages it writes out:
 * the vLLM "Decode Context Parallelism" post, section 4 (contiguous token
   chunks per GPU) and 5.3 (MLA: one latent vector shared by all heads);
 * "DeepSeek-V4 Attention Inference Systems" notes, section 5 (the exact
-  combine in max / sum / unnormalised-output form).
+  combine in max / sum / unnormalised-output form), sections 1 and 9.1
+  (caches read through page tables of fixed-size logical blocks).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against page facts, closed forms, library routines or brute force; see each

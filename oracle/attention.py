@@ -22,6 +22,9 @@ Definitions written out here:
 * Merge -- *Long Context* 3.3: ``lse = logsumexp_c lse_c``,
   ``scale_c = exp(lse_c - lse)``, ``O = sum_c scale_c * O_c``; exact apart
   from the order of additions (3.3; DeepSeek-V4 notes, section 5).
+* Paged cache -- DeepSeek-V4 notes, 1 and 9.1: a request's cache is read
+  through a block table of fixed-size logical blocks mapped to physical pages
+  (``paged_rows``, ``decode_shard_paged``).
 * Merge in statistics form -- DeepSeek-V4 notes, section 5: per shard
   ``m_p = max s``, ``l_p = sum exp(s - m_p)``, ``u_p = sum exp(s - m_p) v``;
   globally ``m = max m_p``, ``Z = sum e^(m_p - m) l_p``,
@@ -37,7 +40,10 @@ Pins (``tests/test_oracle_attention.py``): the two-GPU example of
 float64 ``scaled_dot_product_attention(is_causal=True)`` for C = 1; union of
 all ranks' outputs equals unsharded attention; merged split-KV equals
 unsharded attention; single-key and equal-score closed forms; the two merge
-forms agree.
+forms agree. Paged decode (``tests/test_oracle_paged.py``): a hand-written
+row mapping; shuffled pages equal the contiguous cache (GQA, MLA FP8 with
+per-row scales); unreferenced pages unread; shared prefix pages; invalid
+entries read page 0; page size 1 and one page per request.
 """
 
 import numpy as np
@@ -174,6 +180,55 @@ def decode_shard(q, kcache, begin, end, scale, vcache=None, dv=None, decode=None
             o, lse = attend(q[b, h], keys[:, h // G, :], vals[:, h // G, :], scale)
             O[b, h] = o
             L[b, h] = lse
+    return O, L
+
+
+def paged_rows(block_table, page_size, n_pages, positions):
+    """Pool rows of a request's logical cache positions under a page table.
+
+    DeepSeek-V4 notes, 1 (vLLM maps fixed-size logical blocks of a request's
+    cache into physical pages) and 9.1 (decode keeps the cache paged and reads
+    it through the table). Reading taken: logical position t lies in logical
+    block t // page_size at offset t % page_size; the block's table entry names
+    the physical page, and the row is page * page_size + offset. A table entry
+    outside [0, n_pages) is read as page 0 (the library's contract for an
+    invalid entry: an in-bounds read, not a fault; the pages say nothing).
+    """
+    t = np.asarray(positions, dtype=np.int64)
+    pages = np.asarray(block_table, dtype=np.int64)[t // page_size]
+    pages = np.where((pages >= 0) & (pages < n_pages), pages, 0)
+    return pages * page_size + t % page_size
+
+
+def decode_shard_paged(q, kpool, block_table, page_size, begin, end, scale, vpool=None, dv=None,
+                       decode=None, kv_scale=None, batch=None):
+    """Split-KV decode over a paged cache: ``decode_shard`` of each request on
+    the pool rows its block table names (``paged_rows``).
+
+    q           [B, Hq, Dqk]
+    kpool       [n_pages * page_size, Hkv, Dqk]   rows of all pages
+    vpool       same shape with Dv, or None for MLA (v = k[..., :dv])
+    kv_scale    [n_pages * page_size] per-row scale, or None
+    block_table [B, n_blocks]: logical block j of request b -> physical page
+    begin, end  [B] logical positions, end <= n_blocks * page_size
+    Returns O [B, Hq, Dv], LSE [B, Hq] as ``decode_shard``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, _ = q.shape
+    n_pages = kpool.shape[0] // page_size
+    Dv = dv if vpool is None else vpool.shape[-1]
+    O = np.zeros((B, Hq, Dv))
+    L = np.full((B, Hq), _NEG_INF)
+    for b in (range(B) if batch is None else batch):
+        s0, s1 = int(begin[b]), int(end[b])
+        if s1 <= s0:
+            continue
+        rows = paged_rows(block_table[b], page_size, n_pages, np.arange(s0, s1))
+        kc = kpool[rows][None]
+        vc = None if vpool is None else vpool[rows][None]
+        sc = None if kv_scale is None else np.asarray(kv_scale)[rows][None]
+        o, lse = decode_shard(q[b:b + 1], kc, [0], [s1 - s0], scale, vcache=vc, dv=dv, decode=decode, kv_scale=sc)
+        O[b], L[b] = o[0], lse[0]
     return O, L
 
 

@@ -251,3 +251,17 @@ def config(k):
         c["new_len"] = [int(x) for x in agentic_lengths(5, 16)]
         c["prefix_len"] = [0] * 16
     return c
+
+
+def page_table(config, stream, B, n_blocks, n_pages, shared=0):
+    """Seeded block table [B, n_blocks] int32 of distinct physical page ids
+    drawn from range(n_pages) (a random permutation), except that the first
+    `shared` logical blocks of every request name the same pages as request
+    0's (a shared prefix). Needs n_pages >= shared + B * (n_blocks - shared)."""
+    need = shared + B * (n_blocks - shared)
+    assert n_pages >= need
+    perm = rng(config, stream).permutation(n_pages)[:need].astype(np.int32)
+    table = np.empty((B, n_blocks), np.int32)
+    table[:, :shared] = perm[:shared]
+    table[:, shared:] = perm[shared:].reshape(B, n_blocks - shared)
+    return table

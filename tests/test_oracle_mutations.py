@@ -27,9 +27,21 @@ SPARSE = ["tests/test_oracle_sparse.py"]
 TOPK = ["tests/test_oracle_topk.py"]
 MQ = ["tests/test_oracle_multi_query.py"]
 RR = ["tests/test_oracle_round_robin.py"]
+PAGED = ["tests/test_oracle_paged.py"]
 
 # (name, oracle file, text to replace, replacement, pin files to run)
 MUTATIONS = [
+    ("paged row offset from the block index", "attention.py",
+     "return pages * page_size + t % page_size", "return pages * page_size + t // page_size", PAGED),
+    ("paged block from the offset", "attention.py",
+     "pages = np.asarray(block_table, dtype=np.int64)[t // page_size]",
+     "pages = np.asarray(block_table, dtype=np.int64)[(t // page_size) % len(block_table)][::-1]", PAGED),
+    ("paged invalid entry read as the last page", "attention.py",
+     "pages = np.where((pages >= 0) & (pages < n_pages), pages, 0)",
+     "pages = np.where((pages >= 0) & (pages < n_pages), pages, n_pages - 1)", PAGED),
+    ("paged scales read at the logical position", "attention.py",
+     "sc = None if kv_scale is None else np.asarray(kv_scale)[rows][None]",
+     "sc = None if kv_scale is None else np.asarray(kv_scale)[s0:s1][None]", PAGED),
     ("causal mask drops the diagonal", "attention.py",
      "visible = np.arange(p_hi + 1)[None, :] <= pos[:, None]",
      "visible = np.arange(p_hi + 1)[None, :] < pos[:, None]", ATT),
