@@ -269,8 +269,10 @@ def bench_decode(cpa, torch, synth, steps, warmup, warmup_ms):
                          launch_ms=lm, launch_gbs=launch_bytes / (lm * 1e-3) / 1e9,
                          launch_bytes=launch_bytes)
     res["sparse_fp8"] = bench_sparse(cpa, torch, synth, c, cache_fp8, steps, warmup, warmup_ms, kv_scale=sc)
+    res["paged_fp8"] = bench_paged(cpa, torch, synth, c, q, cache_fp8, sc, steps, warmup, warmup_ms)
     del cache_fp8, sc
     torch.cuda.empty_cache()
+    res["paged_bf16"] = bench_paged(cpa, torch, synth, c, q, cache_bf16, None, steps, warmup, warmup_ms)
     res["round_robin_bf16"] = bench_round_robin(cpa, torch, c, q, cache_bf16, steps, warmup, warmup_ms)
     res["multi_query_bf16"] = bench_multi_query(cpa, torch, synth, c, cache_bf16, 4, steps, warmup, warmup_ms)
     res["sparse_bf16"] = bench_sparse(cpa, torch, synth, c, cache_bf16, steps, warmup, warmup_ms)
@@ -430,6 +432,60 @@ def bench_multi_query(cpa, torch, synth, c, cache, Q, steps, warmup, warmup_ms):
     flops = keys * H * 2 * (576 + 512)
     return dict(Q=Q, gpu_ms_per_step=ms, gbs=step_bytes / (ms * 1e-3) / 1e9, algorithmic_bytes=step_bytes,
                 tflops=flops / (ms * 1e-3) / 1e12, flops=flops)
+
+
+PAGE_SIZE = 64
+
+
+def bench_paged(cpa, torch, synth, c, q, cache, kvs, steps, warmup, warmup_ms):
+    """The MLA decode step (C partial launches + merge) over a paged cache:
+    the same rows as `cache`, in 64-token pages of one pool placed in a
+    seeded random order (block table [B, L / 64])."""
+    B, L, C, H = c["B"], c["L"], c["C"], c["Hq"]
+    dev = cache.device
+    ps = PAGE_SIZE
+    nb = L // ps
+    table = torch.from_numpy(synth.page_table(3, 9, B, nb, B * nb)).to(dev)
+    dst = table.reshape(-1).long()
+    pool = torch.empty((B * nb, ps) + tuple(cache.shape[2:]), dtype=cache.dtype, device=dev)
+    pool[dst] = cache.reshape((B * nb, ps) + tuple(cache.shape[2:]))
+    pool = pool.reshape((B * L,) + tuple(cache.shape[2:]))
+    spool = None
+    if kvs is not None:
+        spool = torch.empty((B * nb, ps), dtype=kvs.dtype, device=dev)
+        spool[dst] = kvs.reshape(B * nb, ps)
+        spool = spool.reshape(-1)
+    shards = cpa.cp_decode_shards(L, C)
+    begins = [torch.full((B,), s0, dtype=torch.int32, device=dev) for s0, _ in shards]
+    ends = [torch.full((B,), s1, dtype=torch.int32, device=dev) for _, s1 in shards]
+    max_len = max(s1 - s0 for s0, s1 in shards)
+    po = torch.empty((C, B, H, 512), dtype=torch.float32, device=dev)
+    pl = torch.empty((C, B, H), dtype=torch.float32, device=dev)
+    mo = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    ml = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, cpa.attn_decode_paged_workspace_size(B, H, 512, max_len, ps)), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        for i in range(C):
+            cpa.attn_decode_shard_paged(q, pool, None, table, ps, begins[i], ends[i], max_len, c["scale"],
+                                        kv_scale=spool, o_part=po[i], lse_part=pl[i], workspace=ws)
+        cpa.attn_merge_states(po, pl, out=mo, lse_out=ml)
+
+    _warm(torch, step, warmup, warmup_ms)
+    sev = _events(torch, 1)[0]
+    sev[0].record()
+    for _ in range(steps):
+        step()
+    sev[1].record()
+    torch.cuda.synchronize()
+    ms = sev[0].elapsed_time(sev[1]) / steps
+    entry = 576 * 2 if kvs is None else 576 + 4
+    step_bytes = (B * L * entry + C * B * nb * 4 + C * B * H * 576 * 2 + 2 * C * B * H * (512 + 1) * 4
+                  + B * H * (512 + 1) * 4)
+    del pool, spool
+    torch.cuda.empty_cache()
+    return dict(page_size=ps, gpu_ms_per_step=ms, gbs=step_bytes / (ms * 1e-3) / 1e9, algorithmic_bytes=step_bytes)
 
 
 def bench_round_robin(cpa, torch, c, q, cache, steps, warmup, warmup_ms):
@@ -901,7 +957,10 @@ def main():
                 "traffic_detail": traffic("decode_mla_kernel<bf16>")[1],
             },
             "round_robin_bf16": {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["round_robin_bf16"].items()},
-            "frac_of_hbm_peak_step": {k: round(dec[k]["gbs"] / PEAK_HBM_GBS, 4) for k in ("bf16", "fp8", "round_robin_bf16")},
+            "paged": {k: {kk: round(vv, 4) if isinstance(vv, float) else vv for kk, vv in dec[k].items()}
+                      for k in ("paged_bf16", "paged_fp8")},
+            "frac_of_hbm_peak_step": {k: round(dec[k]["gbs"] / PEAK_HBM_GBS, 4)
+                                      for k in ("bf16", "fp8", "round_robin_bf16", "paged_bf16", "paged_fp8")},
             "topk_split_index": {k: round(v, 4) if isinstance(v, float) else v for k, v in dec["topk"].items()},
             "sparse_bf16": {k: dict({kk: round(vv, 4) if isinstance(vv, float) else vv for kk, vv in v.items()},
                                     frac_of_hbm_peak=round(v["gbs"] / PEAK_HBM_GBS, 4))
@@ -916,6 +975,7 @@ def main():
                 frac_of_bf16_mfma_peak=round(dec["multi_query_bf16"]["tflops"] / PEAK_BF16_TFLOPS, 4)),
         }
         log(f"[bench] decode bf16 {dec['bf16']['gbs']:.0f} GB/s/step, fp8 {dec['fp8']['gbs']:.0f} GB/s/step, "
+            f"paged (64-token pages) bf16 {dec['paged_bf16']['gbs']:.0f}, fp8 {dec['paged_fp8']['gbs']:.0f} GB/s/step, "
             f"round-robin bf16 {dec['round_robin_bf16']['gbs']:.0f} GB/s/step "
             f"(cache write {dec['round_robin_bf16']['cache_write_gbs']:.0f} GB/s), "
             f"multi-query Q=4 {dec['multi_query_bf16']['gbs']:.0f} GB/s/step, "

@@ -58,7 +58,8 @@ SYMBOLS = ("cpa_last_error", "cpa_abi_version", "cp_plan_zigzag", "cp_plan_inter
            "attn_prefill_shard", "attn_decode_workspace_size", "attn_decode_shard", "attn_merge_states",
            "cp_round_robin_slot", "cp_plan_round_robin", "attn_cache_write_round_robin",
            "attn_decode_shard_mq", "cp_plan_multi_query", "attn_sparse_mla_workspace_size", "attn_sparse_mla",
-           "attn_topk_local", "attn_topk_merge", "attn_decode_shard_noalloc")
+           "attn_topk_local", "attn_topk_merge", "attn_decode_shard_noalloc", "attn_decode_paged_workspace_size",
+           "attn_decode_shard_paged")
 
 _lib_handle = None
 
@@ -96,6 +97,15 @@ def lib():
                                                 P(CpaTensor), P(CpaTensor), ctypes.c_void_p]
         L.attn_decode_shard_mq.restype = ctypes.c_int
         L.attn_decode_shard_mq.argtypes = L.attn_decode_shard.argtypes
+        L.attn_decode_paged_workspace_size.restype = ctypes.c_size_t
+        L.attn_decode_paged_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                       ctypes.c_int64, ctypes.c_int32]
+        L.attn_decode_shard_paged.restype = ctypes.c_int
+        L.attn_decode_shard_paged.argtypes = [P(CpaTensor), P(CpaTensor), P(CpaTensor), P(CpaTensor),
+                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                              P(CpaTensor), P(CpaTensor), ctypes.c_void_p, ctypes.c_size_t,
+                                              ctypes.c_void_p]
         L.cp_plan_multi_query.restype = ctypes.c_int
         L.cp_plan_multi_query.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           P(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -325,6 +335,50 @@ def attn_decode_shard(q, kcache, vcache, kv_begin, kv_end, max_shard_len, softma
                                    ctypes.c_void_p(kv_begin.data_ptr()), ctypes.c_void_p(kv_end.data_ptr()),
                                    int(max_shard_len), float(softmax_scale), ctypes.byref(do), ctypes.byref(dl),
                                    ctypes.c_void_p(ws_ptr), ws_bytes, _stream(stream)))
+    return o_part, lse_part
+
+
+def attn_decode_paged_workspace_size(batch, n_heads_q, head_dim_v, max_shard_len, page_size):
+    return int(lib().attn_decode_paged_workspace_size(int(batch), int(n_heads_q), int(head_dim_v),
+                                                      int(max_shard_len), int(page_size)))
+
+
+def attn_decode_shard_paged(q, kpool, vpool, block_table, page_size, kv_begin, kv_end, max_shard_len,
+                            softmax_scale, kv_scale=None, o_part=None, lse_part=None, workspace=None, stream=None,
+                            kpool_dtype=None):
+    """Split-KV decode over a paged cache. q [B, Hq, Dqk]; kpool [n_pages *
+    page_size, Hkv, Dqk] (torch.uint8 = FP8 E4M3 bytes, then kv_scale [rows]
+    f32); vpool the same with Dv, or None (MLA); block_table int32 device
+    tensor [B, n_blocks] (logical block -> physical page); kv_begin / kv_end
+    int32 device tensors [B] of logical positions. Returns (o_part, lse_part)."""
+    torch = _torch()
+    B, Hq = q.shape[0], q.shape[1]
+    Dv = vpool.shape[-1] if vpool is not None else 512
+    if o_part is None:
+        o_part = torch.empty((B, Hq, Dv), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_paged_workspace_size(B, Hq, Dv, max_shard_len, page_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    dq, dk = tensor_desc(q), tensor_desc(kpool, kpool_dtype)
+    dv = tensor_desc(vpool) if vpool is not None else None
+    ds = tensor_desc(kv_scale) if kv_scale is not None else None
+    do, dl = tensor_desc(o_part), tensor_desc(lse_part)
+    for t in (kv_begin, kv_end):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != q.device:
+            raise TypeError("kv_begin / kv_end must be contiguous int32 tensors on the query's device")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1 \
+            or block_table.device != q.device:
+        raise TypeError("block_table must be an int32 [B, n_blocks] tensor (rows contiguous) on the query's device")
+    _check(lib().attn_decode_shard_paged(ctypes.byref(dq), ctypes.byref(dk), _ptr(dv), _ptr(ds),
+                                         ctypes.c_void_p(block_table.data_ptr()), int(block_table.stride(0)),
+                                         int(block_table.shape[1]), int(page_size),
+                                         ctypes.c_void_p(kv_begin.data_ptr()), ctypes.c_void_p(kv_end.data_ptr()),
+                                         int(max_shard_len), float(softmax_scale), ctypes.byref(do),
+                                         ctypes.byref(dl), ctypes.c_void_p(ws_ptr), ws_bytes, _stream(stream)))
     return o_part, lse_part
 
 

@@ -138,7 +138,7 @@ size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Dv, int nsplit) {
 
 extern "C" const char* cpa_last_error(void) { return cpa::g_err.c_str(); }
 
-extern "C" int32_t cpa_abi_version(void) { return 101; }
+extern "C" int32_t cpa_abi_version(void) { return 102; }
 
 // --------------------------------------------------------------------- merge
 
@@ -194,6 +194,23 @@ extern "C" cpa_status attn_merge_states(int32_t n_states, const cpa_tensor* o_pa
 
 // -------------------------------------------------------------------- decode
 
+// Paged cache (attn_decode_shard_paged): the block table, its row stride,
+// log2 of the page size and the pool's page count.
+struct Paging {
+  const int32_t* table;
+  int64_t stride;
+  int32_t shift, n_pages;
+};
+
+// Splits of a paged decode: at least `ns`, and enough that a split of the
+// longest range touches at most kPageCap pages (a split of n tokens touches
+// at most (n - 1) / page + 2 pages).
+int paged_nsplit(int ns, int64_t max_len, int shift) {
+  const int64_t per = ((int64_t)(cpa::kPageCap - 2)) << shift;  // tokens per split that always fit
+  const int64_t need = (max_len + per - 1) / per;
+  return (int)std::max<int64_t>(ns, need);
+}
+
 namespace {
 
 // rows = query rows of the launch (requests x query rows per request)
@@ -219,7 +236,7 @@ cpa_status decode_impl(const cpa_tensor* q, int64_t Q, int64_t q_q, const cpa_te
                        const cpa_tensor* vcache, const cpa_tensor* kv_scale, const int32_t* kv_begin,
                        const int32_t* kv_end, int64_t max_shard_len, float softmax_scale, const cpa_tensor* o_part,
                        const cpa_tensor* lse_part, void* workspace, size_t ws_bytes, void* stream,
-                       bool lib_scratch = false) {
+                       bool lib_scratch = false, const Paging* pg = nullptr) {
   CPA_TRY(check_tensor(q, "decode q", (1u << CPA_F32) | (1u << CPA_BF16), 3));
   CPA_TRY(check_tensor(kcache, "decode kcache", (1u << CPA_F32) | (1u << CPA_BF16) | (1u << CPA_FP8_E4M3), 4));
   CPA_TRY(check_tensor(o_part, "decode o_part", 1u << CPA_F32, 3));
@@ -283,6 +300,13 @@ cpa_status decode_impl(const cpa_tensor* q, int64_t Q, int64_t q_q, const cpa_te
 
   DecodePlan p{};
   CPA_TRY(decode_plan(R, Hq, kcache, vcache, max_shard_len, &p));
+  if (pg != nullptr) {
+    p.nsplit = paged_nsplit(p.nsplit, max_shard_len, pg->shift);
+    if (p.nsplit > (p.mla ? 64 : 256))
+      return fail(CPA_E_UNSUPPORTED,
+                  "decode_paged: %lld tokens per shard need more than %d pages per split at page size %d",
+                  (long long)max_shard_len, cpa::kPageCap, 1 << pg->shift);
+  }
   // workgroups: (row, split) for MLA, (request, kv head, head block, split)
   // for GQA, times the Q rows, rounded up to whole groups of 8 units
   const int64_t units = p.mla ? B * p.nsplit : B * Hkv * p.head_blocks * p.nsplit;
@@ -342,6 +366,12 @@ cpa_status decode_impl(const cpa_tensor* q, int64_t Q, int64_t q_q, const cpa_te
     a.scale_log2 = softmax_scale * kLog2e;
     a.Q = (int32_t)Q;
     a.q_q = q_q;
+    if (pg != nullptr) {
+      a.block_table = pg->table;
+      a.bt_b = pg->stride;
+      a.page_shift = pg->shift;
+      a.n_pages = pg->n_pages;
+    }
     err = cpa::launch_decode_mla(a, stream);
   } else {
     cpa::DecodeGqaArgs a{};
@@ -372,6 +402,12 @@ cpa_status decode_impl(const cpa_tensor* q, int64_t Q, int64_t q_q, const cpa_te
     a.scale_log2 = softmax_scale * kLog2e;
     a.Q = (int32_t)Q;
     a.q_q = q_q;
+    if (pg != nullptr) {
+      a.block_table = pg->table;
+      a.bt_b = pg->stride;
+      a.page_shift = pg->shift;
+      a.n_pages = pg->n_pages;
+    }
     err = cpa::launch_decode_gqa(a, stream);
   }
   CPA_TRY(hip_status(err, "decode launch"));
@@ -427,6 +463,66 @@ extern "C" cpa_status attn_decode_shard_noalloc(const cpa_tensor* q, const cpa_t
   CPA_TRY(hip_status(cpa::noalloc_scratch(&scratch), "decode_noalloc: scratch lookup"));
   return decode_impl(q, 1, 0, kcache, vcache, kv_scale, kv_begin, kv_end, max_shard_len, softmax_scale, o_part,
                      lse_part, scratch, cpa::kNoAllocScratchBytes, stream, true);
+}
+
+extern "C" size_t attn_decode_paged_workspace_size(int64_t batch, int32_t n_heads_q, int32_t head_dim_v,
+                                                   int64_t max_shard_len, int32_t page_size) {
+  if (page_size < 1 || (page_size & (page_size - 1)) || page_size > (1 << 20)) return 0;
+  const int shift = __builtin_ctz((unsigned)page_size);
+  const int ns = head_dim_v == 512 ? mla_nsplit(batch, max_shard_len) : gqa_nsplit(batch, max_shard_len);
+  return decode_ws_bytes(batch, n_heads_q, head_dim_v, paged_nsplit(ns, max_shard_len, shift));
+}
+
+extern "C" cpa_status attn_decode_shard_paged(const cpa_tensor* q, const cpa_tensor* kpool, const cpa_tensor* vpool,
+                                              const cpa_tensor* kv_scale, const int32_t* block_table,
+                                              int64_t bt_stride, int64_t n_blocks, int32_t page_size,
+                                              const int32_t* kv_begin, const int32_t* kv_end,
+                                              int64_t max_shard_len, float softmax_scale,
+                                              const cpa_tensor* o_part, const cpa_tensor* lse_part,
+                                              void* workspace, size_t ws_bytes, void* stream) {
+  cpa::clear_error();
+  const unsigned kv_types = (1u << CPA_F32) | (1u << CPA_BF16) | (1u << CPA_FP8_E4M3);
+  CPA_TRY(check_tensor(q, "decode_paged q", (1u << CPA_F32) | (1u << CPA_BF16), 3));
+  CPA_TRY(check_tensor(kpool, "decode_paged kpool", kv_types, 3));
+  if (page_size < 1 || (page_size & (page_size - 1)) || page_size > (1 << 20))
+    return fail(CPA_E_INVAL, "decode_paged: page_size %d must be a power of two in [1, 2^20]", page_size);
+  const int64_t B = q->shape[0], rows = kpool->shape[0];
+  if (rows % page_size) return fail(CPA_E_INVAL, "decode_paged: kpool rows %lld not a multiple of page_size", (long long)rows);
+  const int64_t n_pages = rows / page_size;
+  if (n_pages > INT32_MAX) return fail(CPA_E_INVAL, "decode_paged: too many pages");
+  if (n_blocks < 1 || n_blocks * (int64_t)page_size > INT32_MAX)
+    return fail(CPA_E_INVAL, "decode_paged: n_blocks must be >= 1 with n_blocks * page_size < 2^31");
+  if (bt_stride < n_blocks) return fail(CPA_E_INVAL, "decode_paged: block table row stride < n_blocks");
+  if (B > 0 && block_table == nullptr) return fail(CPA_E_INVAL, "decode_paged: block_table is NULL");
+  // [B, Lmax = n_blocks * page_size, Hkv, D] views whose request stride is 0:
+  // every request reads the pool, through its own table row
+  auto view4 = [&](const cpa_tensor* t) {
+    cpa_tensor v = *t;
+    v.ndim = 4;
+    v.shape[0] = B, v.shape[1] = n_blocks * page_size, v.shape[2] = t->shape[1], v.shape[3] = t->shape[2];
+    v.stride[0] = 0, v.stride[1] = t->stride[0], v.stride[2] = t->stride[1], v.stride[3] = t->stride[2];
+    return v;
+  };
+  const cpa_tensor kv = view4(kpool);
+  cpa_tensor vv{};
+  if (vpool != nullptr) {
+    CPA_TRY(check_tensor(vpool, "decode_paged vpool", kv_types, 3));
+    if (vpool->shape[0] != rows) return fail(CPA_E_INVAL, "decode_paged: vpool rows differ from kpool");
+    vv = view4(vpool);
+  }
+  cpa_tensor sv{};
+  const bool has_scale = kv_scale != nullptr && kv_scale->data != nullptr;
+  if (has_scale) {
+    CPA_TRY(check_tensor(kv_scale, "decode_paged kv_scale", 1u << CPA_F32, 1, 0));
+    if (kv_scale->shape[0] != rows) return fail(CPA_E_INVAL, "decode_paged: kv_scale must be f32 [pool rows]");
+    sv = *kv_scale;
+    sv.ndim = 2;
+    sv.shape[0] = B, sv.shape[1] = n_blocks * page_size;
+    sv.stride[0] = 0, sv.stride[1] = kv_scale->stride[0];
+  }
+  const Paging pg{block_table, bt_stride, __builtin_ctz((unsigned)page_size), (int32_t)n_pages};
+  return decode_impl(q, 1, 0, &kv, vpool != nullptr ? &vv : nullptr, has_scale ? &sv : nullptr, kv_begin, kv_end,
+                     max_shard_len, softmax_scale, o_part, lse_part, workspace, ws_bytes, stream, false, &pg);
 }
 
 extern "C" cpa_status attn_decode_shard_mq(const cpa_tensor* q, const cpa_tensor* kcache,

@@ -45,6 +45,7 @@
 
 #include "internal.h"
 #include "lds_dma.h"
+#include "paged.h"
 #include "wave_ops.h"
 
 namespace {
@@ -162,10 +163,12 @@ __device__ __forceinline__ int tile_off(int t, int u) {
   return t * kRow + 16 * (u ^ swz<kRow>(t));
 }
 
-template <int DT, int D>
+// kPaged: K, V and the scales are pools read through a block table (paged.h).
+template <int DT, int D, bool kPaged>
 __global__ __launch_bounds__(kMaxThreads) void decode_gqa_kernel(cpa::DecodeGqaArgs a) {
   using C = Cfg<DT, D>;
   __shared__ __attribute__((aligned(16))) char smem[C::lds];
+  __shared__ int pages_s[kPaged ? cpa::kPageCap : 1];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
 
@@ -197,6 +200,12 @@ __global__ __launch_bounds__(kMaxThreads) void decode_gqa_kernel(cpa::DecodeGqaA
   const int nt_all = (int)((t1 - t0 + kTok - 1) / kTok);
   constexpr int kWaves = C::waves;
   const int nt = nt_all > w ? (nt_all - w + kWaves - 1) / kWaves : 0;  // tiles w, w + waves, ...
+  cpa::PagedRows pr{};
+  if constexpr (kPaged) {
+    pr = cpa::load_pages(pages_s, a.block_table + (int64_t)b * a.bt_b, t0, t1, a.page_shift, a.n_pages, tid,
+                         kWaves * 64);
+    __syncthreads();
+  }
 
   // ---- this wavefront's loads ----
   const uint64_t kb = cpa::uniform_ptr(reinterpret_cast<const char*>(a.k) +
@@ -231,11 +240,25 @@ __global__ __launch_bounds__(kMaxThreads) void decode_gqa_kernel(cpa::DecodeGqaA
       const int q = 1024 * i + 16 * lane, t = q / C::row;
       const uint32_t src = 16u * (uint32_t)(((q % C::row) >> 4) ^ swz<C::row>(t));
       const uint32_t rr = (uint32_t)min(t, lim);
-      dma(kbase, rr * kt + src, kdst + 1024 * i);
-      dma(vbase, rr * vt + src, vdst + 1024 * i);
+      if constexpr (kPaged) {  // every row its own pool row: 64-bit addresses
+        const uint64_t prow = (uint64_t)pr.row(tok0 + rr);
+        const char* ks = reinterpret_cast<const char*>(kb + prow * kt + src);
+        const char* vs = reinterpret_cast<const char*>(vb + prow * vt + src);
+        if (reuse) {
+          cpa::lds_dma16<Policy::kReuse>(ks, kdst + 1024 * i);
+          cpa::lds_dma16<Policy::kReuse>(vs, vdst + 1024 * i);
+        } else {
+          cpa::lds_dma16<Policy::kStream>(ks, kdst + 1024 * i);
+          cpa::lds_dma16<Policy::kStream>(vs, vdst + 1024 * i);
+        }
+      } else {
+        dma(kbase, rr * kt + src, kdst + 1024 * i);
+        dma(vbase, rr * vt + src, vdst + 1024 * i);
+      }
     }
     if constexpr (DT == kFp8) {
-      const float* sp = a.kv_scale + (int64_t)b * a.s_b + (tok0 + min(lane, lim)) * a.s_t;
+      const int64_t srow = kPaged ? pr.row(tok0 + min(lane, lim)) : tok0 + min(lane, lim);
+      const float* sp = a.kv_scale + (int64_t)b * a.s_b + srow * a.s_t;
       const uint32_t sdst = __builtin_amdgcn_readfirstlane(cpa::lds_addr(st + 2 * C::kv_bytes));
       if (lane < kTok) {
         if (reuse) cpa::lds_dma4<Policy::kReuse>(sp, sdst);
@@ -465,15 +488,28 @@ __global__ __launch_bounds__(kMaxThreads) void decode_gqa_kernel(cpa::DecodeGqaA
   }
 }
 
-template <int DT>
+template <int DT, bool kPaged>
 int launch_dt(const cpa::DecodeGqaArgs& a, dim3 grid, hipStream_t st) {
   switch (a.D) {
-    case 64: hipLaunchKernelGGL((decode_gqa_kernel<DT, 64>), grid, dim3(Cfg<DT, 64>::threads), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((decode_gqa_kernel<DT, 128>), grid, dim3(Cfg<DT, 128>::threads), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((decode_gqa_kernel<DT, 256>), grid, dim3(Cfg<DT, 256>::threads), 0, st, a); break;
+    case 64:
+      hipLaunchKernelGGL((decode_gqa_kernel<DT, 64, kPaged>), grid, dim3(Cfg<DT, 64>::threads), 0, st, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL((decode_gqa_kernel<DT, 128, kPaged>), grid, dim3(Cfg<DT, 128>::threads), 0, st, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL((decode_gqa_kernel<DT, 256, kPaged>), grid, dim3(Cfg<DT, 256>::threads), 0, st, a);
+      break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
+}
+
+template <bool kPaged>
+int launch_paging(const cpa::DecodeGqaArgs& a, dim3 grid, hipStream_t st) {
+  if (a.kv_dtype == CPA_F32) return launch_dt<kF32, kPaged>(a, grid, st);
+  if (a.kv_dtype == CPA_BF16) return launch_dt<kBf16, kPaged>(a, grid, st);
+  return launch_dt<kFp8, kPaged>(a, grid, st);
 }
 
 }  // namespace
@@ -486,9 +522,7 @@ int launch_decode_gqa(const DecodeGqaArgs& a, void* stream) {
   const int64_t units = (int64_t)a.B * a.Hkv * gqa_head_blocks(a.Hq / a.Hkv) * a.nsplit;
   const dim3 grid((unsigned)((units + 7) / 8 * 8 * a.Q));
   hipStream_t st = (hipStream_t)stream;
-  if (a.kv_dtype == CPA_F32) return launch_dt<kF32>(a, grid, st);
-  if (a.kv_dtype == CPA_BF16) return launch_dt<kBf16>(a, grid, st);
-  return launch_dt<kFp8>(a, grid, st);
+  return a.block_table != nullptr ? launch_paging<true>(a, grid, st) : launch_paging<false>(a, grid, st);
 }
 
 }  // namespace cpa

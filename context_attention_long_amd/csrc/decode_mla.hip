@@ -29,7 +29,8 @@ using namespace cpa::mla;
 // (mla_fp8.h). kP: kStream (one query row per request: every cache byte is
 // read once) or kReuse (several query rows read each tile through the
 // shared L2).
-template <bool kFp8, cpa::Policy kP>
+// kPaged: the cache is a pool read through a block table (paged.h).
+template <bool kFp8, cpa::Policy kP, bool kPaged>
 __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::DecodeMlaArgs a) {
   constexpr int kTileLds = kFp8 ? f8::kStages * f8::kTileBytes : kSmemBytes;
   constexpr int kScaleLds = kFp8 ? f8::kStages * f8::kScaleSlot : 16;
@@ -37,6 +38,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
   __shared__ __attribute__((aligned(16))) char ssc[kScaleLds];
   __shared__ __attribute__((aligned(16))) char plds[2 * kH * kPRowBytes];
   __shared__ float alpha_s[2 * kH], lsum_s[kH];
+  __shared__ int pages_s[kPaged ? cpa::kPageCap : 1];
 
   const int u = (int)(blockIdx.x / (8 * a.Q)) * 8 + (int)(blockIdx.x % 8);
   const int k = (int)(blockIdx.x / 8) % a.Q;
@@ -53,6 +55,16 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
   end = end < beg ? beg : (end > a.Lmax ? a.Lmax : end);
   const int64_t len = end - beg;
   const Tiles T(beg + len * split / a.nsplit, beg + len * (split + 1) / a.nsplit, (unsigned)u * 2654435761u >> 7);
+  cpa::PagedRows pr{};
+  if constexpr (kPaged) {
+    pr = cpa::load_pages(pages_s, a.block_table + (int64_t)b * a.bt_b, T.t0, T.t1, a.page_shift, a.n_pages, tid,
+                         kWsThreads);
+    __syncthreads();
+  }
+  auto rows_of = [&]() {
+    if constexpr (kPaged) return pr;
+    else return cpa::LinearRows{};
+  };
 
   if (qk_role) {
     const uint16_t* qhead = a.q + (int64_t)b * a.q_b + (int64_t)k * a.q_q + (int64_t)(16 * w + c) * a.q_h;
@@ -84,11 +96,12 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
     if constexpr (kFp8) {
       const f8::Lds S{smem, ssc, plds, alpha_s, lsum_s, f8::kStages - 1};
       f8::ws_pv<kP>(T, reinterpret_cast<const uint8_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t,
-                    a.kv_scale + (int64_t)b * a.s_b, a.s_t, tid - 256, w, g, c, f8::bases(w, g, c), oacc, S);
+                    a.kv_scale + (int64_t)b * a.s_b, a.s_t, tid - 256, w, g, c, f8::bases(w, g, c), oacc, S,
+                    rows_of());
     } else {
       const Lds S{smem, plds, alpha_s, lsum_s};
       ws_pv<kP>(T, reinterpret_cast<const uint16_t*>(a.cache) + (int64_t)b * a.c_b, a.c_t, tid - 256, w, g, c,
-                lds_bases(w, g, c), oacc, S);
+                lds_bases(w, g, c), oacc, S, rows_of());
     }
     __syncthreads();
 #pragma unroll
@@ -111,14 +124,19 @@ int launch_decode_mla(const DecodeMlaArgs& a, void* stream) {
   const dim3 grid((unsigned)(((int64_t)a.B * a.nsplit + 7) / 8 * 8 * a.Q));
   constexpr auto kS = Policy::kStream, kR = Policy::kReuse;
   hipStream_t st = (hipStream_t)stream;
-  if (a.fp8 && a.Q == 1)
-    hipLaunchKernelGGL((decode_mla_ws_kernel<true, kS>), grid, dim3(kWsThreads), 0, st, a);
+  if (a.block_table != nullptr) {  // one query row per request (the host checks)
+    if (a.fp8)
+      hipLaunchKernelGGL((decode_mla_ws_kernel<true, kS, true>), grid, dim3(kWsThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_mla_ws_kernel<false, kS, true>), grid, dim3(kWsThreads), 0, st, a);
+  } else if (a.fp8 && a.Q == 1)
+    hipLaunchKernelGGL((decode_mla_ws_kernel<true, kS, false>), grid, dim3(kWsThreads), 0, st, a);
   else if (a.fp8)
-    hipLaunchKernelGGL((decode_mla_ws_kernel<true, kR>), grid, dim3(kWsThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mla_ws_kernel<true, kR, false>), grid, dim3(kWsThreads), 0, st, a);
   else if (a.Q == 1)
-    hipLaunchKernelGGL((decode_mla_ws_kernel<false, kS>), grid, dim3(kWsThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mla_ws_kernel<false, kS, false>), grid, dim3(kWsThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_mla_ws_kernel<false, kR>), grid, dim3(kWsThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_mla_ws_kernel<false, kR, false>), grid, dim3(kWsThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -52,6 +52,12 @@ struct DecodeGqaArgs {
   // output row b*Q + k (strides o_b / l_b then step one row).
   int32_t Q;
   int64_t q_q;
+  // Paged cache when block_table is set (paged.h): token t of request b is
+  // pool row block_table[b*bt_b + (t >> page_shift)] * 2^page_shift +
+  // (t & (2^page_shift - 1)); k_b, v_b and s_b are then 0.
+  const int32_t* block_table;
+  int64_t bt_b;
+  int32_t page_shift, n_pages;
 };
 
 struct DecodeMlaArgs {
@@ -73,6 +79,10 @@ struct DecodeMlaArgs {
   // Q query rows per request, as in DecodeGqaArgs.
   int32_t Q;
   int64_t q_q;
+  // Paged cache, as in DecodeGqaArgs (c_b and s_b are then 0).
+  const int32_t* block_table;
+  int64_t bt_b;
+  int32_t page_shift, n_pages;
 };
 
 struct SparseMlaArgs {
@@ -155,6 +165,10 @@ struct CacheWriteArgs {
 // one decode launch, e.g. 4 splits of 64 requests x 64 heads x 512 dims
 // (33.6 MB) fit; 2 splits of 200 requests (52 MB) do not.
 constexpr size_t kNoAllocScratchBytes = (size_t)48 << 20;
+
+// Paged decode: page ids of one split a workgroup keeps in LDS. The host
+// picks enough splits that no split touches more pages.
+constexpr int kPageCap = 1024;
 // Device address of the current device's scratch array (looked up once per
 // device); returns hipSuccess or the lookup's error.
 int noalloc_scratch(void** ptr);

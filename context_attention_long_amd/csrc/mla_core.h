@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "lds_dma.h"
+#include "paged.h"
 #include "wave_ops.h"
 
 namespace cpa {

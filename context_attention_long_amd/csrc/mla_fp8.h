@@ -30,7 +30,7 @@
 //    dimension for 8 tokens -- and four v_cvt_scalef32_pk_bf16_fp8 turn the
 //    8 codes into the bf16 operand. No bf16 copy of the tile is written.
 //  * rows are XOR-swizzled in 16-byte units inside aligned groups of four;
-//    the swizzle (bits r2 and r3 ^ r4 of the row) keeps the three read
+//    the swizzle (bits r0 ^ r2 and r3 ^ r4 of the row) keeps the three read
 //    patterns (QK 16-byte reads, rope 8-byte reads, transposing V reads)
 //    free of LDS bank conflicts.
 #pragma once
@@ -295,10 +295,12 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
 // tp + 256 k (k < 4); then waves 0 and 1 load units 1024 + tp and waves 2
 // and 3 the tile's scales (both the same 64 values, one 4-byte load per
 // lane; entries past the tile re-read its last token).
-template <Policy kPol>
+// rows.row(t) is the cache row (and scale entry) of token t: the token
+// itself, or its row in a paged pool (every load then takes its own address).
+template <Policy kPol, typename Rows = LinearRows>
 __device__ __forceinline__ void ws_pv(const Tiles& T, const uint8_t* base, int64_t c_t, const float* sbase,
                                       int64_t s_t, int tp, int w, int g, int c, const Bases& L,
-                                      f32x4 (&oacc)[kMv][4], const Lds& S) {
+                                      f32x4 (&oacc)[kMv][4], const Lds& S, const Rows& rows = Rows{}) {
   if (T.ntiles <= 0) return;
   const int lane = tp & 63;
   const bool unit5 = w < 2;  // wave-uniform
@@ -316,25 +318,25 @@ __device__ __forceinline__ void ws_pv(const Tiles& T, const uint8_t* base, int64
   auto scale_load = [&](int i) {
     const int64_t tok0 = T.t0 + (int64_t)T.phys(i) * kBN;
     const int lim = (int)min((int64_t)(kBN - 1), T.t1 - 1 - tok0);
-    lds_dma4<kPol>(sbase + (tok0 + min(lane, lim)) * s_t,
+    lds_dma4<kPol>(sbase + rows.row(tok0 + min(lane, lim)) * s_t,
                    __builtin_amdgcn_readfirstlane(lds_addr(scale_slot(S, i))));
   };
   // all loads of tile i at once (prologue; the ragged last tile)
   auto issue = [&](int i) {
     const int64_t tok0 = T.t0 + (int64_t)T.phys(i) * kBN;
-    if (tok0 + kBN <= T.t1) {
-      const uint64_t tb = sb + (uint64_t)(tok0 * c_t);
+    if (tok0 + kBN <= T.t1 && rows.consecutive(tok0, tok0 + kBN - 1)) {  // one base, per-thread offsets
+      const uint64_t tb = Rows::kLinear ? sb + (uint64_t)(tok0 * c_t) : uniform_ptr(base + rows.row(tok0) * c_t);
 #pragma unroll
       for (int k = 0; k < 4; ++k) lds_dma16_s<kPol>(tb, toff[k], dst(i, k));
       if (unit5) lds_dma16_s<kPol>(tb, toff[4], dst(i, 4));
     } else {
-      const int lim = (int)(T.t1 - 1 - tok0);
+      const int lim = (int)min((int64_t)(kBN - 1), T.t1 - 1 - tok0);
 #pragma unroll
       for (int k = 0; k < kLoads; ++k) {
         if (k == 4 && !unit5) break;
         const int U = k < 4 ? tp + kThreads * k : 4 * kThreads + tp;
         const int r = U / kRowUnits, pu = U % kRowUnits;
-        lds_dma16<kPol>(base + (tok0 + min(r, lim)) * c_t + 16 * (pu ^ swz(r)), dst(i, k));
+        lds_dma16<kPol>(base + rows.row(tok0 + min(r, lim)) * c_t + 16 * (pu ^ swz(r)), dst(i, k));
       }
     }
     if (!unit5) scale_load(i);
@@ -385,9 +387,10 @@ __device__ __forceinline__ void ws_pv(const Tiles& T, const uint8_t* base, int64
     // loads are spread over the first m-steps, a ragged one issued at once
     const int nt = i + kStages - 1;
     const int64_t nxt0 = T.t0 + (int64_t)T.phys(nt < n ? nt : 0) * kBN;
-    const bool spread = (nt < n) && (nxt0 + kBN <= T.t1);
+    const bool spread = (nt < n) && (nxt0 + kBN <= T.t1) && rows.consecutive(nxt0, nxt0 + kBN - 1);
     if (nt < n && !spread) issue(nt);
-    const uint64_t ntb = sb + (uint64_t)(nxt0 * c_t);
+    const uint64_t ntb =
+        Rows::kLinear ? sb + (uint64_t)(nxt0 * c_t) : uniform_ptr(base + (spread ? rows.row(nxt0) : 0) * c_t);
     pv(i, [&](int m) {
       if (spread) {
         if (m < 4) lds_dma16_s<kPol>(ntb, toff[m], dst(nt, m));

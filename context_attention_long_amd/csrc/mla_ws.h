@@ -93,11 +93,14 @@ __device__ __forceinline__ void ws_qk(const Tiles& T, int w, int g, int c, const
   __syncthreads();  // P of the last tile visible
 }
 
-// PV role, bf16 cache rows `base` (token 0) with `c_t` elements per token.
-// tp = thread index inside the role (0..255).
-template <Policy P>
+// PV role, bf16 cache rows `base` (row 0) with `c_t` elements per row;
+// rows.row(t) is the row of token t (the token itself, or its row in a paged
+// pool: every load then takes its own address). tp = thread index inside the
+// role (0..255).
+template <Policy P, typename Rows = LinearRows>
 __device__ __forceinline__ void ws_pv(const Tiles& T, const uint16_t* base, int64_t c_t, int tp, int w, int g, int c,
-                                      const LdsBases& L, f32x4 (&oacc)[kMv][4], const Lds& S) {
+                                      const LdsBases& L, f32x4 (&oacc)[kMv][4], const Lds& S,
+                                      const Rows& rows = Rows{}) {
   if (T.ntiles <= 0) return;
   uint32_t toff[kLdChunks];  // byte offset of this thread's chunks inside a full tile
 #pragma unroll
@@ -110,8 +113,8 @@ __device__ __forceinline__ void ws_pv(const Tiles& T, const uint16_t* base, int6
   auto issue = [&](int i) {  // all loads of tile i at once
     const int64_t tok0 = T.t0 + (int64_t)T.phys(i) * kBN;
     char* dst0 = stage(i);
-    if (tok0 + kBN <= T.t1) {
-      const uint16_t* tb = base + tok0 * c_t;
+    if (tok0 + kBN <= T.t1 && rows.consecutive(tok0, tok0 + kBN - 1)) {  // one base, per-thread offsets
+      const uint16_t* tb = base + rows.row(tok0) * c_t;
 #pragma unroll
       for (int k = 0; k < kLdChunks; ++k) lds_dma16_sbase<P>(tb, toff[k], lds_addr(dst0 + kThreads * k * 16));
     } else {
@@ -120,7 +123,7 @@ __device__ __forceinline__ void ws_pv(const Tiles& T, const uint16_t* base, int6
         const int Pc = tp + kThreads * k;
         const int row = Pc / kRowChunks, pc = Pc % kRowChunks;
         const int64_t tok = min(tok0 + row, T.t1 - 1);
-        lds_dma16<P>(base + tok * c_t + swz(row, pc) * 8, lds_addr(dst0 + kThreads * k * 16));
+        lds_dma16<P>(base + rows.row(tok) * c_t + swz(row, pc) * 8, lds_addr(dst0 + kThreads * k * 16));
       }
     }
   };
@@ -173,9 +176,9 @@ __device__ __forceinline__ void ws_pv(const Tiles& T, const uint16_t* base, int6
     // spread over the m-steps (two at the first), the clamped last tile is
     // issued at once
     const int64_t nxt0 = T.t0 + (int64_t)T.phys(i + 3 < n ? i + 3 : 0) * kBN;
-    const bool spread = (i + 3 < n) && (nxt0 + kBN <= T.t1);
+    const bool spread = (i + 3 < n) && (nxt0 + kBN <= T.t1) && rows.consecutive(nxt0, nxt0 + kBN - 1);
     if (i + 3 < n && !spread) issue(i + 3);
-    const uint64_t ntb = uniform_ptr(base + nxt0 * c_t);
+    const uint64_t ntb = uniform_ptr(base + (Rows::kLinear ? nxt0 : (spread ? rows.row(nxt0) : 0)) * c_t);
     const uint32_t ndst = __builtin_amdgcn_readfirstlane(lds_addr(stage(i + 3)));
     pv(i, [&](int m) {
       if (spread) {

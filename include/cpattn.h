@@ -218,6 +218,40 @@ cpa_status attn_decode_shard_noalloc(const cpa_tensor* q, const cpa_tensor* kcac
                                      const cpa_tensor* lse_part, void* stream);
 
 /*
+ * Split-KV decode over a paged cache ("DeepSeek-V4 Attention Inference
+ * Systems", 1: logical cache blocks of a fixed size mapped to physical pages
+ * of shared pools; 9.1: decode reads the paged cache directly). The same
+ * computation and results as attn_decode_shard, where token t of request b
+ * (t a logical position in [kv_begin[b], kv_end[b])) is the pool row
+ *   block_table[b * bt_stride + t / page_size] * page_size + t % page_size.
+ *   q           [B, Hq, Dqk]                   bf16 or f32, as attn_decode_shard
+ *   kpool       [n_pages * page_size, Hkv, Dqk] f32, bf16 or FP8 E4M3
+ *   vpool       [n_pages * page_size, Hkv, Dv]  same dtype, or NULL for MLA
+ *   kv_scale    [n_pages * page_size] f32       per-row scale, FP8 only
+ *   block_table DEVICE int32, B rows of n_blocks entries bt_stride apart;
+ *               an entry outside [0, n_pages) is read as page 0
+ *   page_size   a power of two in [1, 2^20]; logical positions are clamped
+ *               to [0, n_blocks * page_size]
+ *   max_shard_len  must bound kv_end - kv_begin here (it sizes the splits,
+ *               and a split keeps the ids of the pages it touches on chip;
+ *               a longer range is read in bounds but its result is not
+ *               defined)
+ *   workspace   at least attn_decode_paged_workspace_size(...) bytes
+ * Supported shapes and dtypes as attn_decode_shard (one query row per
+ * request). Pages can be shared between requests (e.g. a common prefix).
+ * CPA_E_UNSUPPORTED when the pages of max_shard_len tokens do not fit the
+ * split limit (1024 pages per split; 64 splits MLA, 256 GQA).
+ */
+size_t attn_decode_paged_workspace_size(int64_t batch, int32_t n_heads_q, int32_t head_dim_v,
+                                        int64_t max_shard_len, int32_t page_size);
+cpa_status attn_decode_shard_paged(const cpa_tensor* q, const cpa_tensor* kpool, const cpa_tensor* vpool,
+                                   const cpa_tensor* kv_scale, const int32_t* block_table, int64_t bt_stride,
+                                   int64_t n_blocks, int32_t page_size, const int32_t* kv_begin,
+                                   const int32_t* kv_end, int64_t max_shard_len, float softmax_scale,
+                                   const cpa_tensor* o_part, const cpa_tensor* lse_part, void* workspace,
+                                   size_t ws_bytes, void* stream);
+
+/*
  * Multi-query split-KV decode (speculative / MTP decode under decode CP:
  * Long Context 9 lists it; DeepSeek-V4 notes, 11, sweeps the query/spec
  * width 1, 2, 4, 8). Request b has Q query rows; row k attends cache rows

@@ -80,6 +80,19 @@ def _poisoning(m):
                     a["workspace"] = _ff(need, q.device)
         return fill
 
+    def paged(a):
+        q, vp = a["q"], a["vpool"]
+        B, hq = q.shape[0], q.shape[1]
+        dv = vp.shape[-1] if vp is not None else 512
+        if a["o_part"] is None:
+            a["o_part"] = _nan((B, hq, dv), f32, q.device)
+        if a["lse_part"] is None:
+            a["lse_part"] = _nan((B, hq), f32, q.device)
+        if a["workspace"] is None:
+            need = m.attn_decode_paged_workspace_size(B, hq, dv, a["max_shard_len"], a["page_size"])
+            if need > 0:
+                a["workspace"] = _ff(need, q.device)
+
     def sparse(a):
         q, idx = a["q"], a["idx"]
         N = q.shape[0]
@@ -104,6 +117,7 @@ def _poisoning(m):
         "attn_prefill_shard": wrap(m.attn_prefill_shard, prefill),
         "attn_decode_shard": wrap(m.attn_decode_shard, decode(False)),
         "attn_decode_shard_mq": wrap(m.attn_decode_shard_mq, decode(True)),
+        "attn_decode_shard_paged": wrap(m.attn_decode_shard_paged, paged),
         "attn_sparse_mla": wrap(m.attn_sparse_mla, sparse),
         "attn_merge_states": wrap(m.attn_merge_states, merge),
     }

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = cpa.lib()
     for n in _declared():
         assert hasattr(L, n), n
-    assert L.cpa_abi_version() == 101
+    assert L.cpa_abi_version() == 102
 
 
 def test_nm_exports_are_c_symbols():
