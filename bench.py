@@ -78,8 +78,8 @@ def _src_digest(files):
 
 KERNEL_SOURCES = {
     "prefill_gqa_kernel": ("prefill.hip", "lds_dma.h"),
-    "decode_mla_kernel<bf16>": ("decode_mla.hip", "mla_core.h", "mla_ws.h", "lds_dma.h", "wave_ops.h"),
-    "decode_gqa_kernel<bf16>": ("decode_gqa.hip", "lds_dma.h", "wave_ops.h"),
+    "decode_mla_kernel<bf16>": ("decode_mla.hip", "mla_core.h", "mla_ws.h", "lds_dma.h", "wave_ops.h", "paged.h"),
+    "decode_gqa_kernel<bf16>": ("decode_gqa.hip", "lds_dma.h", "wave_ops.h", "paged.h"),
 }
 
 
