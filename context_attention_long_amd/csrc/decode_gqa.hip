@@ -144,17 +144,26 @@ __device__ __forceinline__ void wait_vm(int n) {
 }
 
 // Tiles are row-major (16 rows of `kRow` bytes) with the 16-byte units of
-// row t stored XOR-swizzled: slot u of the row holds unit u ^ swz(t), the
-// swizzle a bit permutation of the row index chosen for the row size so that
-// both operand reads touch every LDS bank the minimum number of times (64
-// banks x 4 bytes; a model of every read pattern of every dtype and head
-// dim was checked): the QK reads (one unit of 16 rows per 16 lanes) and
-// the transposing V reads (2 units of 8 rows per 32 lanes). Each load
-// instruction still fetches whole rows (1 KB of consecutive row bytes).
+// row t stored XOR-swizzled: slot u of the row holds unit u ^ swz(t). The
+// LDS has 64 banks of 4 bytes; a 16-byte read is served in four passes of
+// 16 lanes (lanes 4p..4p+3 of each 16-lane group), an 8-byte read (plain or
+// transposing) in two passes of 32 consecutive lanes. The swizzle is a
+// linear map of the row's low bits chosen so that every pass of every
+// operand read touches each bank once, for every dtype and head dim: the QK
+// reads (16-byte: rows 4p..4p+3, units 4k + g; FP8 8-byte: 16 rows, one
+// unit half), the bf16 transposing V reads (rows 0..7 or 8..15, two units),
+// the FP8 ones (8 rows, units n and n + 1) and the f32 V reads (16-byte:
+// rows 4g + e, units 16N + c). Rows of 256 bytes or more start on bank 0,
+// so the pattern is fixed by bits 0-3 of the slot: bits 2-3 = row bits 0-1
+// xor 2-3 (four distinct over four consecutive rows and over rows e + 4g),
+// bit 1 = row bit 2, bit 0 = row bit 3. Each load instruction still fetches
+// whole rows (1 KB of consecutive row bytes).
 template <int kRow>
 __device__ __forceinline__ int swz(int t) {
-  if constexpr (kRow >= 256) return ((t & 7) << 1) | ((t >> 3) & 1);  // 16 units per 256 B
-  else if constexpr (kRow == 128) return (t & 2) | (((t >> 2) & 1) << 2) | ((t >> 3) & 1);  // 2 rows per 256 B
+  if constexpr (kRow >= 256)  // 16 units per 256 B
+    return ((t >> 3) & 1) | (((t >> 2) & 1) << 1) | (((t ^ (t >> 2)) & 1) << 2) | ((((t >> 1) ^ (t >> 3)) & 1) << 3);
+  else if constexpr (kRow == 128)  // 2 rows per 256 B
+    return ((t >> 3) & 1) | (((t >> 2) & 1) << 1) | (((t >> 1) & 1) << 2);
   else return (((t >> 2) & 1) << 1) | ((t >> 3) & 1);  // 64-byte rows: 4 rows per 256 B
 }
 
@@ -180,12 +189,15 @@ __global__ __launch_bounds__(kMaxThreads) void decode_gqa_kernel(cpa::DecodeGqaA
   const int k = (int)(bx / 8 % a.Q);
   const int64_t n_units = (int64_t)a.B * a.Hkv * HB * a.nsplit;
   if (u >= n_units) return;
-  const int split = (int)(u % a.nsplit);
-  int64_t rest = u / a.nsplit;
+  // the kv head varies fastest: the workgroups of one (request, head block,
+  // split) -- consecutive block indices, on different XCDs -- read the same
+  // tokens' rows of the Hkv heads at the same time
+  const int kvh = (int)(u % a.Hkv);
+  int64_t rest = u / a.Hkv;
+  const int split = (int)(rest % a.nsplit);
+  rest /= a.nsplit;
   const int hb = (int)(rest % HB);
-  rest /= HB;
-  const int kvh = (int)(rest % a.Hkv);
-  const int b = (int)(rest / a.Hkv);
+  const int b = (int)(rest / HB);
   const int row = b * a.Q + k;
   const int h0 = kvh * G + hb * kHB;      // first query head of the block
   const int nh = min(kHB, G - hb * kHB);  // heads in the block
