@@ -90,7 +90,7 @@ struct Cfg {
   static constexpr int vm = 2 * loads + (DT == kFp8 ? 1 : 0);  // vector-memory ops per tile
   static constexpr int nacc = D / 16;             // O^T accumulators (16 dims x 16 heads each)
   static constexpr int stage_lds = waves * stages * tile;
-  static constexpr int merge_lds = waves * kHB * (D + 2) * 4;
+  static constexpr int merge_lds = waves * kHB * (D + 3) * 4;  // O rows of D + 1, max, sum
   static constexpr int lds = stage_lds > merge_lds ? stage_lds : merge_lds;
   static_assert(loads >= 1 && kv_bytes % 1024 == 0, "whole wave-wide loads per tile part");
   static_assert((stages - 1) * vm <= 63, "vmcnt range");
@@ -146,24 +146,22 @@ __device__ __forceinline__ void wait_vm(int n) {
 // Tiles are row-major (16 rows of `kRow` bytes) with the 16-byte units of
 // row t stored XOR-swizzled: slot u of the row holds unit u ^ swz(t). The
 // LDS has 64 banks of 4 bytes; a 16-byte read is served in four passes of
-// 16 lanes (lanes 4p..4p+3 of each 16-lane group), an 8-byte read (plain or
-// transposing) in two passes of 32 consecutive lanes. The swizzle is a
-// linear map of the row's low bits chosen so that every pass of every
-// operand read touches each bank once, for every dtype and head dim: the QK
-// reads (16-byte: rows 4p..4p+3, units 4k + g; FP8 8-byte: 16 rows, one
-// unit half), the bf16 transposing V reads (rows 0..7 or 8..15, two units),
-// the FP8 ones (8 rows, units n and n + 1) and the f32 V reads (16-byte:
-// rows 4g + e, units 16N + c). Rows of 256 bytes or more start on bank 0,
-// so the pattern is fixed by bits 0-3 of the slot: bits 2-3 = row bits 0-1
-// xor 2-3 (four distinct over four consecutive rows and over rows e + 4g),
-// bit 1 = row bit 2, bit 0 = row bit 3. Each load instruction still fetches
-// whole rows (1 KB of consecutive row bytes).
+// 16 lanes (the lanes of one half-wave whose quad index (lane >> 2) & 7 has
+// even, or odd, parity; measured), an 8-byte read (plain or transposing) in
+// two passes of 32 consecutive lanes. The swizzle is a linear map of the
+// row's low bits, found by search over every pass of every operand read of
+// the nine dtype / head-dim tiles, under which each pass touches each bank
+// once: the QK reads (16-byte: rows c, units 4k + g; FP8 8-byte: 16 rows,
+// one unit half), the bf16 transposing V reads (rows 0..7 or 8..15, two
+// units), the FP8 ones (8 rows, units n and n + 1) and the f32 V reads
+// (16-byte: rows 4g + e, units 16N + c). Each load instruction still
+// fetches whole rows (1 KB of consecutive row bytes).
 template <int kRow>
 __device__ __forceinline__ int swz(int t) {
-  if constexpr (kRow >= 256)  // 16 units per 256 B
-    return ((t >> 3) & 1) | (((t >> 2) & 1) << 1) | (((t ^ (t >> 2)) & 1) << 2) | ((((t >> 1) ^ (t >> 3)) & 1) << 3);
-  else if constexpr (kRow == 128)  // 2 rows per 256 B
-    return ((t >> 3) & 1) | (((t >> 2) & 1) << 1) | (((t >> 1) & 1) << 2);
+  if constexpr (kRow >= 256)  // 16 units per 256 B: t0, t1, t0 ^ t2, t2 ^ t3
+    return (t & 1) | (t & 2) | (((t ^ (t >> 2)) & 1) << 2) | ((((t >> 2) ^ (t >> 3)) & 1) << 3);
+  else if constexpr (kRow == 128)  // 2 rows per 256 B: t1, t1 ^ t2, t1 ^ t3
+    return ((t >> 1) & 1) | ((((t >> 1) ^ (t >> 2)) & 1) << 1) | ((((t >> 1) ^ (t >> 3)) & 1) << 2);
   else return (((t >> 2) & 1) << 1) | ((t >> 3) & 1);  // 64-byte rows: 4 rows per 256 B
 }
 
@@ -461,8 +459,11 @@ __global__ __launch_bounds__(kMaxThreads) void decode_gqa_kernel(cpa::DecodeGqaA
   // ---- merge the wavefronts' states and write the split's result ----
   const float l_run = sum4_rows(l_part);
   __syncthreads();  // every wavefront is done with its stages
-  float* mo = reinterpret_cast<float*>(smem);       // [waves][16][D] unnormalised O
-  float* mm = mo + kWaves * kHB * D;                // [waves][16] running max
+  // [waves][16][D + 1] unnormalised O: the odd row stride puts the 16 heads
+  // a store instruction writes in different banks
+  constexpr int Dp = D + 1;
+  float* mo = reinterpret_cast<float*>(smem);
+  float* mm = mo + kWaves * kHB * Dp;               // [waves][16] running max
   float* ml = mm + kWaves * kHB;                    // [waves][16] running sum
 #pragma unroll
   for (int n = 0; n < C::nacc; ++n)
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(kMaxThreads) void decode_gqa_kernel(cpa::DecodeGqaA
     for (int r = 0; r < 4; ++r) {
       // lane (head c, group g) holds O^T rows 4g + r of accumulator n
       const int d = DT == kF32 ? 64 * (n / 4) + 4 * (4 * g + r) + (n % 4) : 16 * n + 4 * g + r;
-      mo[(w * kHB + c) * D + d] = acc[n][r];
+      mo[(w * kHB + c) * Dp + d] = acc[n][r];
     }
   if (g == 0) {
     mm[w * kHB + c] = m_run;
@@ -488,7 +489,7 @@ __global__ __launch_bounds__(kMaxThreads) void decode_gqa_kernel(cpa::DecodeGqaA
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) {
         const float f = __builtin_amdgcn_exp2f(mm[v * kHB + h] - M);  // 0 for an empty wavefront
-        num += f * mo[(v * kHB + h) * D + d];
+        num += f * mo[(v * kHB + h) * Dp + d];
         den += f * ml[v * kHB + h];
       }
     }
