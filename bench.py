@@ -53,17 +53,17 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # they were measured at; after any change the field is null until re-measured.
 TRAFFIC = {
     # profiles/prefill_gqa_zigzag_16k_c4_rank1.md
-    "prefill_gqa_kernel": dict(digest="430ae3ec42fd765b", fetch_kib=67683.4, write_kib=33792.5,
+    "prefill_gqa_kernel": dict(digest="430ae3ec42fd765b", fetch_kib=67611.6, write_kib=33792.3,
                               fetch_scale=1.99994, write_scale=1.0,
-                              fetch_bytes=138611445, write_bytes=34603520),
+                              fetch_bytes=138464403, write_bytes=34603315),
     # profiles/decode_mla_b64_h64_ctx131072_c8.md
-    "decode_mla_kernel<bf16>": dict(digest="9f32b9aa1f4d02d0", fetch_kib=599186.4, write_kib=32833.1,
+    "decode_mla_kernel<bf16>": dict(digest="cf4ccc50b8bbe02e", fetch_kib=599185.9, write_kib=32832.6,
                                    fetch_scale=1.99994, write_scale=1.0,
-                                   fetch_bytes=1227096933, write_bytes=33621094),
+                                   fetch_bytes=1227095909, write_bytes=33620582),
     # profiles/decode_gqa_b8_h32_kv8_ctx131072_c8.md
-    "decode_gqa_kernel<bf16>": dict(digest="103ea9ce126df465", fetch_kib=262384.9, write_kib=520.0,
+    "decode_gqa_kernel<bf16>": dict(digest="99ed0efbebf30435", fetch_kib=262291.3, write_kib=520.0,
                                    fetch_scale=1.99994, write_scale=1.0,
-                                   fetch_bytes=537348154, write_bytes=532480),
+                                   fetch_bytes=537156467, write_bytes=532480),
 }
 
 
