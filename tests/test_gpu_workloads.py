@@ -91,6 +91,41 @@ def test_mla_decode_workload(cpa, mla_decode_inputs, fp8):
         print(f"MLA decode fp8={fp8} shard {si} request {b} errors:", e)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_mla_decode_paged_workload(cpa, mla_decode_inputs, fp8):
+    """The MLA decode workload over a paged cache: the same rows in 64-token
+    pages of one pool, placed by a seeded random block table; the 8 shard
+    launches must give results bit-identical to the contiguous launches
+    (whose parity with the oracle test_mla_decode_workload checks)."""
+    import torch
+    c, q, bits, codes, scales = mla_decode_inputs
+    B, L, C = c["B"], c["L"], c["C"]
+    ps = 64
+    nb = L // ps
+    qd = H.bf16_tensor(q)
+    cd = H.u8_tensor(codes) if fp8 else H.bf16_tensor(bits)
+    sd = H.f32_tensor(scales) if fp8 else None
+    table = H.i32_tensor(synth.page_table(3, 9, B, nb, B * nb))
+    dst = table.reshape(-1).long()
+    pool = torch.empty((B * nb, ps) + tuple(cd.shape[2:]), dtype=cd.dtype, device=cd.device)
+    pool[dst] = cd.reshape((B * nb, ps) + tuple(cd.shape[2:]))
+    pool = pool.reshape((B * L,) + tuple(cd.shape[2:]))
+    spool = None
+    if fp8:
+        spool = torch.empty((B * nb, ps), dtype=torch.float32, device=cd.device)
+        spool[dst] = sd.reshape(B * nb, ps)
+        spool = spool.reshape(-1)
+    shards = plans.contiguous_shards(L, C)
+    for i, (s0, s1) in enumerate(shards):
+        beg, end = H.i32_tensor(np.full(B, s0)), H.i32_tensor(np.full(B, s1))
+        o1, l1 = cpa.attn_decode_shard_paged(qd, pool, None, table, ps, beg, end, s1 - s0, c["scale"], kv_scale=spool)
+        o2, l2 = cpa.attn_decode_shard(qd, cd, None, beg, end, s1 - s0, c["scale"], kv_scale=sd)
+        _sync()
+        assert bool(torch.isfinite(o1).all()) and bool(torch.isfinite(l1).all())
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"shard {i}: paged differs from contiguous"
+    print(f"MLA decode paged fp8={fp8}: 8 shards bit-identical to the contiguous cache", flush=True)
+
+
 def test_mla_prefill_zigzag_workload(cpa):
     """MLA zigzag prefill: 64 heads, 576/512, 131072 new tokens after a
     32768-token cached prefix, C=8 (16 blocks of 8192), rank 0's share."""
