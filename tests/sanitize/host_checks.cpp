@@ -242,6 +242,65 @@ static void check_prefill() {
   EXPECT_CALL(attn_prefill_shard(&qm, &lat, nullptr, seg, 2, -1.f, &om, &lm, nullptr), CPA_E_INVAL, false);
 }
 
+// Decode over a paged cache: pools of whole pages, a block table per request.
+static void check_decode_paged(int B, int L, const int32_t* kb, const int32_t* ke, void* ws, size_t big) {
+  const int ps = 64, nb = (L + ps - 1) / ps, n_pages = 2 * B * nb;
+  const int32_t* table = static_cast<const int32_t*>(dev(128));
+  cpa_tensor qm = tensor(CPA_BF16, {B, 64, 576}), pool = tensor(CPA_BF16, {(int64_t)n_pages * ps, 1, 576}),
+             om = tensor(CPA_F32, {B, 64, 512}), lm = tensor(CPA_F32, {B, 64});
+  const size_t need = attn_decode_paged_workspace_size(B, 64, 512, L, ps);
+  CHECK(need > 0 && attn_decode_paged_workspace_size(B, 64, 512, L, 48) == 0);
+  EXPECT_CALL(attn_decode_shard_paged(&qm, &pool, nullptr, nullptr, table, nb, nb, ps, kb, ke, L, 0.05f, &om, &lm, ws,
+                                      need, nullptr),
+              CPA_OK, true);
+  EXPECT_CALL(attn_decode_shard_paged(&qm, &pool, nullptr, nullptr, table, nb, nb, ps, kb, ke, L, 0.05f, &om, &lm, ws,
+                                      4096, nullptr),
+              CPA_E_CAPACITY, false);
+  EXPECT_CALL(attn_decode_shard_paged(&qm, &pool, nullptr, nullptr, table, nb, nb, 48, kb, ke, L, 0.05f, &om, &lm, ws,
+                                      big, nullptr),
+              CPA_E_INVAL, false);  // page size not a power of two
+  cpa_tensor ragged = tensor(CPA_BF16, {(int64_t)n_pages * ps + 5, 1, 576});
+  EXPECT_CALL(attn_decode_shard_paged(&qm, &ragged, nullptr, nullptr, table, nb, nb, ps, kb, ke, L, 0.05f, &om, &lm,
+                                      ws, big, nullptr),
+              CPA_E_INVAL, false);  // pool rows not whole pages
+  EXPECT_CALL(attn_decode_shard_paged(&qm, &pool, nullptr, nullptr, nullptr, nb, nb, ps, kb, ke, L, 0.05f, &om, &lm,
+                                      ws, big, nullptr),
+              CPA_E_INVAL, false);
+  EXPECT_CALL(attn_decode_shard_paged(&qm, &pool, nullptr, nullptr, table, nb - 1, nb, ps, kb, ke, L, 0.05f, &om, &lm,
+                                      ws, big, nullptr),
+              CPA_E_INVAL, false);  // table row stride < n_blocks
+  EXPECT_CALL(attn_decode_shard_paged(&qm, &pool, nullptr, nullptr, table, (int64_t)1 << 26, (int64_t)1 << 26, ps, kb,
+                                      ke, L, 0.05f, &om, &lm, ws, big, nullptr),
+              CPA_E_INVAL, false);  // n_blocks x page size past 2^31
+  EXPECT_CALL(attn_decode_shard_paged(&qm, &pool, nullptr, nullptr, table, nb, nb, ps, kb, ke, (int64_t)nb * ps + 1,
+                                      0.05f, &om, &lm, ws, big, nullptr),
+              CPA_OK, true);  // a bound past the table is allowed: positions clamp to it
+  // 16-token pages: 1022 pages per split cover 16352 tokens, so a
+  // 1.1M-token shard needs more splits than the MLA merge takes
+  const int nb16 = 70000;
+  cpa_tensor pool16 = tensor(CPA_BF16, {(int64_t)nb16 * 16, 1, 576});
+  EXPECT_CALL(attn_decode_shard_paged(&qm, &pool16, nullptr, nullptr, table, nb16, nb16, 16, kb, ke,
+                                      (int64_t)nb16 * 16, 0.05f, &om, &lm, ws, big, nullptr),
+              CPA_E_UNSUPPORTED, false);
+  // FP8 GQA pools with the per-row scale of the pool
+  cpa_tensor q = tensor(CPA_BF16, {B, 32, 128}), kf = tensor(CPA_FP8_E4M3, {(int64_t)n_pages * ps, 8, 128}),
+             vf = tensor(CPA_FP8_E4M3, {(int64_t)n_pages * ps, 8, 128}), o = tensor(CPA_F32, {B, 32, 128}),
+             l = tensor(CPA_F32, {B, 32}), sc = tensor(CPA_F32, {(int64_t)n_pages * ps}),
+             sshort = tensor(CPA_F32, {(int64_t)n_pages * ps - 1}), vshort = tensor(CPA_FP8_E4M3, {(int64_t)ps, 8, 128});
+  EXPECT_CALL(attn_decode_shard_paged(&q, &kf, &vf, &sc, table, nb + 3, nb, ps, kb, ke, L, 0.1f, &o, &l, ws, big,
+                                      nullptr),
+              CPA_OK, true);
+  EXPECT_CALL(attn_decode_shard_paged(&q, &kf, &vf, &sshort, table, nb, nb, ps, kb, ke, L, 0.1f, &o, &l, ws, big,
+                                      nullptr),
+              CPA_E_INVAL, false);
+  EXPECT_CALL(attn_decode_shard_paged(&q, &kf, &vf, nullptr, table, nb, nb, ps, kb, ke, L, 0.1f, &o, &l, ws, big,
+                                      nullptr),
+              CPA_E_INVAL, false);  // FP8 without its scales
+  EXPECT_CALL(attn_decode_shard_paged(&q, &kf, &vshort, &sc, table, nb, nb, ps, kb, ke, L, 0.1f, &o, &l, ws, big,
+                                      nullptr),
+              CPA_E_INVAL, false);  // value pool of another size
+}
+
 static void check_decode() {
   const int B = 6, L = 5000;
   const size_t big = (size_t)1 << 34;  // workspace bytes (never touched)
@@ -325,6 +384,7 @@ static void check_decode() {
              lq0 = tensor(CPA_F32, {B, 65, 64});
   EXPECT_CALL(attn_decode_shard_mq(&qq0, &lat, nullptr, nullptr, kb, ke, L, 0.05f, &oq0, &lq0, ws, big, nullptr),
               CPA_E_INVAL, false);  // Q > 64
+  check_decode_paged(B, L, kb, ke, ws, big);
 }
 
 static void check_sparse_topk_cachewrite() {
