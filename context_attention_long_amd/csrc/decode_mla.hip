@@ -40,8 +40,22 @@ __global__ __launch_bounds__(kWsThreads, 1) void decode_mla_ws_kernel(cpa::Decod
   __shared__ float alpha_s[2 * kH], lsum_s[kH];
   __shared__ int pages_s[kPaged ? cpa::kPageCap : 1];
 
-  const int u = (int)(blockIdx.x / (8 * a.Q)) * 8 + (int)(blockIdx.x % 8);
-  const int k = (int)(blockIdx.x / 8) % a.Q;
+  // Work unit u = b * nsplit + split and query row k. Block indices are
+  // dealt round-robin to the 8 XCDs (index mod 8). When the requests divide
+  // evenly over the XCDs, every workgroup of request b runs on XCD b mod 8:
+  // its query rows come from HBM once and reach the other splits through
+  // that XCD's L2. Otherwise consecutive units go to consecutive XCDs. The Q
+  // rows of one unit are 8 indices apart either way (one XCD, so they share
+  // the unit's tiles in L2).
+  int u, k;
+  if (a.B % 8 == 0 && a.nsplit > 1) {
+    const int x = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8), per = a.nsplit * a.Q;
+    u = ((j / per) * 8 + x) * a.nsplit + (j % per) / a.Q;
+    k = (j % per) % a.Q;
+  } else {
+    u = (int)(blockIdx.x / (8 * a.Q)) * 8 + (int)(blockIdx.x % 8);
+    k = (int)(blockIdx.x / 8) % a.Q;
+  }
   if (u >= a.B * a.nsplit) return;
   const int split = u % a.nsplit;
   const int b = u / a.nsplit;

@@ -34,8 +34,19 @@ __global__ __launch_bounds__(kWsThreads, 1) void sparse_mla_kernel(cpa::SparseMl
   __shared__ float alpha_s[2 * kH], lsum_s[kH];
   const Lds S{smem, plds, alpha_s, lsum_s};
 
-  const int split = (int)(blockIdx.x % a.nsplit);
-  const int n = (int)(blockIdx.x / a.nsplit);
+  // (query, split) of this workgroup. Block indices are dealt round-robin
+  // to the 8 XCDs (index mod 8); when the queries divide evenly over them,
+  // the splits of query n all run on XCD n mod 8, so its bf16 query rows
+  // come from HBM once and reach the other splits through that XCD's L2.
+  int split, n;
+  if (a.N % 8 == 0 && a.nsplit > 1) {
+    const int x = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
+    n = (j / a.nsplit) * 8 + x;
+    split = j % a.nsplit;
+  } else {
+    split = (int)(blockIdx.x % a.nsplit);
+    n = (int)(blockIdx.x / a.nsplit);
+  }
   const int tid = threadIdx.x;
   const int w = (tid >> 6) & 3, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const bool qk_role = tid < 256;
