@@ -150,16 +150,18 @@ def bench_prefill(cpa, torch, synth, steps, warmup, warmup_ms):
     # fit in that cache, so the timed steps above may find them there. Two
     # flushes: a 512 MiB write (it leaves the cache full of dirty lines, whose
     # write-back then competes with the kernel's reads) and a 512 MiB read.
+    # Each (flush, launch) loop is warmed like the steps above before it is
+    # timed: the clock settles to the new mix of work (the first few hundred
+    # milliseconds of flushes ran the launch up to 15 % slower).
     scratch = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
-    cold_reps = min(steps, 10)
+    cold_reps = min(steps, 20)
     cold = {}
     for kind in ("write", "read"):
+        flush = (lambda i: scratch.fill_(float(i))) if kind == "write" else (lambda i: scratch.sum())
+        _warm(torch, lambda: (flush(0), step()), warmup, warmup_ms)
         cevs = _events(torch, cold_reps)
         for i in range(cold_reps):
-            if kind == "write":
-                scratch.fill_(float(i))
-            else:
-                scratch.sum()
+            flush(i)
             step(cevs[i])
         torch.cuda.synchronize()
         cold[kind] = sorted(a.elapsed_time(b) for a, b in cevs)
