@@ -57,9 +57,9 @@ TRAFFIC = {
                               fetch_scale=1.99994, write_scale=1.0,
                               fetch_bytes=138464403, write_bytes=34603315),
     # profiles/decode_mla_b64_h64_ctx131072_c8.md
-    "decode_mla_kernel<bf16>": dict(digest="cf4ccc50b8bbe02e", fetch_kib=599185.9, write_kib=32832.6,
+    "decode_mla_kernel<bf16>": dict(digest="d9fc94b6f76ea876", fetch_kib=592268.5, write_kib=32833.4,
                                    fetch_scale=1.99994, write_scale=1.0,
-                                   fetch_bytes=1227095909, write_bytes=33620582),
+                                   fetch_bytes=1212929499, write_bytes=33621402),
     # profiles/decode_gqa_b8_h32_kv8_ctx131072_c8.md
     "decode_gqa_kernel<bf16>": dict(digest="99ed0efbebf30435", fetch_kib=262291.3, write_kib=520.0,
                                    fetch_scale=1.99994, write_scale=1.0,
