@@ -188,6 +188,8 @@ def _mla_inputs(B, L, fp8, seed, std=0.5):
     (2, 64, [(0, 64)]),                      # exactly two tiles
     (3, 1000, [(0, 333), (333, 1000)]),      # ragged tails, several splits
     (4, 130, [(5, 5), (0, 1), (7, 130)]),    # empty shard, single key
+    (8, 1000, [(0, 1000), (100, 900)]),      # 8 requests: each request's splits on one XCD
+    (16, 600, [(0, 600)]),
 ])
 def test_decode_mla_small(cpa, fp8, B, L, ranges):
     import torch

@@ -100,6 +100,7 @@ def _mla_case(cpa, layout, fp8, B, Q, L_list, C, seed, n_repl=0):
     ("contiguous", 4, [700, 6, 333], 2),    # ragged; rank 1 of request 1 starts after row 0 (an empty row)
     ("contiguous", 2, [64, 65], 1),         # exactly two tiles / one key past them
     ("round_robin", 3, [500, 3, 97], 3),
+    ("contiguous", 2, [400, 9, 333, 64, 65, 2, 700, 250], 2),  # 8 requests: each request's workgroups on one XCD
 ])
 def test_mla_multi_query(cpa, fp8, layout, Q, L_list, C):
     _mla_case(cpa, layout, fp8, len(L_list), Q, L_list, C, seed=Q * 100 + C + fp8)

@@ -71,6 +71,23 @@ def test_sparse_decode_shaped(cpa, K):
     H.check_lowp(o, l, ro, rl, f"sparse K={K}")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_sparse_decode_shaped_8_queries(cpa, fp8):
+    """8 queries of 2,048 rows: the queries divide over the 8 XCDs, so the
+    splits of a query run on one XCD (their workgroup order differs from the
+    4-query case)."""
+    N, L, K = 8, 5000, 2048
+    if fp8:
+        rng, qb, codes, sc = _fp8_inputs(N, N, L, 700)
+        idx = np.stack([rng.choice(L, K, replace=False) for _ in range(N)]).astype(np.int32)
+        o, l, ro, rl = _run_fp8(cpa, qb, codes, sc, idx, 1 / 24)
+    else:
+        rng, qb, cb = _inputs(N, N, L, 701)
+        idx = np.stack([rng.choice(L, K, replace=False) for _ in range(N)]).astype(np.int32)
+        o, l, ro, rl = _run(cpa, qb, cb, idx, 1 / 24)
+    H.check_lowp(o, l, ro, rl, f"sparse 8 queries fp8={fp8}")
+
+
 def test_sparse_whole_tiles_of_padding(cpa):
     """Lists whose first tiles are all padding (the heads have seen no
     selection yet), with padding tiles in the middle and at the end."""
