@@ -14,7 +14,7 @@ partial launches on one device plus the exact merge; bf16 cache and FP8 E4M3
 cache with per-token scale, in GB/s of algorithmic bytes (cache bytes read
 once, plus queries, partial outputs/LSEs and the merge). ``decode_gqa``: the
 same step for a GQA cache at a serving shape (batch 8, 32/8 heads, d=128,
-131072 tokens, C=8), bf16 and FP8; ``decode_config1``: the fp32 GQA decode of
+131072 tokens, C=8), bf16 and FP8; ``decode_gqa_f32_4k``: the fp32 GQA decode of
 batch 1, 8/1 heads, 4096 tokens, C=4, with the last-level cache flushed.
 
 Also reported: the dominant kernel's roofline (live HIP-event timing on the
@@ -116,7 +116,7 @@ def _events(torch, n):
 
 
 def bench_prefill(cpa, torch, synth, steps, warmup, warmup_ms):
-    c = synth.config(2)
+    c = synth.workload("gqa_zigzag_prefill_16k")
     plan = cpa.cp_plan_zigzag(c["C"], c["rank"], c["new_len"], c["prefix_len"])
     T = sum(c["new_len"])
     dev = torch.device("cuda:0")
@@ -170,11 +170,13 @@ def bench_prefill(cpa, torch, synth, steps, warmup, warmup_ms):
                 inputs=(q, k, v), cold_ms=cold)
 
 
-def bench_prefill_config(cpa, torch, synth, k, steps, warmup, warmup_ms):
-    """One more prefill shard workload (config 4: MLA zigzag with a cached
-    prefix; config 5: interleave over the ragged agentic batch), timed per
+def bench_prefill_workload(cpa, torch, synth, name, steps, warmup, warmup_ms):
+    """One more prefill shard workload (mla_zigzag_prefill_prefix32k: MLA
+    zigzag with a cached prefix; gqa_interleave_prefill_agentic16: interleave
+    over the ragged agentic batch), timed per
     launch with HIP events: algorithmic TFLOP/s."""
-    c = synth.config(k)
+    c = synth.workload(name)
+    k = c["seed"]
     planner = cpa.cp_plan_zigzag if c["strategy"] == "zigzag" else cpa.cp_plan_interleave
     plan = planner(c["C"], c["rank"], c["new_len"], c["prefix_len"])
     T = sum(c["new_len"]) + sum(c["prefix_len"])
@@ -205,7 +207,7 @@ def bench_prefill_config(cpa, torch, synth, k, steps, warmup, warmup_ms):
 
 
 def bench_decode(cpa, torch, synth, steps, warmup, warmup_ms):
-    c = synth.config(3)
+    c = synth.workload("mla_decode_131k")
     B, L, C, H = c["B"], c["L"], c["C"], c["Hq"]
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
@@ -649,12 +651,12 @@ def bench_gqa_decode(cpa, torch, steps, warmup, warmup_ms):
     return res
 
 
-def bench_decode_config1(cpa, torch, synth, steps, warmup, warmup_ms):
+def bench_decode_gqa_f32_4k(cpa, torch, synth, steps, warmup, warmup_ms):
     """Split-KV decode + LSE merge, fp32: batch 1, 8 query heads on 1 kv head,
     head dim 128, 4096-token context as C=4 contiguous 1024-token shards (4
     partial launches + merge per step), with the last-level cache flushed
     (a 512 MiB write) before every timed step, and cache-hot."""
-    c = synth.config(1)
+    c = synth.workload("gqa_decode_f32_4k")
     B, Hq, Hkv, D, L, C = c["B"], c["Hq"], c["Hkv"], c["Dqk"], c["L"], c["C"]
     dev = torch.device("cuda:0")
     q = torch.from_numpy(synth.f32_normal(1, 1, (B, Hq, D))).to(dev)
@@ -717,10 +719,10 @@ def _segment_end_rows(plan):
     return list(dict.fromkeys(rows))
 
 
-def cpu_baseline(synth, prefill, seconds, per_config_seconds=5.0, min_rows=0):
+def cpu_baseline(synth, prefill, seconds, per_workload_seconds=5.0, min_rows=0):
     """The float64 oracle, as it stands, on this host's cores, on bounded
     samples of every workload: the zigzag GQA prefill shard (the headline
-    comparison, ``value``), and per configuration: the fp32 GQA decode in
+    comparison, ``value``), and per workload: the fp32 GQA decode in
     full, one request of the MLA decode (bf16 and FP8, extrapolated to the
     batch), and sampled local rows of the MLA zigzag and ragged interleave
     prefill shards (segment ends first, then random rows; extrapolated to
@@ -735,7 +737,7 @@ def cpu_baseline(synth, prefill, seconds, per_config_seconds=5.0, min_rows=0):
         limiter = None
     per = {}
 
-    # config 2: zigzag GQA prefill shard (headline)
+    # the zigzag GQA prefill shard (headline)
     c = prefill["cfg"]
     ref = plans.plan_zigzag(c["C"], c["rank"], c["new_len"], c["prefix_len"])
     T = sum(c["new_len"])
@@ -749,12 +751,12 @@ def cpu_baseline(synth, prefill, seconds, per_config_seconds=5.0, min_rows=0):
             "sample": f"{done_rows} of {ref.n_local} local query rows (all 32 heads, random order) of the same "
                       f"zigzag workload in {dt:.1f} s; float64 numpy; the full step would take "
                       f"{prefill['flops'] / (flops / dt):.0f} s"}
-    per["config2"] = dict(rows=done_rows, rows_total=ref.n_local, seconds=round(dt, 2),
+    per["gqa_zigzag_prefill_16k"] = dict(rows=done_rows, rows_total=ref.n_local, seconds=round(dt, 2),
                           rows_per_s=round(done_rows / dt, 2), fp64_gflops=round(flops / dt / 1e9, 2),
                           full_step_seconds_extrapolated=round(prefill["flops"] / (flops / dt), 1))
 
-    # config 1: fp32 GQA decode, 4 shards + merge, in full
-    c1 = synth.config(1)
+    # the fp32 GQA decode (batch 1, 8/1 heads, 4096 tokens), 4 shards + merge, in full
+    c1 = synth.workload("gqa_decode_f32_4k")
     q = synth.f32_normal(1, 1, (c1["B"], c1["Hq"], c1["Dqk"])).astype(np.float64)
     k = synth.f32_normal(1, 2, (c1["B"], c1["L"], c1["Hkv"], c1["Dqk"]), chunk=1).astype(np.float64)
     v = synth.f32_normal(1, 3, (c1["B"], c1["L"], c1["Hkv"], c1["Dv"]), chunk=1).astype(np.float64)
@@ -762,31 +764,32 @@ def cpu_baseline(synth, prefill, seconds, per_config_seconds=5.0, min_rows=0):
     _oracle_decode_all_shards(att, q, k, c1["L"], c1["C"], c1["scale"], vcache=v)
     dt = time.perf_counter() - t0
     fl = _decode_flops(c1["L"], c1["Hq"], c1["Dqk"], c1["Dv"]) * c1["B"]
-    per["config1"] = dict(sample="the whole step (4 shard decodes + merge)", seconds=round(dt, 4),
+    per["gqa_decode_f32_4k"] = dict(sample="the whole step (4 shard decodes + merge)", seconds=round(dt, 4),
                           fp64_gflops=round(fl / dt / 1e9, 3),
                           cache_gbs=round(c1["B"] * c1["L"] * c1["Hkv"] * (c1["Dqk"] + c1["Dv"]) * 4 / dt / 1e9, 3))
 
-    # config 3: MLA decode, request 0 of the batch (its draw is that of the
+    # the MLA decode (batch 64, 131072 tokens, C=8): request 0 of the batch (its draw is that of the
     # full cache), 8 shards + merge, bf16 and FP8; extrapolated to 64 requests
-    c3 = synth.config(3)
+    c3 = synth.workload("mla_decode_131k")
     q3 = synth.bf16_normal(3, 1, (c3["B"], c3["Hq"], c3["Dqk"]))[:1]
     bits, codes, scales = synth.latent_cache_both(3, 2, 1, c3["L"], c3["Dqk"], c3["std"])
     fl = _decode_flops(c3["L"], c3["Hq"], c3["Dqk"], c3["Dv"])
-    per["config3"] = {}
+    per["mla_decode_131k"] = {}
     for name, cache, kw in (("bf16", bits, dict(decode=formats.bf16_bits_to_f64)),
                             ("fp8", codes, dict(decode=formats.e4m3_to_f64, kv_scale=scales))):
         t0 = time.perf_counter()
         _oracle_decode_all_shards(att, formats.bf16_bits_to_f64(q3), cache, c3["L"], c3["C"], c3["scale"],
                                   dv=c3["Dv"], **kw)
         dt = time.perf_counter() - t0
-        per["config3"][name] = dict(sample="request 0 of 64: 64 heads x 131072 tokens, 8 shard decodes + merge",
+        per["mla_decode_131k"][name] = dict(sample="request 0 of 64: 64 heads x 131072 tokens, 8 shard decodes + merge",
                                     seconds=round(dt, 2), fp64_gflops=round(fl / dt / 1e9, 2),
                                     full_step_seconds_extrapolated=round(dt * c3["B"], 1))
     del bits, codes, scales
 
-    # configs 4 and 5: sampled local rows of the prefill shards
-    for kcfg in (4, 5):
-        ck = synth.config(kcfg)
+    # the MLA zigzag and the ragged interleave prefill shards: sampled local rows
+    for wname in ("mla_zigzag_prefill_prefix32k", "gqa_interleave_prefill_agentic16"):
+        ck = synth.workload(wname)
+        kcfg = ck["seed"]
         planner = plans.plan_zigzag if ck["strategy"] == "zigzag" else plans.plan_interleave
         pk = planner(ck["C"], ck["rank"], ck["new_len"], ck["prefix_len"])
         Tk = sum(ck["new_len"]) + sum(ck["prefix_len"])
@@ -809,10 +812,10 @@ def cpu_baseline(synth, prefill, seconds, per_config_seconds=5.0, min_rows=0):
             kv_slabs.update(range(kv0 // 4096, (kv0 + p) // 4096 + 1))
         kk = synth.bf16_normal_slabs(kcfg, 2, (Tk, ck["Hkv"], ck["Dqk"]), kv_slabs)
         vk = None if ck["Hkv"] == 1 else synth.bf16_normal_slabs(kcfg, 3, (Tk, ck["Hkv"], ck["Dv"]), kv_slabs)
-        done_rows, flops, dt = _oracle_rows(att, qk, kk, vk, pk, ck, rows_needed, per_config_seconds, min_rows,
+        done_rows, flops, dt = _oracle_rows(att, qk, kk, vk, pk, ck, rows_needed, per_workload_seconds, min_rows,
                                             formats.bf16_bits_to_f64)
         total = int(np.sum(pk.pos_id.astype(np.int64) + 1)) * ck["Hq"] * 2 * (ck["Dqk"] + ck["Dv"])
-        per[f"config{kcfg}"] = dict(
+        per[wname] = dict(
             sample=f"{done_rows} local rows ({min(done_rows, len(ends))} of them segment ends, the rest random) "
                    f"of {pk.n_local}, all heads",
             rows=done_rows, rows_total=pk.n_local, seconds=round(dt, 2), rows_per_s=round(done_rows / dt, 3),
@@ -820,7 +823,7 @@ def cpu_baseline(synth, prefill, seconds, per_config_seconds=5.0, min_rows=0):
         del qk, kk, vk
     if limiter is not None:
         limiter.unregister() if hasattr(limiter, "unregister") else None
-    head["per_config"] = per
+    head["per_workload"] = per
     return head
 
 
@@ -834,8 +837,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the secondary MLA decode figures")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--cpu-config-seconds", type=float, default=5.0,
-                    help="CPU oracle time per sampled configuration (MLA and interleave prefill)")
+    ap.add_argument("--cpu-workload-seconds", type=float, default=5.0,
+                    help="CPU oracle time per sampled workload (MLA and interleave prefill)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="sample at least this many local rows of the MLA / interleave prefill shards")
     ap.add_argument("--cpu-only", action="store_true", help="only the CPU oracle baselines (no GPU figures)")
@@ -854,10 +857,10 @@ def main():
     import synth
     if args.cpu_only:
         from oracle import plans as oplans
-        c2 = synth.config(2)
+        c2 = synth.workload("gqa_zigzag_prefill_16k")
         ref = oplans.plan_zigzag(c2["C"], c2["rank"], c2["new_len"], c2["prefix_len"])
         flops = int(np.sum(ref.pos_id.astype(np.int64) + 1)) * c2["Hq"] * 2 * (c2["Dqk"] + c2["Dv"])
-        base = cpu_baseline(synth, {"cfg": c2, "flops": flops}, args.cpu_seconds, args.cpu_config_seconds,
+        base = cpu_baseline(synth, {"cfg": c2, "flops": flops}, args.cpu_seconds, args.cpu_workload_seconds,
                             args.cpu_rows)
         print(json.dumps({"cpu_baseline": base}), flush=True)
         return
@@ -887,8 +890,8 @@ def main():
         return
     if args.gqa_only:
         g = bench_gqa_decode(cpa, torch, args.steps, args.warmup, args.warmup_ms)
-        c1 = bench_decode_config1(cpa, torch, synth, args.steps, args.warmup, args.warmup_ms)
-        print(json.dumps({"decode_gqa": g, "decode_config1": c1}), flush=True)
+        c1 = bench_decode_gqa_f32_4k(cpa, torch, synth, args.steps, args.warmup, args.warmup_ms)
+        print(json.dumps({"decode_gqa": g, "decode_gqa_f32_4k": c1}), flush=True)
         return
 
     log("[bench] zigzag prefill shard ...")
@@ -986,7 +989,7 @@ def main():
             f"prefill {dec['sparse_bf16']['prefill']['gbs']:.0f} GB/s (FP8 {dec['sparse_fp8']['prefill']['gbs']:.0f})")
 
     if not args.no_decode:
-        log("[bench] split-KV GQA decode (serving shape, bf16 and FP8) and config 1 (fp32) ...")
+        log("[bench] split-KV GQA decode (serving shape, bf16 and FP8) and the fp32 4096-token GQA decode ...")
         g = bench_gqa_decode(cpa, torch, max(3, args.steps // 2), args.warmup, args.warmup_ms)
         rnd = lambda d: {k: round(v, 4) if isinstance(v, float) else v for k, v in d.items()}
         line["decode_gqa"] = {"workload": g["workload"], "unit": "GB/s", "bf16": rnd(g["bf16"]), "fp8": rnd(g["fp8"]),
@@ -996,20 +999,21 @@ def main():
                                   "frac": round(g["bf16"]["launch_gbs"] / PEAK_HBM_GBS, 4),
                                   "traffic": traffic("decode_gqa_kernel<bf16>")[0],
                                   "traffic_detail": traffic("decode_gqa_kernel<bf16>")[1]}}
-        c1 = bench_decode_config1(cpa, torch, synth, max(3, args.steps // 2), args.warmup, args.warmup_ms)
-        line["decode_config1"] = {k: (rnd(v) if isinstance(v, dict) else v) for k, v in c1.items()}
+        c1 = bench_decode_gqa_f32_4k(cpa, torch, synth, max(3, args.steps // 2), args.warmup, args.warmup_ms)
+        line["decode_gqa_f32_4k"] = {k: (rnd(v) if isinstance(v, dict) else v) for k, v in c1.items()}
         log(f"[bench] GQA decode bf16 {g['bf16']['gbs']:.0f} GB/s/step, fp8 {g['fp8']['gbs']:.0f} GB/s/step; "
-            f"config 1 (cache flushed) {c1['cache_flushed']['gbs']:.1f} GB/s/step")
+            f"fp32 4096-token decode (cache flushed) {c1['cache_flushed']['gbs']:.1f} GB/s/step")
 
     if not args.no_extra_prefill:
-        for k, key in ((4, "prefill_mla_zigzag"), (5, "prefill_interleave")):
-            log(f"[bench] {key} (config {k}) ...")
-            line[key] = bench_prefill_config(cpa, torch, synth, k, max(2, args.steps // 10), 1, args.warmup_ms)
+        for wname, key in (("mla_zigzag_prefill_prefix32k", "prefill_mla_zigzag"),
+                           ("gqa_interleave_prefill_agentic16", "prefill_interleave")):
+            log(f"[bench] {key} ({wname}) ...")
+            line[key] = bench_prefill_workload(cpa, torch, synth, wname, max(2, args.steps // 10), 1, args.warmup_ms)
             log(f"[bench] {key}: {line[key]['kernel_ms']} ms, {line[key]['tflops']} TFLOP/s")
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
-        line["cpu_baseline"] = cpu_baseline(synth, pre, args.cpu_seconds, args.cpu_config_seconds, args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(synth, pre, args.cpu_seconds, args.cpu_workload_seconds, args.cpu_rows)
     print(json.dumps(line), flush=True)
 
 

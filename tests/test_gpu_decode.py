@@ -109,7 +109,7 @@ def _decode_case(cpa, B, Hq, Hkv, D, L, shards, qdt, kvdt, seed, ragged=False):
 def test_decode_gqa_f32_workload(cpa):
     """Split-KV decode + merge, fp32: batch 1, 8 query heads on 1 kv head,
     head dim 128, 4096-token context cut into 4 contiguous 1024-token shards."""
-    c = synth.config(1)
+    c = synth.workload("gqa_decode_f32_4k")
     B, Hq, Hkv, D, L = c["B"], c["Hq"], c["Hkv"], c["Dqk"], c["L"]
     q = synth.f32_normal(1, 1, (B, Hq, D))
     k = synth.f32_normal(1, 2, (B, L, Hkv, D), chunk=1)

@@ -129,7 +129,7 @@ def _sample_rows(plan, n_extra, seed):
 def test_prefill_zigzag_gqa_workload(cpa):
     """Zigzag prefill shard: causal GQA, 32 query heads on 8 kv heads, d=128,
     16384-token prompt, C=4, rank 1 (blocks 1 and 6), bf16 in."""
-    c = synth.config(2)
+    c = synth.workload("gqa_zigzag_prefill_16k")
     plan = cpa.cp_plan_zigzag(c["C"], c["rank"], c["new_len"], c["prefix_len"])
     T = sum(c["new_len"])
     qb = synth.bf16_normal(2, 1, (plan.n_local, c["Hq"], c["Dqk"]))

@@ -41,7 +41,7 @@ def _sample_rows(plan, n_extra, seed):
 
 @pytest.fixture(scope="module")
 def mla_decode_inputs():
-    c = synth.config(3)
+    c = synth.workload("mla_decode_131k")
     print("[mla decode] generating inputs", flush=True)
     q = synth.bf16_normal(3, 1, (c["B"], c["Hq"], c["Dqk"]))
     bits, codes, scales = synth.latent_cache_both(3, 2, c["B"], c["L"], c["Dqk"], c["std"])
@@ -130,7 +130,7 @@ def test_mla_prefill_zigzag_workload(cpa):
     """MLA zigzag prefill: 64 heads, 576/512, 131072 new tokens after a
     32768-token cached prefix, C=8 (16 blocks of 8192), rank 0's share."""
     import torch
-    c = synth.config(4)
+    c = synth.workload("mla_zigzag_prefill_prefix32k")
     plan = cpa.cp_plan_zigzag(c["C"], c["rank"], c["new_len"], c["prefix_len"])
     T = sum(c["new_len"]) + sum(c["prefix_len"])
     print("[mla prefill] generating inputs", flush=True)
@@ -165,7 +165,7 @@ def test_interleave_ragged_workload(cpa):
     """Interleave prefill on a ragged batch: 16 agentic-length requests
     (T = 728,040), C=4, rank 2; causal GQA 32/8, d=128, bf16."""
     import torch
-    c = synth.config(5)
+    c = synth.workload("gqa_interleave_prefill_agentic16")
     plan = cpa.cp_plan_interleave(c["C"], c["rank"], c["new_len"], c["prefix_len"])
     assert plan.n_local == 182010
     T = sum(c["new_len"])
