@@ -107,3 +107,28 @@ def test_multi_query_plan_rejects_bad_arguments():
                  (R_, 2, 0, [8], 2, -1)):
         with pytest.raises(cpa.CpaError):
             cpa.cp_plan_multi_query(*args)
+
+
+def test_named_workloads_draw_the_recorded_inputs(golden_dir):
+    """The named synthetic workloads keep their sizes and seed families: the
+    ragged interleave batch is the recorded 16-length mix, and every
+    workload's first query values come from its own family."""
+    import json
+    import os
+
+    import synth
+    with open(os.path.join(golden_dir, "agentic_lengths_seed5.json")) as f:
+        fix = json.load(f)
+    w = synth.workload("gqa_interleave_prefill_agentic16")
+    assert w["new_len"] == fix["lengths"] and sum(w["new_len"]) == fix["total"] == 728040
+    sizes = {"gqa_decode_f32_4k": (1, 8, 1, 128, 4096), "mla_decode_131k": (64, 64, 1, 576, 131072)}
+    for name, (B, Hq, Hkv, D, L) in sizes.items():
+        c = synth.workload(name)
+        assert (c["B"], c["Hq"], c["Hkv"], c["Dqk"], c["L"]) == (B, Hq, Hkv, D, L)
+    assert synth.workload("gqa_zigzag_prefill_16k")["new_len"] == [16384]
+    assert synth.workload("mla_zigzag_prefill_prefix32k")["prefix_len"] == [32768]
+    seeds = [synth.workload(n)["seed"] for n in synth.WORKLOADS]
+    assert len(set(seeds)) == len(seeds)
+    a = synth.bf16_normal(synth.workload("mla_decode_131k")["seed"], 1, (2, 3, 4))
+    b = synth.bf16_normal(synth.workload("gqa_zigzag_prefill_16k")["seed"], 1, (2, 3, 4))
+    assert not np.array_equal(a, b)
