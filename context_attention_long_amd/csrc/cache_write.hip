@@ -16,10 +16,13 @@ namespace {
 
 // Each wavefront takes 64 consecutive entries: lane l reads entry l's slot and
 // request (coalesced), a ballot finds the entries this rank owns, and the
-// wavefront copies each owned row with all 64 lanes.
+// wavefront copies their rows as (row, chunk) items spread over its lanes,
+// four items per lane in flight (all loads, then all stores).
 template <typename V>
 __global__ __launch_bounds__(256) void cache_write_rr_kernel(cpa::CacheWriteArgs a) {
-  const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  __shared__ int own_lane[4][64];  // per wavefront: lane of the j-th owned entry
+  const int wv = threadIdx.x >> 6;
+  const int64_t base = ((int64_t)blockIdx.x * 4 + wv) * 64;
   const int lane = threadIdx.x & 63;
   if (base >= a.n) return;
   const int64_t i = base + lane;
@@ -33,16 +36,32 @@ __global__ __launch_bounds__(256) void cache_write_rr_kernel(cpa::CacheWriteArgs
       if (r < a.Lmax) row = r;
     }
   }
-  uint64_t owned = __ballot(row >= 0);
-  const int nv = (int)(a.row_bytes / sizeof(V));
-  while (owned) {
-    const int e = __builtin_ctzll(owned);
-    owned &= owned - 1;
-    const int64_t r = __shfl(row, e);
-    const int32_t q = __shfl(req, e);
-    const V* s = reinterpret_cast<const V*>(a.src + (base + e) * a.src_row);
-    V* d = reinterpret_cast<V*>(a.dst + q * a.dst_b + r * a.dst_row);
-    for (int k = lane; k < nv; k += 64) d[k] = __builtin_nontemporal_load(s + k);
+  const uint64_t owned = __ballot(row >= 0);
+  const int n_own = __popcll(owned);
+  if (n_own == 0) return;
+  if (row >= 0)
+    own_lane[wv][__builtin_amdgcn_mbcnt_hi((uint32_t)(owned >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)owned, 0u))] =
+        lane;
+  const int nv = (int)(a.row_bytes / sizeof(V));  // chunks per row
+  const int total = n_own * nv;
+  constexpr int U = 4;
+  for (int t0 = 0; t0 < total; t0 += 64 * U) {
+    V buf[U];
+    int64_t doff[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + 64 * u + lane;
+      const int tt = t < total ? t : total - 1;  // past the end: repeat the last item, store nothing
+      const int j = tt / nv, k = tt - j * nv;
+      const int e = own_lane[wv][j];
+      const int64_t r = __shfl(row, e);
+      const int32_t q = __shfl(req, e);
+      buf[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(a.src + (base + e) * a.src_row) + k);
+      doff[u] = t < total ? q * a.dst_b + r * a.dst_row + (int64_t)k * (int64_t)sizeof(V) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (doff[u] >= 0) *reinterpret_cast<V*>(a.dst + doff[u]) = buf[u];
   }
 }
 
