@@ -303,8 +303,9 @@ __device__ __forceinline__ void ws_pv(const Tiles& T, const uint8_t* base, int64
                                       int64_t s_t, int tp, int w, int g, int c, const Bases& L,
                                       f32x4 (&oacc)[kMv][4], const Lds& S, const Rows& rows = Rows{}) {
   if (T.ntiles <= 0) return;
-  // the PV wavefronts' phase is the longer of the two per tile: they win
-  // instruction arbitration on their SIMD (2-3 % shorter launches, measured)
+  // the PV wavefronts win instruction arbitration on their SIMD: measured
+  // 2-3 % shorter launches than equal priorities (the QK wavefronts first,
+  // for their MFMAs or the whole step, was slower)
   __builtin_amdgcn_s_setprio(3);
   const int lane = tp & 63;
   const bool unit5 = w < 2;  // wave-uniform
@@ -426,8 +427,9 @@ __device__ __forceinline__ void ws_pv_gather(const Tiles& T, const uint8_t* base
                                              int c, const Bases& L, f32x4 (&oacc)[kMv][4], const Lds& S,
                                              char* ring) {
   if (T.ntiles <= 0) return;
-  // the PV wavefronts' phase is the longer of the two per tile: they win
-  // instruction arbitration on their SIMD (2-3 % shorter launches, measured)
+  // the PV wavefronts win instruction arbitration on their SIMD: measured
+  // 2-3 % shorter launches than equal priorities (the QK wavefronts first,
+  // for their MFMAs or the whole step, was slower)
   __builtin_amdgcn_s_setprio(3);
   const int lane = tp & 63;
   const int n = T.ntiles;
