@@ -61,10 +61,13 @@ def _gather(pool, table, ps, n_log):
     return pool[rows]
 
 
-@pytest.mark.parametrize("fp8,ps,shared,bad", [(False, 64, 0, False), (False, 16, 2, True), (True, 32, 0, False),
-                                               (True, 256, 1, True), (True, 1, 0, False)])
-def test_mla_paged_vs_oracle(cpa, fp8, ps, shared, bad):
-    B, H_, L = 4, 64, 700
+@pytest.mark.parametrize("fp8,ps,shared,bad,B", [(False, 64, 0, False, 4), (False, 16, 2, True, 4), (True, 32, 0, False, 4),
+                                                 (True, 256, 1, True, 4), (True, 1, 0, False, 4),
+                                                 (False, 64, 1, False, 8), (True, 64, 0, True, 8)])
+def test_mla_paged_vs_oracle(cpa, fp8, ps, shared, bad, B):
+    """B = 8: the requests divide over the 8 XCDs, so each request's splits
+    run on one XCD (the other work-unit order)."""
+    H_, L = 64, 700
     n_blocks = (L + ps - 1) // ps
     n_pages = shared + B * (n_blocks - shared) + 3
     table = _table(B, n_blocks, n_pages, ps + 7 * fp8, shared=shared, bad=bad)
