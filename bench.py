@@ -850,7 +850,7 @@ def main():
                     help="first run one 2 GiB device-to-device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(shards are evaluated as partial launches on one device). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -38,7 +38,7 @@ extern "C" {
 typedef enum cpa_status {
   CPA_OK = 0,
   CPA_E_INVAL = 1,        /* null pointer, bad shape, dtype, stride or alignment */
-  CPA_E_UNSUPPORTED = 2,  /* head dims or dtype combination this build has no kernel for */
+  CPA_E_UNSUPPORTED = 2,  /* head dims or dtype combination the library has no kernel for */
   CPA_E_CAPACITY = 3,     /* a caller array or workspace is too small; sizes written back */
   CPA_E_HIP = 4           /* the HIP runtime reported an error at launch */
 } cpa_status;
