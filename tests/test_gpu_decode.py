@@ -41,7 +41,8 @@ def test_merge_worked_example_fig8(cpa, golden_dir):
     assert abs(H.host(lo)[0, 0] - math.log(8)) < 1e-6
 
 
-@pytest.mark.parametrize("S,N,Hh,Dv", [(1, 3, 5, 8), (4, 7, 3, 128), (8, 64, 64, 512), (3, 2, 2, 1028)])
+@pytest.mark.parametrize("S,N,Hh,Dv", [(1, 3, 5, 8), (4, 7, 3, 128), (8, 64, 64, 512), (3, 2, 2, 1028),
+                                         (12, 5, 3, 264), (16, 3, 4, 64), (9, 2, 3, 772)])
 def test_merge_random_states(cpa, S, N, Hh, Dv):
     rng = np.random.default_rng(S * 1000 + Dv)
     o = rng.standard_normal((S, N, Hh, Dv)).astype(np.float32)
